@@ -1,0 +1,301 @@
+"""CPU oracle for the ResidualKV hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+run this module: only the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it.  It shares no code with the HIP library and does
+not import it.
+
+It is a plain, slow, step-by-step statement of what the path computes, for
+one (instance, KV head) at a time, on NumPy arrays.  Floating point is fp64
+except where a quantised code or scale is decided: there both this oracle and
+the kernels take the decision from the same fp32 residual (see
+``ref_mean_f32`` and ``residual_f32``), and the decision itself is the exact
+round-to-nearest-even of that fp32 value (fp64 here is provably enough to get
+the exact answer).
+
+Sources (the method's pages):
+  [P1] "ResidualKV: Residual-Based KV Cache Compression for Efficient
+       Long-Context Inference" (paper page with summary and transcript):
+       section "DeltaKV Framework Architecture" -- strided reference
+       selection, top-k nearest by L2 distance, mean reference KV_R,
+       residual z = f(KV) - f(KV_R), reconstruction KV^ = KV^_delta + KV_R;
+       section "Key concepts" -- residual computation;
+       section "Performance Results" -- residuals suit token-wise
+       quantisation; transcript -- the cache is split into uncompressed
+       reference tokens and compressed tokens.
+  [P3] "New KV Cache Compression Method Cuts Long-Context Inference Costs by
+       85%", section "How ResidualKV Works" -- global reference tokens plus
+       compact quantised residual codes, reconstruction on the fly, and a
+       dynamic-stride schedule with roughly logarithmic reference growth.
+
+Readings where the pages are silent (each is the plainest one the rest
+supports):
+  * position j is a reference iff j mod s(j) == 0 (so position 0 always is);
+  * token i's candidates are the references at positions <= i (itself
+    included when i is a reference);
+  * fewer than k candidates: k_eff = |candidates|, slots padded with 0xFFFF;
+  * distances use keys rounded to bf16 (RNE) in every input precision;
+  * ties in distance go to the lower position;
+  * the compressor/decompressor pair is the identity; the residual is stored
+    as symmetric absmax group-quantised codes with an fp16 scale;
+  * bits == 0 means no quantisation: the residual is kept exactly (fp64).
+"""
+
+import numpy as np
+
+IDX_PAD = 0xFFFF
+V_TILE = 32          # tokens per tile of the transposed V-code layout
+
+
+# ---------------------------------------------------------------------------
+# Reference schedule  ([P1] "DeltaKV Framework Architecture", strided
+# reference selection; [P3] "How ResidualKV Works", dynamic-stride schedule)
+# ---------------------------------------------------------------------------
+
+def stride_at(j: int, base: int, double_after: int) -> int:
+    """Stride in force at position j.
+
+    Fixed schedule (double_after == 0): ``base`` everywhere.  Dynamic
+    schedule: ``base`` below ``double_after``; from there the stride doubles
+    each time the position doubles, so [A, 2A) uses 2*base, [2A, 4A) uses
+    4*base, and so on (A = double_after).
+    """
+    if double_after == 0 or j < double_after:
+        return base
+    band = 0
+    while j >= double_after << band:
+        band += 1
+    return base << band
+
+
+def ref_positions(n: int, base: int, double_after: int = 0) -> np.ndarray:
+    """Sorted reference positions T in [0, n): j is in T iff j mod s(j) == 0."""
+    return np.array([j for j in range(n) if j % stride_at(j, base, double_after) == 0],
+                    dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Rounding helpers (IEEE 754 round-to-nearest-even)
+# ---------------------------------------------------------------------------
+
+def bf16_round(x) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 (ties to even); returns fp32.
+
+    bf16 keeps the top 16 bits of an fp32 word; adding 0x7FFF plus the lowest
+    kept bit before truncating implements round-half-to-even on the dropped
+    16 bits.  (Inputs here are finite.)
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
+    return r.view(np.float32)
+
+
+def fp16_scale(x64: np.ndarray) -> np.ndarray:
+    """Nearest fp16 to fp64 values x (ties to even), saturating at 65504."""
+    with np.errstate(over="ignore"):
+        h = np.asarray(x64, dtype=np.float64).astype(np.float16)
+    return np.where(np.isinf(h), np.float16(65504.0), h)
+
+
+# ---------------------------------------------------------------------------
+# Encode, one token row at a time ([P1] "DeltaKV Framework Architecture")
+# ---------------------------------------------------------------------------
+
+def candidate_count(i: int, T: np.ndarray) -> int:
+    """|C_i|: references at positions <= i."""
+    return int(np.searchsorted(T, i, side="right"))
+
+
+def distances(key_i: np.ndarray, ref_keys: np.ndarray) -> np.ndarray:
+    """Squared L2 distance from one key to each candidate key, fp64, summed
+    directly over (a - b)^2 (exact for bf16-valued inputs)."""
+    diff = ref_keys.astype(np.float64) - key_i.astype(np.float64)[None, :]
+    return (diff * diff).sum(axis=1)
+
+
+def select_topk(dist: np.ndarray, k: int) -> np.ndarray:
+    """Slots of the k_eff nearest candidates, lowest slot first among equal
+    distances; returned in ascending slot order."""
+    k_eff = min(k, dist.shape[0])
+    order = np.argsort(dist, kind="stable")[:k_eff]
+    return np.sort(order)
+
+
+def ref_mean_f32(ref_rows: np.ndarray) -> np.ndarray:
+    """KV_R: mean of the selected reference rows, in fp32.
+
+    The rows (ascending slot order) are added one after another in fp32
+    arithmetic, then the sum is divided by k_eff in fp32 -- the precision in
+    which the residual, and so every code, is decided.
+    """
+    rows = np.asarray(ref_rows, dtype=np.float32)
+    s = rows[0].copy()
+    for m in range(1, rows.shape[0]):
+        s = (s + rows[m]).astype(np.float32)
+    return (s / np.float32(rows.shape[0])).astype(np.float32)
+
+
+def residual_f32(x: np.ndarray, mean32: np.ndarray) -> np.ndarray:
+    """z = KV_i - KV_R in fp32 (compressor = identity)."""
+    return (np.asarray(x, dtype=np.float32) - mean32).astype(np.float32)
+
+
+def quantize_residual(delta32: np.ndarray, bits: int, group: int):
+    """Symmetric absmax group quantisation of one fp32 residual row.
+
+    For each run of ``group`` contiguous elements: a = max |z|, the scale is
+    the fp16 nearest to a / qmax (qmax = 2^(bits-1) - 1), and each code is
+    the integer nearest to z / scale (ties to even) clamped to [-qmax, qmax];
+    a zero scale gives zero codes.  Returns (scales fp16 [d/group],
+    codes int64 [d]).
+    """
+    qmax = (1 << (bits - 1)) - 1
+    z = np.asarray(delta32, dtype=np.float32).astype(np.float64)
+    zg = z.reshape(-1, group)
+    a = np.abs(zg).max(axis=1)
+    scale = fp16_scale(a / qmax)
+    s64 = scale.astype(np.float64)
+    codes = np.zeros_like(zg)
+    nz = s64 > 0
+    codes[nz] = np.rint(zg[nz] / s64[nz, None])
+    codes = np.clip(codes, -qmax, qmax)
+    return scale, codes.reshape(-1).astype(np.int64)
+
+
+def encode(K, V, base, double_after, k, bits, group, rows=None):
+    """Encode one (instance, KV head).
+
+    K, V: [N, d] arrays holding the input values (bf16 inputs widened to
+    fp32 exactly).  Returns a dict with, for the requested rows (all by
+    default):
+      rows      int64 [R]
+      idx       uint16 [R, k]   ascending reference slots, 0xFFFF padding
+      k_eff     int64 [R]
+      mean      fp32 [R, 2, d]  KV_R for K and V
+      delta     fp32 [R, 2, d]  residual (fp32)
+      scales    fp16 [R, 2, d/group]        (bits > 0)
+      codes     int64 [R, 2, d]             (bits > 0)
+      resid64   fp64 [R, 2, d]  exact residual (bits == 0)
+    plus ``T`` (reference positions).
+    """
+    K = np.asarray(K, dtype=np.float32)
+    V = np.asarray(V, dtype=np.float32)
+    n, d = K.shape
+    T = ref_positions(n, base, double_after)
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    keys = bf16_round(K)
+    R = rows.shape[0]
+    out = {
+        "T": T, "rows": rows,
+        "idx": np.full((R, k), IDX_PAD, dtype=np.uint16),
+        "k_eff": np.zeros(R, dtype=np.int64),
+        "mean": np.zeros((R, 2, d), dtype=np.float32),
+        "delta": np.zeros((R, 2, d), dtype=np.float32),
+    }
+    if bits > 0:
+        out["scales"] = np.zeros((R, 2, d // group), dtype=np.float16)
+        out["codes"] = np.zeros((R, 2, d), dtype=np.int64)
+    else:
+        out["resid64"] = np.zeros((R, 2, d), dtype=np.float64)
+    for r, i in enumerate(rows):
+        c = candidate_count(int(i), T)
+        dist = distances(keys[i], keys[T[:c]])
+        sel = select_topk(dist, k)
+        out["idx"][r, :sel.shape[0]] = sel
+        out["k_eff"][r] = sel.shape[0]
+        pos = T[sel]
+        for p, X in enumerate((K, V)):
+            m32 = ref_mean_f32(X[pos])
+            z32 = residual_f32(X[i], m32)
+            out["mean"][r, p] = m32
+            out["delta"][r, p] = z32
+            if bits > 0:
+                s, q = quantize_residual(z32, bits, group)
+                out["scales"][r, p] = s
+                out["codes"][r, p] = q
+            else:
+                out["resid64"][r, p] = X[i].astype(np.float64) - m32.astype(np.float64)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Storage formats of the compressed cache
+# ---------------------------------------------------------------------------
+
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Token-major packing of one row of codes: element t occupies bits
+    [t*bits, (t+1)*bits) of the row's little-endian bit string, as a
+    two's-complement field.  Returns uint8 [d*bits/8]."""
+    c = np.asarray(codes, dtype=np.int64)
+    field = c & ((1 << bits) - 1)
+    nbytes = c.shape[0] * bits // 8
+    out = np.zeros(nbytes, dtype=np.uint8)
+    for t, f in enumerate(field):
+        bit = t * bits
+        out[bit // 8] |= np.uint8((int(f) << (bit % 8)) & 0xFF)
+    return out
+
+
+def pack_v_tile(codes_tile: np.ndarray, bits: int) -> np.ndarray:
+    """Transposed packing of a tile of V codes: codes_tile is int [32, d]
+    (tokens x dims; missing tokens are zero).  For each dim t the 32 codes of
+    the tile form one little-endian bit string, token u at bits
+    [u*bits, (u+1)*bits).  Returns uint8 [d, 32*bits/8]."""
+    ct = np.asarray(codes_tile, dtype=np.int64)
+    return np.stack([pack_codes(ct[:, t], bits) for t in range(ct.shape[1])])
+
+
+def ref_store(K, V, T) -> np.ndarray:
+    """The uncompressed reference tokens: [2, |T|, d] (K plane, V plane)."""
+    return np.stack([np.asarray(K)[T], np.asarray(V)[T]])
+
+
+# ---------------------------------------------------------------------------
+# Reconstruction and decode attention ([P1] "DeltaKV Framework
+# Architecture", reconstruction; [P3] on-the-fly reconstruction)
+# ---------------------------------------------------------------------------
+
+def reconstruct(enc, K, V, bits):
+    """KV^_i for the encoded rows, fp64 [R, 2, d].
+
+    Reference positions are stored uncompressed and come back as they are.
+    Every other position is KV_R (the fp32 mean the residual was taken
+    against) plus the dequantised residual scale * code (bits > 0) or the
+    exact residual (bits == 0).
+    """
+    T = enc["T"]
+    is_ref = np.isin(enc["rows"], T)
+    out = enc["mean"].astype(np.float64).copy()
+    if bits > 0:
+        g = enc["codes"].shape[-1] // enc["scales"].shape[-1]
+        sc = np.repeat(enc["scales"].astype(np.float64), g, axis=-1)
+        out += sc * enc["codes"].astype(np.float64)
+    else:
+        out += enc["resid64"]
+    raw = np.stack([np.asarray(K, np.float64)[enc["rows"]],
+                    np.asarray(V, np.float64)[enc["rows"]]], axis=1)
+    out[is_ref] = raw[is_ref]
+    return out
+
+
+def decode_attn(q, k_hat, v_hat, scale):
+    """Single-query attention over a reconstructed cache, fp64.
+
+    q: [Hq, d]; k_hat, v_hat: [Hkv, N, d].  Query head h reads KV head
+    h // (Hq / Hkv).  logits = scale * q . k, softmax over all N positions,
+    output = sum_i p_i v_i.  Returns [Hq, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    hq = q.shape[0]
+    hkv = k_hat.shape[0]
+    grp = hq // hkv
+    out = np.zeros((hq, q.shape[1]), dtype=np.float64)
+    for h in range(hq):
+        kh = k_hat[h // grp]
+        logits = scale * (kh @ q[h])
+        m = logits.max()
+        w = np.exp(logits - m)
+        p = w / w.sum()
+        out[h] = p @ v_hat[h // grp]
+    return out
