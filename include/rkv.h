@@ -1,0 +1,186 @@
+/*
+ * rkv.h -- C ABI of librkv, the MI355X (gfx950) ResidualKV hot path.
+ *
+ * ResidualKV (also called DeltaKV) keeps a KV cache as two parts: a small set
+ * of uncompressed reference tokens, and, for every position, the residual of
+ * its K and V against the mean of its k nearest references, stored as
+ * quantised codes.  Attention rebuilds each token as reference mean plus
+ * residual while it reads the cache.
+ *
+ * Sources: "ResidualKV: Residual-Based KV Cache Compression for Efficient
+ * Long-Context Inference" (paper page), section "DeltaKV Framework
+ * Architecture" (strided reference selection, top-k nearest by L2 distance,
+ * mean reference KV_R, residual, reconstruction KV^ = KV^_delta + KV_R) and
+ * section "Practical Deployment via Sparse-vLLM" (a batched L2-distance
+ * search and a fused gather / mean / residual-add reconstruction);
+ * "New KV Cache Compression Method Cuts Long-Context Inference Costs by 85%",
+ * section "How ResidualKV Works" (quantised residual codes, on-the-fly
+ * reconstruction, dynamic-stride schedule).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them.  Scratch memory is the caller's
+ *     workspace, sized by the matching *_workspace query.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  The returned status reports argument validation and launch
+ *     errors only; a kernel fault shows up at the caller's next sync.
+ *   - Errors come back as rkv_status; nothing throws across the ABI.  After
+ *     RKV_ERR_HIP, rkv_last_hip_error() (thread-local) holds the hipError_t.
+ *   - Layouts are dense and row-major, innermost dimension last.
+ *     "inst" is an independent sequence-layer instance (batch x layers):
+ *     every instance has its own cache and its own references.
+ */
+#ifndef RKV_H
+#define RKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RKV_OK = 0,
+  RKV_ERR_INVALID_ARG = 1,  /* NULL pointer, bad shape, bad stride, ...    */
+  RKV_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head_dim != 128)  */
+  RKV_ERR_WORKSPACE = 3,    /* workspace smaller than the query returned    */
+  RKV_ERR_HIP = 4,          /* a HIP call failed; see rkv_last_hip_error()  */
+  RKV_ERR_RANGE = 5         /* more than 65535 references (uint16 slots)    */
+} rkv_status;
+
+typedef enum { RKV_F32 = 0, RKV_BF16 = 1 } rkv_dtype;
+
+/* Reference schedule.  Position j is a reference iff j mod s(j) == 0, where
+ * s(j) = base for j < double_after (or everywhere when double_after == 0),
+ * and for j >= double_after the stride doubles each time the position
+ * doubles: s = 2*base on [A, 2A), 4*base on [2A, 4A), ... (A = double_after).
+ * The fixed schedule is the paper page's strided reference selection; the
+ * doubling one is the news page's dynamic-stride schedule, whose reference
+ * count grows about logarithmically.  Requires base >= 1 and, when
+ * double_after > 0, double_after a multiple of 2*base. */
+typedef struct {
+  int32_t base;
+  int64_t double_after;
+} rkv_stride;
+
+/* Shape of a compressed cache and its device buffers (all caller-owned).
+ *
+ *   ref_idx  uint16 [inst][H][N][k]     slots (rank in the reference list) of
+ *                                       the k_eff nearest references of each
+ *                                       position, ascending, 0xFFFF padding
+ *                                       (k_eff = min(k, #references <= pos)).
+ *   codes_k  uint8  [inst][H][N][D*bits/8]
+ *                                       K residual codes, token-major: code of
+ *                                       dim t is a two's-complement field at
+ *                                       bits [t*bits, (t+1)*bits) of the row.
+ *            bits == 0: double [inst][H][N][D], the exact residual.
+ *   codes_v  uint8  [inst][H][ceil(N/32)][D][32*bits/8]
+ *                                       V residual codes, transposed per tile
+ *                                       of 32 positions: for each dim, the 32
+ *                                       codes of the tile form one bit string,
+ *                                       position u at bits [u*bits,(u+1)*bits);
+ *                                       positions past N are 0.
+ *            bits == 0: double [inst][H][N][D], the exact residual.
+ *   scales   uint16 [inst][H][N][2][D/group]   fp16 bit patterns, plane 0 = K,
+ *                                       1 = V.  Unused (may be NULL) when
+ *                                       bits == 0.
+ *   ref_kv   dtype  [inst][H][2][n_refs][D]    the uncompressed references
+ *                                       (plane 0 = K rows, 1 = V rows).
+ *
+ * Every position, references included, gets a record; decode and
+ * reconstruction read a reference position from ref_kv. */
+typedef struct {
+  rkv_dtype dtype;       /* K/V/q element type                                 */
+  int64_t n_inst;        /* independent instances (batch x layers)             */
+  int32_t n_kv_heads;    /* H                                                  */
+  int64_t seq_len;       /* N, positions per instance                          */
+  int32_t head_dim;      /* D; 128 is the supported value                      */
+  rkv_stride stride;     /* reference schedule                                 */
+  int32_t k;             /* nearest references averaged per token, 1..16       */
+  int32_t bits;          /* residual code width: 2, 4, 8, or 0 = no quantising */
+  int32_t group;         /* dims per fp16 scale: 32, 64 or 128 (divides D)     */
+  int64_t n_refs;        /* written by rkv_cache_init                          */
+  uint16_t *ref_idx;
+  uint8_t *codes_k;
+  uint8_t *codes_v;
+  uint16_t *scales;
+  void *ref_kv;
+} rkv_cache;
+
+/* Number of references below seq_len; -1 if the schedule is invalid. */
+int64_t rkv_num_refs(int64_t seq_len, rkv_stride stride);
+
+/* Position of reference `slot`; -1 if out of range or invalid. */
+int64_t rkv_ref_position(int64_t slot, rkv_stride stride);
+
+/* Validates the shape fields of *c and fills c->n_refs.  Pointers are not
+ * inspected.  RKV_ERR_RANGE if the schedule yields more than 65535
+ * references; RKV_ERR_UNSUPPORTED for head_dim != 128. */
+rkv_status rkv_cache_init(rkv_cache *c);
+
+/* Bytes of each cache buffer for the shape in *c (after rkv_cache_init):
+ * sizes[0..4] = ref_idx, codes_k, codes_v, scales, ref_kv. */
+rkv_status rkv_cache_sizes(const rkv_cache *c, size_t sizes[5]);
+
+/* Workspace bytes for rkv_encode / rkv_select_refs / rkv_quantize. */
+rkv_status rkv_encode_workspace(const rkv_cache *c, size_t *bytes);
+
+/* Encode: K, V dtype [inst][H][N][D] -> the compressed cache in *c.
+ * = rkv_select_refs followed by rkv_quantize on the same stream. */
+rkv_status rkv_encode(const void *K, const void *V, const rkv_cache *c,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* Reference selection ("Batch L2 distance" search of the paper page):
+ * writes ref_kv, and ref_idx as the k_eff references with the smallest
+ * squared L2 distance between bf16-rounded keys (ties: lower slot), found
+ * among the references at positions <= the token's own.  The distances are
+ * |k|^2 + |r|^2 - 2 k.r with bf16 products and fp32 accumulation; they never
+ * leave the chip.  Fills ws. */
+rkv_status rkv_select_refs(const void *K, const void *V, const rkv_cache *c,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* Residual quantisation with the indices already in c->ref_idx and the
+ * references in c->ref_kv (as rkv_select_refs leaves them): for each
+ * position and each of K and V, KV_R = the fp32 mean of its selected
+ * references (added in ascending slot order), residual = x - KV_R in fp32,
+ * and per group of `group` dims an fp16 scale nearest to max|residual|/qmax
+ * (qmax = 2^(bits-1)-1) and codes nearest to residual/scale (ties to even),
+ * clamped to +-qmax.  bits == 0 stores the exact residual in double.
+ * Writes codes_k, codes_v, scales.  ws is unused. */
+rkv_status rkv_quantize(const void *K, const void *V, const rkv_cache *c,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* Rebuild the cache: K_hat, V_hat float [inst][H][N][D].  Reference
+ * positions come back from ref_kv; others as KV_R + scale*code (or + the
+ * exact residual when bits == 0). */
+rkv_status rkv_reconstruct(const rkv_cache *c, float *K_hat, float *V_hat,
+                           void *stream);
+
+/* Workspace bytes for rkv_decode_attn with n_q_heads query heads and
+ * n_split partitions of the sequence per (instance, KV head). */
+rkv_status rkv_decode_workspace(const rkv_cache *c, int32_t n_q_heads,
+                                int32_t n_split, size_t *bytes);
+
+/* Decode attention straight from the compressed cache: one query per
+ * instance, q dtype [inst][n_q_heads][D]; query head h reads KV head
+ * h / (n_q_heads / H).  out float [inst][n_q_heads][D] =
+ * softmax(softmax_scale * q . K^) . V^ over all N positions, where K^, V^
+ * are the reconstructed cache.  The reference mean is folded into the dot
+ * products (q . KV_R is the mean of q . K_ref over the selected slots), so
+ * no K^/V^ is materialised.  n_split >= 1 partitions each sequence; the
+ * result does not depend on it beyond rounding.  bits must be 2, 4 or 8. */
+rkv_status rkv_decode_attn(const void *q, int32_t n_q_heads,
+                           const rkv_cache *c, float softmax_scale,
+                           float *out, int32_t n_split, void *ws,
+                           size_t ws_bytes, void *stream);
+
+const char *rkv_status_string(rkv_status s);
+int32_t rkv_last_hip_error(void);
+int32_t rkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RKV_H */

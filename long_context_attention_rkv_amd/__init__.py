@@ -1,0 +1,199 @@
+"""ResidualKV hot path for MI355X (gfx950): Python binding of librkv.
+
+Thin wrappers with the names of the C entry points in include/rkv.h.  They
+only marshal arguments: tensors become device pointers, the current torch
+stream becomes the HIP stream, and buffers of the right size come from
+torch's allocator.  Every step of the path runs in librkv's HIP kernels; if
+librkv.so is missing, every call raises.
+"""
+
+import ctypes as C
+
+import torch
+
+from . import _lib as L
+
+__all__ = [
+    "RkvError", "Cache", "rkv_num_refs", "rkv_ref_position", "rkv_encode",
+    "rkv_select_refs", "rkv_quantize", "rkv_reconstruct", "rkv_decode_attn",
+    "rkv_encode_workspace", "rkv_decode_workspace", "library_path",
+]
+
+_DT = {"f32": (L.RKV_F32, torch.float32), "bf16": (L.RKV_BF16, torch.bfloat16)}
+
+
+class RkvError(RuntimeError):
+    def __init__(self, msg, status):
+        super().__init__(msg)
+        self.status = status
+
+
+def library_path() -> str:
+    return L.LIB_PATH
+
+
+def _load():
+    return L.load()
+
+
+def _check(status: int, what: str):
+    if status != L.RKV_OK:
+        lib = _load()
+        msg = lib.rkv_status_string(status).decode()
+        if status == L.RKV_ERR_HIP:
+            msg += f" (hipError_t {lib.rkv_last_hip_error()})"
+        raise RkvError(f"{what}: {msg}", status)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else C.c_void_p(0)
+
+
+def _stride(base, double_after):
+    return L.RkvStride(int(base), int(double_after))
+
+
+def rkv_num_refs(seq_len: int, base: int, double_after: int = 0) -> int:
+    return int(_load().rkv_num_refs(int(seq_len), _stride(base, double_after)))
+
+
+def rkv_ref_position(slot: int, base: int, double_after: int = 0) -> int:
+    return int(_load().rkv_ref_position(int(slot), _stride(base, double_after)))
+
+
+class Cache:
+    """A compressed cache: the rkv_cache shape plus torch-owned device
+    buffers (ref_idx, codes_k, codes_v, scales, ref_kv) as raw bytes."""
+
+    BUFFERS = ("ref_idx", "codes_k", "codes_v", "scales", "ref_kv")
+
+    def __init__(self, n_inst, n_kv_heads, seq_len, dtype, stride_base, k, bits, group,
+                 double_after=0, head_dim=128, device="cuda", allocate=True):
+        self.dtype = dtype
+        self.torch_dtype = _DT[dtype][1]
+        s = L.RkvCache()
+        s.dtype = _DT[dtype][0]
+        s.n_inst = int(n_inst)
+        s.n_kv_heads = int(n_kv_heads)
+        s.seq_len = int(seq_len)
+        s.head_dim = int(head_dim)
+        s.stride = _stride(stride_base, double_after)
+        s.k = int(k)
+        s.bits = int(bits)
+        s.group = int(group)
+        _check(_load().rkv_cache_init(C.byref(s)), "rkv_cache_init")
+        self.c = s
+        sizes = (C.c_size_t * 5)()
+        _check(_load().rkv_cache_sizes(C.byref(s), sizes), "rkv_cache_sizes")
+        self.sizes = dict(zip(self.BUFFERS, [int(x) for x in sizes]))
+        self.buffers = {}
+        if allocate:
+            for name in self.BUFFERS:
+                t = torch.empty(max(1, self.sizes[name]), dtype=torch.uint8, device=device)
+                self.buffers[name] = t
+                setattr(s, name, t.data_ptr() if self.sizes[name] else None)
+
+    @property
+    def n_refs(self) -> int:
+        return int(self.c.n_refs)
+
+    def nbytes(self) -> int:
+        return sum(self.sizes.values())
+
+    def __getattr__(self, name):
+        b = self.__dict__.get("buffers", {})
+        if name in b:
+            return b[name]
+        raise AttributeError(name)
+
+
+def _ws(nbytes, device, ws):
+    if ws is None:
+        ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device=device)
+    return ws
+
+
+def rkv_encode_workspace(cache: Cache) -> int:
+    n = C.c_size_t()
+    _check(_load().rkv_encode_workspace(C.byref(cache.c), C.byref(n)), "rkv_encode_workspace")
+    return int(n.value)
+
+
+def rkv_decode_workspace(cache: Cache, n_q_heads: int, n_split: int) -> int:
+    n = C.c_size_t()
+    _check(_load().rkv_decode_workspace(C.byref(cache.c), int(n_q_heads), int(n_split),
+                                       C.byref(n)), "rkv_decode_workspace")
+    return int(n.value)
+
+
+def _check_kv(K, V, cache):
+    c = cache.c
+    want = (c.n_inst, c.n_kv_heads, c.seq_len, c.head_dim)
+    for name, t in (("K", K), ("V", V)):
+        if t.dtype != cache.torch_dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {cache.torch_dtype} device tensor")
+        if t.numel() != want[0] * want[1] * want[2] * want[3]:
+            raise ValueError(f"{name} must hold {want} elements")
+
+
+def rkv_encode(K, V, cache: Cache, ws=None, stream=None):
+    _check_kv(K, V, cache)
+    nb = rkv_encode_workspace(cache)
+    ws = _ws(nb, K.device, ws)
+    _check(_load().rkv_encode(_ptr(K), _ptr(V), C.byref(cache.c), _ptr(ws), ws.numel(),
+                             _stream(stream)), "rkv_encode")
+    return ws
+
+
+def rkv_select_refs(K, V, cache: Cache, ws=None, stream=None):
+    _check_kv(K, V, cache)
+    nb = rkv_encode_workspace(cache)
+    ws = _ws(nb, K.device, ws)
+    _check(_load().rkv_select_refs(_ptr(K), _ptr(V), C.byref(cache.c), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "rkv_select_refs")
+    return ws
+
+
+def rkv_quantize(K, V, cache: Cache, stream=None):
+    _check_kv(K, V, cache)
+    _check(_load().rkv_quantize(_ptr(K), _ptr(V), C.byref(cache.c), C.c_void_p(0), 0,
+                               _stream(stream)), "rkv_quantize")
+
+
+def rkv_reconstruct(cache: Cache, K_hat=None, V_hat=None, stream=None):
+    c = cache.c
+    shape = (c.n_inst, c.n_kv_heads, c.seq_len, c.head_dim)
+    dev = cache.buffers["ref_kv"].device
+    if K_hat is None:
+        K_hat = torch.empty(shape, dtype=torch.float32, device=dev)
+        V_hat = torch.empty(shape, dtype=torch.float32, device=dev)
+    for t in (K_hat, V_hat):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != K_hat.numel():
+            raise ValueError("K_hat/V_hat must be contiguous float32 of the cache shape")
+    _check(_load().rkv_reconstruct(C.byref(c), _ptr(K_hat), _ptr(V_hat), _stream(stream)),
+           "rkv_reconstruct")
+    return K_hat, V_hat
+
+
+def rkv_decode_attn(q, n_q_heads: int, cache: Cache, softmax_scale: float, out=None,
+                    n_split: int = 1, ws=None, stream=None):
+    c = cache.c
+    if q.dtype != cache.torch_dtype or not q.is_cuda or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous {cache.torch_dtype} device tensor")
+    if q.numel() != c.n_inst * n_q_heads * c.head_dim:
+        raise ValueError("q must hold n_inst * n_q_heads * head_dim elements")
+    if out is None:
+        out = torch.empty((c.n_inst, n_q_heads, c.head_dim), dtype=torch.float32,
+                          device=q.device)
+    nb = rkv_decode_workspace(cache, n_q_heads, n_split)
+    ws = _ws(nb, q.device, ws)
+    _check(_load().rkv_decode_attn(_ptr(q), int(n_q_heads), C.byref(c), float(softmax_scale),
+                                  _ptr(out), int(n_split), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "rkv_decode_attn")
+    return out

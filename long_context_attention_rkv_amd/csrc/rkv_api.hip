@@ -1,0 +1,254 @@
+// Host side of librkv: argument checks, buffer sizes and kernel dispatch.
+// The entry points are declared (and documented) in include/rkv.h.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/rkv.h"
+#include "rkv_common.h"
+
+namespace rkv {
+hipError_t launch_refstore(int dtype, const void* K, const void* V, void* ref_kv, void* refkey,
+                           float* refnorm, int64_t n_inst, int H, int64_t N, int64_t n_refs,
+                           Sched sc, hipStream_t st);
+hipError_t launch_dist_topk(int dtype, const void* K, const void* refkey, const float* refnorm,
+                            uint16_t* idx, int64_t n_inst, int H, int64_t N, int64_t n_refs,
+                            Sched sc, int k, hipStream_t st);
+hipError_t launch_quantize(int dtype, int bits, const void* K, const void* V,
+                           const uint16_t* idx, const void* ref_kv, uint8_t* ck, uint8_t* cv,
+                           uint16_t* sc16, int64_t n_inst, int H, int64_t N, int64_t n_refs,
+                           Sched sc, int k, int group, hipStream_t st);
+hipError_t launch_reconstruct(int dtype, int bits, const uint16_t* idx, const void* ref_kv,
+                              const uint8_t* ck, const uint8_t* cv, const uint16_t* sc16,
+                              float* Kh, float* Vh, int64_t n_inst, int H, int64_t N,
+                              int64_t n_refs, Sched sc, int k, int group, hipStream_t st);
+hipError_t launch_decode(int dtype, int bits, const void* q, int n_q_heads, const uint16_t* idx,
+                         const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
+                         const uint16_t* sc16, float softmax_scale, float* out, int n_split,
+                         void* ws, int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
+                         int k, int group, hipStream_t st);
+size_t decode_ws_bytes(int64_t n_inst, int H, int n_q_heads, int n_split, int64_t n_refs);
+}  // namespace rkv
+
+using rkv::Sched;
+
+namespace {
+
+thread_local int32_t g_last_hip = 0;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool sched_ok(rkv_stride s) {
+  if (s.base < 1) return false;
+  if (s.double_after < 0) return false;
+  if (s.double_after > 0 && s.double_after % (2 * (int64_t)s.base) != 0) return false;
+  return true;
+}
+
+Sched to_sched(rkv_stride s) { return Sched{s.base, s.double_after}; }
+
+rkv_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return RKV_OK;
+  g_last_hip = (int32_t)e;
+  return RKV_ERR_HIP;
+}
+
+size_t elt_bytes(rkv_dtype d) { return d == RKV_F32 ? 4 : 2; }
+
+rkv_status check_shape(const rkv_cache* c) {
+  if (!c) return RKV_ERR_INVALID_ARG;
+  if (c->dtype != RKV_F32 && c->dtype != RKV_BF16) return RKV_ERR_INVALID_ARG;
+  if (c->n_inst < 0 || c->n_kv_heads < 1 || c->seq_len < 0) return RKV_ERR_INVALID_ARG;
+  if (c->n_inst > 65535 || c->n_kv_heads > 65535) return RKV_ERR_INVALID_ARG;
+  if (!sched_ok(c->stride)) return RKV_ERR_INVALID_ARG;
+  if (c->k < 1 || c->k > 16) return RKV_ERR_INVALID_ARG;
+  if (c->bits != 0 && c->bits != 2 && c->bits != 4 && c->bits != 8) return RKV_ERR_INVALID_ARG;
+  if (c->head_dim != 128) return c->head_dim > 0 ? RKV_ERR_UNSUPPORTED : RKV_ERR_INVALID_ARG;
+  if (c->bits != 0) {
+    if (c->group != 32 && c->group != 64 && c->group != 128) return RKV_ERR_INVALID_ARG;
+  }
+  const int64_t nr = rkv::sched_count(c->seq_len, to_sched(c->stride));
+  if (nr > 65535) return RKV_ERR_RANGE;
+  return RKV_OK;
+}
+
+rkv_status check_ready(const rkv_cache* c) {
+  rkv_status s = check_shape(c);
+  if (s != RKV_OK) return s;
+  if (c->n_refs != rkv::sched_count(c->seq_len, to_sched(c->stride))) return RKV_ERR_INVALID_ARG;
+  if (c->n_inst == 0 || c->seq_len == 0) return RKV_OK;
+  if (!c->ref_idx || !c->codes_k || !c->codes_v || !c->ref_kv) return RKV_ERR_INVALID_ARG;
+  if (c->bits != 0 && !c->scales) return RKV_ERR_INVALID_ARG;
+  return RKV_OK;
+}
+
+void sizes_of(const rkv_cache* c, size_t out[5]) {
+  const size_t ih = (size_t)c->n_inst * c->n_kv_heads;
+  const size_t N = (size_t)c->seq_len;
+  const size_t D = (size_t)c->head_dim;
+  out[0] = ih * N * c->k * 2;
+  if (c->bits == 0) {
+    out[1] = ih * N * D * 8;
+    out[2] = ih * N * D * 8;
+    out[3] = 0;
+  } else {
+    out[1] = ih * N * D * c->bits / 8;
+    out[2] = ih * ((N + 31) / 32) * D * (32 * c->bits / 8);
+    out[3] = ih * N * 2 * (D / c->group) * 2;
+  }
+  out[4] = ih * 2 * (size_t)c->n_refs * D * elt_bytes(c->dtype);
+}
+
+size_t encode_ws(const rkv_cache* c) {
+  const size_t nr = (size_t)c->n_inst * c->n_kv_heads * c->n_refs;
+  return align_up(nr * 128 * 2) + align_up(nr * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t rkv_num_refs(int64_t seq_len, rkv_stride stride) {
+  if (!sched_ok(stride) || seq_len < 0) return -1;
+  return rkv::sched_count(seq_len, to_sched(stride));
+}
+
+int64_t rkv_ref_position(int64_t slot, rkv_stride stride) {
+  if (!sched_ok(stride) || slot < 0) return -1;
+  return rkv::sched_pos(slot, to_sched(stride));
+}
+
+rkv_status rkv_cache_init(rkv_cache* c) {
+  rkv_status s = check_shape(c);
+  if (s != RKV_OK) return s;
+  c->n_refs = rkv::sched_count(c->seq_len, to_sched(c->stride));
+  return RKV_OK;
+}
+
+rkv_status rkv_cache_sizes(const rkv_cache* c, size_t sizes[5]) {
+  if (!sizes) return RKV_ERR_INVALID_ARG;
+  rkv_status s = check_shape(c);
+  if (s != RKV_OK) return s;
+  if (c->n_refs != rkv::sched_count(c->seq_len, to_sched(c->stride))) return RKV_ERR_INVALID_ARG;
+  sizes_of(c, sizes);
+  return RKV_OK;
+}
+
+rkv_status rkv_encode_workspace(const rkv_cache* c, size_t* bytes) {
+  if (!bytes) return RKV_ERR_INVALID_ARG;
+  rkv_status s = check_shape(c);
+  if (s != RKV_OK) return s;
+  if (c->n_refs != rkv::sched_count(c->seq_len, to_sched(c->stride))) return RKV_ERR_INVALID_ARG;
+  *bytes = encode_ws(c);
+  return RKV_OK;
+}
+
+rkv_status rkv_select_refs(const void* K, const void* V, const rkv_cache* c, void* ws,
+                           size_t ws_bytes, void* stream) {
+  rkv_status s = check_ready(c);
+  if (s != RKV_OK) return s;
+  if (c->n_inst == 0 || c->seq_len == 0) return RKV_OK;
+  if (!K || !V) return RKV_ERR_INVALID_ARG;
+  const size_t need = encode_ws(c);
+  if (!ws || ws_bytes < need) return RKV_ERR_WORKSPACE;
+  const size_t nr = (size_t)c->n_inst * c->n_kv_heads * c->n_refs;
+  char* refkey = (char*)ws;
+  float* refnorm = (float*)((char*)ws + align_up(nr * 128 * 2));
+  hipStream_t st = (hipStream_t)stream;
+  const Sched sc = to_sched(c->stride);
+  hipError_t e = rkv::launch_refstore((int)c->dtype, K, V, c->ref_kv, refkey, refnorm, c->n_inst,
+                                      c->n_kv_heads, c->seq_len, c->n_refs, sc, st);
+  if (e != hipSuccess) return hip_status(e);
+  e = rkv::launch_dist_topk((int)c->dtype, K, refkey, refnorm, c->ref_idx, c->n_inst,
+                            c->n_kv_heads, c->seq_len, c->n_refs, sc, c->k, st);
+  return hip_status(e);
+}
+
+rkv_status rkv_quantize(const void* K, const void* V, const rkv_cache* c, void* ws,
+                        size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  rkv_status s = check_ready(c);
+  if (s != RKV_OK) return s;
+  if (c->n_inst == 0 || c->seq_len == 0) return RKV_OK;
+  if (!K || !V) return RKV_ERR_INVALID_ARG;
+  hipError_t e = rkv::launch_quantize((int)c->dtype, c->bits, K, V, c->ref_idx, c->ref_kv,
+                                      c->codes_k, c->codes_v, c->scales, c->n_inst,
+                                      c->n_kv_heads, c->seq_len, c->n_refs,
+                                      to_sched(c->stride), c->k, c->group, (hipStream_t)stream);
+  return hip_status(e);
+}
+
+rkv_status rkv_encode(const void* K, const void* V, const rkv_cache* c, void* ws,
+                      size_t ws_bytes, void* stream) {
+  rkv_status s = rkv_select_refs(K, V, c, ws, ws_bytes, stream);
+  if (s != RKV_OK) return s;
+  return rkv_quantize(K, V, c, ws, ws_bytes, stream);
+}
+
+rkv_status rkv_reconstruct(const rkv_cache* c, float* K_hat, float* V_hat, void* stream) {
+  rkv_status s = check_ready(c);
+  if (s != RKV_OK) return s;
+  if (c->n_inst == 0 || c->seq_len == 0) return RKV_OK;
+  if (!K_hat || !V_hat) return RKV_ERR_INVALID_ARG;
+  hipError_t e = rkv::launch_reconstruct((int)c->dtype, c->bits, c->ref_idx, c->ref_kv,
+                                         c->codes_k, c->codes_v, c->scales, K_hat, V_hat,
+                                         c->n_inst, c->n_kv_heads, c->seq_len, c->n_refs,
+                                         to_sched(c->stride), c->k, c->group,
+                                         (hipStream_t)stream);
+  return hip_status(e);
+}
+
+rkv_status rkv_decode_workspace(const rkv_cache* c, int32_t n_q_heads, int32_t n_split,
+                                size_t* bytes) {
+  if (!bytes) return RKV_ERR_INVALID_ARG;
+  rkv_status s = check_shape(c);
+  if (s != RKV_OK) return s;
+  if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0 || n_split < 1 || n_split > 4096)
+    return RKV_ERR_INVALID_ARG;
+  *bytes = rkv::decode_ws_bytes(c->n_inst, c->n_kv_heads, n_q_heads, n_split,
+                                rkv::sched_count(c->seq_len, to_sched(c->stride)));
+  return RKV_OK;
+}
+
+rkv_status rkv_decode_attn(const void* q, int32_t n_q_heads, const rkv_cache* c,
+                           float softmax_scale, float* out, int32_t n_split, void* ws,
+                           size_t ws_bytes, void* stream) {
+  rkv_status s = check_ready(c);
+  if (s != RKV_OK) return s;
+  if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0 || n_split < 1 || n_split > 4096)
+    return RKV_ERR_INVALID_ARG;
+  if (c->bits == 0) return RKV_ERR_UNSUPPORTED;
+  const int G = n_q_heads / c->n_kv_heads;
+  if (G * (c->head_dim / c->group) > 16) return RKV_ERR_UNSUPPORTED;
+  if (c->n_inst == 0) return RKV_OK;
+  if (!q || !out) return RKV_ERR_INVALID_ARG;
+  if (c->seq_len == 0) return RKV_ERR_INVALID_ARG;
+  const size_t need = rkv::decode_ws_bytes(c->n_inst, c->n_kv_heads, n_q_heads, n_split, c->n_refs);
+  if (!ws || ws_bytes < need) return RKV_ERR_WORKSPACE;
+  hipError_t e = rkv::launch_decode((int)c->dtype, c->bits, q, n_q_heads, c->ref_idx, c->ref_kv,
+                                    c->codes_k, c->codes_v, c->scales, softmax_scale, out,
+                                    n_split, ws, c->n_inst, c->n_kv_heads, c->seq_len,
+                                    c->n_refs, to_sched(c->stride), c->k, c->group,
+                                    (hipStream_t)stream);
+  return hip_status(e);
+}
+
+const char* rkv_status_string(rkv_status s) {
+  switch (s) {
+    case RKV_OK: return "ok";
+    case RKV_ERR_INVALID_ARG: return "invalid argument";
+    case RKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case RKV_ERR_WORKSPACE: return "workspace too small";
+    case RKV_ERR_HIP: return "HIP error";
+    case RKV_ERR_RANGE: return "more than 65535 references";
+  }
+  return "unknown status";
+}
+
+int32_t rkv_last_hip_error(void) { return g_last_hip; }
+
+int32_t rkv_version(void) { return 1; }
+
+}  // extern "C"

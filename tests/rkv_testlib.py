@@ -1,0 +1,132 @@
+"""Helpers shared by the test files: reading the library's output buffers
+back into plain arrays (following the layouts documented in include/rkv.h),
+and the parity comparisons against the oracle."""
+
+import numpy as np
+import torch
+
+import oracle
+
+
+def to_np_f32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+def buf_u16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy().view(np.uint16)
+
+
+def sign_extend(v: np.ndarray, bits: int) -> np.ndarray:
+    v = v.astype(np.int64)
+    return np.where(v >= (1 << (bits - 1)), v - (1 << bits), v)
+
+
+def unpack_rows(b: np.ndarray, bits: int) -> np.ndarray:
+    """uint8 [..., nbytes] token-major bit strings -> int [..., nbytes*8/bits]."""
+    b = b.astype(np.int64)
+    per = 8 // bits
+    fields = [(b >> (bits * j)) & ((1 << bits) - 1) for j in range(per)]
+    out = np.stack(fields, axis=-1).reshape(*b.shape[:-1], b.shape[-1] * per)
+    return sign_extend(out, bits)
+
+
+class GpuCache:
+    """Host copy of a library cache, one (instance, head) at a time."""
+
+    def __init__(self, cache):
+        c = cache.c
+        self.n_inst, self.H, self.N, self.D = c.n_inst, c.n_kv_heads, c.seq_len, c.head_dim
+        self.k, self.bits, self.group, self.n_refs = c.k, c.bits, c.group, c.n_refs
+        self.dtype = cache.dtype
+        ih = self.n_inst * self.H
+        self.idx = buf_u16(cache.ref_idx)[: ih * self.N * self.k].reshape(ih, self.N, self.k)
+        self.tiles = (self.N + 31) // 32
+        if self.bits:
+            ck = cache.codes_k.cpu().numpy()[: cache.sizes["codes_k"]]
+            self.codes_k_bytes = ck.reshape(ih, self.N, 16 * self.bits)
+            cv = cache.codes_v.cpu().numpy()[: cache.sizes["codes_v"]]
+            self.codes_v_bytes = cv.reshape(ih, self.tiles, self.D, 4 * self.bits)
+            ng = self.D // self.group
+            self.scales = buf_u16(cache.scales)[: ih * self.N * 2 * ng].reshape(
+                ih, self.N, 2, ng).view(np.float16)
+        else:
+            ck = cache.codes_k.cpu().numpy()[: cache.sizes["codes_k"]].view(np.float64)
+            cv = cache.codes_v.cpu().numpy()[: cache.sizes["codes_v"]].view(np.float64)
+            self.resid = np.stack([ck.reshape(ih, self.N, self.D),
+                                   cv.reshape(ih, self.N, self.D)], axis=2)
+        rk = cache.ref_kv.cpu()
+        if self.dtype == "bf16":
+            rk = rk[: cache.sizes["ref_kv"]].view(torch.bfloat16).float().numpy()
+        else:
+            rk = rk[: cache.sizes["ref_kv"]].view(torch.float32).numpy()
+        self.ref_kv = rk.reshape(ih, 2, self.n_refs, self.D)
+
+    def codes(self, ih: int) -> np.ndarray:
+        """int [N, 2, D] codes of one (instance, head)."""
+        k = unpack_rows(self.codes_k_bytes[ih], self.bits)               # [N, D]
+        v = unpack_rows(self.codes_v_bytes[ih], self.bits)               # [tiles, D, 32]
+        v = v.transpose(0, 2, 1).reshape(self.tiles * 32, self.D)[: self.N]
+        return np.stack([k, v], axis=1)
+
+
+def near_tie_ok(keys_bf16, T, i, gpu_sel, ora_sel, rel=1e-5):
+    """Mismatched reference sets of token i are acceptable only as near-ties:
+    the extra GPU picks and the missed oracle picks, matched by rank, have
+    exact distances within rel * max(D_a, D_b, |k_i|^2)."""
+    ki = keys_bf16[i].astype(np.float64)
+    d = lambda s: float(((keys_bf16[T[s]].astype(np.float64) - ki) ** 2).sum())
+    extra = sorted(set(gpu_sel) - set(ora_sel), key=d)
+    missed = sorted(set(ora_sel) - set(gpu_sel), key=d)
+    if len(extra) != len(missed):
+        return False
+    floor = float((ki * ki).sum())
+    for a, b in zip(extra, missed):
+        da, db = d(a), d(b)
+        if abs(da - db) > rel * max(da, db, floor):
+            return False
+    return True
+
+
+def compare_encode(gc: GpuCache, ih: int, K: np.ndarray, V: np.ndarray, stride_base,
+                   double_after, rows=None):
+    """Compare one (instance, head) of a GPU cache with the oracle on `rows`.
+
+    Returns a dict of counts; raises AssertionError on any failure."""
+    enc = oracle.encode(K, V, stride_base, double_after, gc.k, gc.bits, gc.group, rows=rows)
+    T = enc["T"]
+    assert T.shape[0] == gc.n_refs
+    # the reference store is an exact copy
+    np.testing.assert_array_equal(gc.ref_kv[ih, 0], K[T])
+    np.testing.assert_array_equal(gc.ref_kv[ih, 1], V[T])
+    keys = oracle.bf16_round(K)
+    rows_ = enc["rows"]
+    gidx = gc.idx[ih][rows_]
+    match = np.all(gidx == enc["idx"], axis=1)
+    near = 0
+    for r in np.nonzero(~match)[0]:
+        i = int(rows_[r])
+        gsel = [int(x) for x in gidx[r] if x != 0xFFFF]
+        osel = [int(x) for x in enc["idx"][r] if x != 0xFFFF]
+        assert gidx[r].tolist()[len(gsel):] == [0xFFFF] * (gc.k - len(gsel)), (i, gidx[r])
+        assert gsel == sorted(gsel) and len(gsel) == len(osel), (i, gsel, osel)
+        assert near_tie_ok(keys, T, i, gsel, osel), (i, gsel, osel)
+        near += 1
+    m = np.nonzero(match)[0]
+    if gc.bits:
+        codes = gc.codes(ih)[rows_]
+        sc = gc.scales[ih][rows_]
+        bad_s = np.nonzero(np.any(sc[m].view(np.uint16) != enc["scales"][m].view(np.uint16),
+                                  axis=(1, 2)))[0]
+        assert bad_s.size == 0, f"scale mismatch at rows {rows_[m][bad_s][:10]}"
+        bad_c = np.nonzero(np.any(codes[m] != enc["codes"][m], axis=(1, 2)))[0]
+        assert bad_c.size == 0, f"code mismatch at rows {rows_[m][bad_c][:10]}"
+    else:
+        res = gc.resid[ih][rows_]
+        np.testing.assert_array_equal(res[m], enc["resid64"][m])
+    return {"rows": len(rows_), "near_ties": near, "enc": enc, "matched": match}
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))

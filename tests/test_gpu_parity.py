@@ -1,0 +1,291 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars (from the method's contract):
+  * reference sets bit-exact except counted near-ties (exact distance gap
+    within 1e-5 relative, floored at |k_i|^2);
+  * codes and scales bit-exact on every token whose set matches;
+  * reference store bit-exact;
+  * reconstruction within 1e-5 relative L2 (fp32 arithmetic);
+  * decode attention within 2e-3 relative L2.
+Inputs are the seeded prototype-mixture caches of the workloads (or smaller
+slices of them); the oracle reads the very tensors the GPU consumed.
+"""
+
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import gpu_available
+from rkv_testlib import GpuCache, compare_encode, rel_l2, to_np_f32
+from synth import gen_head_kv, gen_queries, get_config
+
+pytestmark = pytest.mark.gpu
+
+if gpu_available():
+    import long_context_attention_rkv_amd as rkv
+
+
+def _need_gpu():
+    if not gpu_available():
+        pytest.skip("no GPU")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def make_kv(cfg, n_inst, seq_len, device="cuda"):
+    """[n_inst, H, N, D] K and V; instance i = (layer i // batch, seq i % batch)."""
+    dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    K = torch.empty(n_inst, cfg.n_kv_heads, seq_len, cfg.head_dim, dtype=dt, device=device)
+    V = torch.empty_like(K)
+    for i in range(n_inst):
+        layer, seq = divmod(i, max(cfg.batch, 1))
+        for h in range(cfg.n_kv_heads):
+            k, v = gen_head_kv(cfg, layer, seq, h, device=device, seq_len=seq_len)
+            K[i, h].copy_(k)
+            V[i, h].copy_(v)
+    return K, V
+
+
+def make_q(cfg, n_inst, device="cuda"):
+    return torch.stack([gen_queries(cfg, *divmod(i, max(cfg.batch, 1)), device=device)
+                        for i in range(n_inst)])
+
+
+def encode(cfg, K, V, bits, n_inst, seq_len):
+    cache = rkv.Cache(n_inst, cfg.n_kv_heads, seq_len, cfg.dtype, cfg.stride_base, cfg.k,
+                      bits, cfg.group, double_after=cfg.double_after)
+    rkv.rkv_encode(K, V, cache)
+    torch.cuda.synchronize()
+    return cache
+
+
+def _cfg(index, **kw):
+    return dataclasses.replace(get_config(index), **kw)
+
+
+# (id, config, bits, n_inst, seq_len)
+SMALL = [
+    ("tiny_int8_f32", get_config(0), 8, 1, 1024),
+    ("tiny_int4_f32_ragged", _cfg(0, n_kv_heads=2), 4, 2, 999),
+    ("llama_int4_bf16_ragged", _cfg(1, n_kv_heads=2), 4, 1, 1000),
+    ("stress_int2_k16", _cfg(4, n_kv_heads=2, batch=2), 2, 2, 777),
+    ("stress_int4_k16", _cfg(4, n_kv_heads=2, batch=2), 4, 2, 777),
+    ("dynamic_int4", _cfg(3, n_kv_heads=2, double_after=512, drift_block=128), 4, 1, 2600),
+    ("bf16_int8_g128", _cfg(1, n_kv_heads=1, group=128), 8, 1, 600),
+    ("edge_k_exceeds_refs", _cfg(1, n_kv_heads=1, stride_base=64, k=16), 4, 1, 200),
+    ("edge_one_token", _cfg(1, n_kv_heads=1), 4, 1, 1),
+    ("edge_33_tokens", _cfg(0, n_kv_heads=1, stride_base=5, k=3), 8, 1, 33),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_encode_parity_small(case):
+    _need_gpu()
+    name, cfg, bits, n_inst, N = case
+    say(f"[encode parity] {name}: N={N} H={cfg.n_kv_heads} inst={n_inst} bits={bits}")
+    K, V = make_kv(cfg, n_inst, N)
+    cache = encode(cfg, K, V, bits, n_inst, N)
+    gc = GpuCache(cache)
+    Kn, Vn = to_np_f32(K), to_np_f32(V)
+    near = 0
+    for i in range(n_inst):
+        for h in range(cfg.n_kv_heads):
+            r = compare_encode(gc, i * cfg.n_kv_heads + h, Kn[i, h], Vn[i, h],
+                               cfg.stride_base, cfg.double_after)
+            near += r["near_ties"]
+    say(f"  near-ties: {near} of {n_inst * cfg.n_kv_heads * N} tokens")
+
+
+@pytest.mark.parametrize("case", SMALL[:6], ids=[c[0] for c in SMALL[:6]])
+def test_reconstruct_parity_small(case):
+    _need_gpu()
+    name, cfg, bits, n_inst, N = case
+    say(f"[reconstruct parity] {name}")
+    K, V = make_kv(cfg, n_inst, N)
+    cache = encode(cfg, K, V, bits, n_inst, N)
+    Kh, Vh = rkv.rkv_reconstruct(cache)
+    torch.cuda.synchronize()
+    Khn, Vhn = Kh.cpu().numpy(), Vh.cpu().numpy()
+    gc = GpuCache(cache)
+    Kn, Vn = to_np_f32(K), to_np_f32(V)
+    for i in range(n_inst):
+        for h in range(cfg.n_kv_heads):
+            r = compare_encode(gc, i * cfg.n_kv_heads + h, Kn[i, h], Vn[i, h],
+                               cfg.stride_base, cfg.double_after)
+            kv = oracle.reconstruct(r["enc"], Kn[i, h], Vn[i, h], bits)
+            m = r["matched"]
+            assert rel_l2(Khn[i, h][m], kv[m, 0]) <= 1e-5
+            assert rel_l2(Vhn[i, h][m], kv[m, 1]) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_no_quantisation_is_lossless(dtype):
+    _need_gpu()
+    cfg = _cfg(1, n_kv_heads=2, dtype=dtype)
+    say(f"[bits=0] {dtype}")
+    K, V = make_kv(cfg, 1, 700)
+    cache = encode(cfg, K, V, 0, 1, 700)
+    gc = GpuCache(cache)
+    Kn, Vn = to_np_f32(K), to_np_f32(V)
+    for h in range(2):
+        compare_encode(gc, h, Kn[0, h], Vn[0, h], cfg.stride_base, 0)
+    Kh, Vh = rkv.rkv_reconstruct(cache)
+    torch.cuda.synchronize()
+    # the exact residual rebuilds every position bit for bit
+    assert torch.equal(Kh, K.float()) and torch.equal(Vh, V.float())
+
+
+def test_stride1_k1_gives_zero_residuals():
+    _need_gpu()
+    cfg = _cfg(1, n_kv_heads=2, stride_base=1, k=1)
+    say("[stride 1, k 1]")
+    K, V = make_kv(cfg, 1, 300)
+    cache = encode(cfg, K, V, 4, 1, 300)
+    gc = GpuCache(cache)
+    assert np.array_equal(gc.idx[:, :, 0], np.tile(np.arange(300), (2, 1)))
+    for ih in range(2):
+        assert np.all(gc.codes(ih) == 0)
+    assert np.all(gc.scales.view(np.uint16) == 0)
+
+
+def test_encode_is_deterministic():
+    _need_gpu()
+    cfg = _cfg(1, n_kv_heads=4)
+    say("[determinism]")
+    K, V = make_kv(cfg, 1, 2048)
+    c1 = encode(cfg, K, V, 4, 1, 2048)
+    c2 = encode(cfg, K, V, 4, 1, 2048)
+    for name in rkv.Cache.BUFFERS:
+        assert torch.equal(c1.buffers[name], c2.buffers[name]), name
+
+
+# ------------------------------------------------------------------ decode
+
+DECODE = [
+    ("tiny", get_config(0), 8, 1, 1024),
+    ("llama_ragged", _cfg(1, n_kv_heads=2, n_q_heads=8), 4, 1, 1000),
+    ("llama_int8", _cfg(1, n_kv_heads=2, n_q_heads=8), 8, 1, 640),
+    ("gqa7_g64_int2", _cfg(4, n_kv_heads=2, n_q_heads=14, batch=1), 2, 2, 500),
+    ("gqa7_g64_int4", _cfg(4, n_kv_heads=2, n_q_heads=14, batch=1), 4, 1, 500),
+    ("g128_gqa4", _cfg(1, n_kv_heads=1, n_q_heads=4, group=128), 4, 1, 300),
+]
+
+
+def _oracle_decode(cfg, K, V, q, bits, scale):
+    n_inst, H = K.shape[0], K.shape[1]
+    out = np.zeros((n_inst, q.shape[1], q.shape[2]))
+    for i in range(n_inst):
+        kh, vh = [], []
+        for h in range(H):
+            enc = oracle.encode(K[i, h], V[i, h], cfg.stride_base, cfg.double_after, cfg.k,
+                                bits, cfg.group)
+            kv = oracle.reconstruct(enc, K[i, h], V[i, h], bits)
+            kh.append(kv[:, 0])
+            vh.append(kv[:, 1])
+        out[i] = oracle.decode_attn(q[i], np.stack(kh), np.stack(vh), scale)
+    return out
+
+
+@pytest.mark.parametrize("case", DECODE, ids=[c[0] for c in DECODE])
+def test_decode_parity(case):
+    _need_gpu()
+    name, cfg, bits, n_inst, N = case
+    say(f"[decode parity] {name}: N={N} Hkv={cfg.n_kv_heads} Hq={cfg.n_q_heads} bits={bits}")
+    K, V = make_kv(cfg, n_inst, N)
+    q = make_q(cfg, n_inst)
+    cache = encode(cfg, K, V, bits, n_inst, N)
+    Kn, Vn, qn = to_np_f32(K), to_np_f32(V), to_np_f32(q)
+    for scale in (1.0 / math.sqrt(cfg.head_dim), 1.0):
+        got = rkv.rkv_decode_attn(q, cfg.n_q_heads, cache, scale, n_split=3)
+        torch.cuda.synchronize()
+        want = _oracle_decode(cfg, Kn, Vn, qn, bits, scale)
+        err = rel_l2(got.cpu().numpy(), want)
+        say(f"  scale={scale:.4f} rel L2 = {err:.2e}")
+        assert err <= 2e-3
+
+
+def test_decode_split_invariance():
+    _need_gpu()
+    cfg = _cfg(1, n_kv_heads=2, n_q_heads=8)
+    say("[decode split invariance]")
+    K, V = make_kv(cfg, 2, 3000)
+    q = make_q(cfg, 2)
+    cache = encode(cfg, K, V, 4, 2, 3000)
+    outs = [rkv.rkv_decode_attn(q, 8, cache, 1.0, n_split=s).cpu().numpy()
+            for s in (1, 2, 7, 40, 200)]
+    # The P.V product rounds each p*scale operand to fp16 (relative error
+    # <= 2^-11) against a running maximum that depends on the split, so two
+    # split counts may differ by up to 2 * 2^-11 relative in the worst
+    # (fully aligned) case; random rounding keeps it near 1e-4.
+    for o in outs[1:]:
+        assert rel_l2(o, outs[0]) <= 2 * 2.0 ** -11
+
+
+# ------------------------------------------------------------------ full sizes
+# The workloads at their real per-instance shapes, in the launch
+# configuration the benchmark times; the oracle checks sampled tokens.
+
+FULL = [
+    ("llama3_8b_layer", 1, 4, 1),
+    ("llama3_8b_32k_one_instance", 2, 4, 1),
+    ("dynamic_131k", 3, 4, 1),
+    ("prefill_stress_int4", 4, 4, 1),
+    ("prefill_stress_int2", 4, 2, 1),
+]
+
+
+def _sample_rows(N, n, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 2, 31, 32, 63, 64, 127, 128, N // 2, N - 129, N - 65, N - 33, N - 2, N - 1]
+    rows = set(r for r in fixed if 0 <= r < N)
+    rows.update(rng.integers(0, N, n).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("case", FULL, ids=[c[0] for c in FULL])
+def test_full_size_sampled_encode(case):
+    _need_gpu()
+    name, index, bits, n_inst = case
+    cfg = get_config(index)
+    N = cfg.seq_len
+    say(f"[full-size encode] {name}: N={N} H={cfg.n_kv_heads} inst={n_inst} bits={bits}")
+    K, V = make_kv(cfg, n_inst, N)
+    cache = encode(cfg, K, V, bits, n_inst, N)
+    gc = GpuCache(cache)
+    near = 0
+    for h in range(cfg.n_kv_heads):
+        Kn = to_np_f32(K[0, h])
+        Vn = to_np_f32(V[0, h])
+        rows = _sample_rows(N, 40, h)
+        near += compare_encode(gc, h, Kn, Vn, cfg.stride_base, cfg.double_after,
+                               rows=rows)["near_ties"]
+    say(f"  near-ties: {near}")
+
+
+@pytest.mark.parametrize("index", [1, 2])
+def test_full_size_decode_one_kv_head(index):
+    """Decode at the full context of the workload for all query heads of KV
+    head 0 (the oracle rebuilds that head completely)."""
+    _need_gpu()
+    cfg = get_config(index)
+    N = cfg.seq_len
+    say(f"[full-size decode] {cfg.name}: N={N}")
+    K, V = make_kv(cfg, 1, N)
+    q = make_q(cfg, 1)
+    cache = encode(cfg, K, V, 4, 1, N)
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    got = rkv.rkv_decode_attn(q, cfg.n_q_heads, cache, scale, n_split=16).cpu().numpy()
+    G = cfg.n_q_heads // cfg.n_kv_heads
+    Kn, Vn = to_np_f32(K[0, 0]), to_np_f32(V[0, 0])
+    enc = oracle.encode(Kn, Vn, cfg.stride_base, cfg.double_after, cfg.k, 4, cfg.group)
+    kv = oracle.reconstruct(enc, Kn, Vn, 4)
+    want = oracle.decode_attn(to_np_f32(q[0, :G]), kv[None, :, 0], kv[None, :, 1], scale)
+    err = rel_l2(got[0, :G], want)
+    say(f"  rel L2 = {err:.2e}")
+    assert err <= 2e-3
