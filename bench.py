@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of the ResidualKV hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over the workload's synthetic
+cache: encode every (layer, sequence, KV head) -- reference store,
+distance/top-k selection, residual quantisation -- then decode attention for
+one query token per sequence in every layer, straight from the compressed
+cache.  Inputs are generated on the GPU before timing and stay resident in
+HBM.  Prints one JSON line.
+
+Besides the step time it measures, with HIP events on the stream the kernels
+run on:
+  * rkv_select_refs (reference store + distance/top-k) and rkv_quantize on
+    the whole workload;
+  * decode attention of one layer (batch of sequences), the Infinity Cache
+    flushed between repetitions;
+and reports each against its roofline (HBM 8 TB/s, dense bf16 MFMA
+2.5 PFLOP/s).  The CPU oracle is timed on a bounded sample of the same
+workload as a reference point (not a target).
+"""
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "encoded KV tokens/s + decode-attn HBM GB/s (% peak) at 32K ctx"
+
+
+def _record_bytes(cfg, bits):
+    d = cfg.head_dim
+    return 2 * d * bits // 8 + 2 * (d // cfg.group) * 2 + 2 * cfg.k
+
+
+def algorithmic(cfg, bits, n_refs, T_positions_count_le):
+    """Algorithmic work of the workload (per whole-workload launch)."""
+    import numpy as np
+    d = cfg.head_dim
+    elt = 2 if cfg.dtype == "bf16" else 4
+    ih = cfg.n_inst * cfg.n_kv_heads
+    N = cfg.seq_len
+    rec = _record_bytes(cfg, bits)
+    # causal candidate pairs per (instance, head): sum_i |C_i|
+    pairs = int(T_positions_count_le.sum())
+    out = {
+        "head_tokens": ih * N,
+        "candidate_pairs": ih * pairs,
+        # distance contraction: 2*d flops per (token, candidate) pair
+        "select_flops": 2.0 * d * ih * pairs,
+        # quantiser: read K and V rows and the token's reference slots,
+        # write K/V codes and scales (the reference gathers stay on chip)
+        "quantize_bytes": ih * N * (2 * d * elt + 2 * cfg.k + rec - 2 * cfg.k),
+        # whole encode: read K, V; write the records and the reference store
+        "encode_bytes": ih * N * (2 * d * elt + rec) + ih * n_refs * 2 * d * elt,
+    }
+    # decode of one layer: the records of the non-reference positions, each
+    # reference row once, q in and out
+    per_seq_head = (N - n_refs) * rec + n_refs * 2 * d * elt
+    out["decode_layer_bytes"] = (cfg.batch * cfg.n_kv_heads * per_seq_head +
+                                 cfg.batch * cfg.n_q_heads * d * (elt + 4))
+    return out
+
+
+def cpu_info():
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"model": model or platform.processor(), "cpu_count": os.cpu_count(),
+            "affinity": aff}
+
+
+def cpu_baseline(cfg, bits, K_head, V_head, seconds):
+    """Time the oracle's encode on rows sampled uniformly over one (layer,
+    sequence, KV head) of the workload until about `seconds` of CPU work."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(0)
+    N = cfg.seq_len
+    done, t_used, batch = 0, 0.0, 64
+    while t_used < seconds:
+        rows = np.sort(rng.integers(0, N, batch))
+        t0 = time.perf_counter()
+        oracle.encode(K_head, V_head, cfg.stride_base, cfg.double_after, cfg.k, bits,
+                      cfg.group, rows=rows)
+        t_used += time.perf_counter() - t0
+        done += batch
+        batch = min(batch * 2, 4096)
+    return {"value": done / t_used, "unit": "head-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"oracle encode of {done} token rows drawn uniformly over one "
+                       f"(layer, sequence, KV head) of {cfg.name} (N={N}), "
+                       f"{t_used:.1f} s on one host core; NumPy fp64/fp32, single-threaded"),
+            "host": cpu_info()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama3_8b_32k")
+    ap.add_argument("--bits", type=int, default=None)
+    ap.add_argument("--kernel-reps", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="also run a plain copy of this many MiB (counter calibration)")
+    a = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each (instance, KV head) is independent; see DESIGN.md for how it would "
+              "shard). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import long_context_attention_rkv_amd as rkv
+    from synth import gen_head_kv, gen_queries, get_config
+
+    if not os.path.exists(rkv.library_path()):
+        from long_context_attention_rkv_amd.build import build
+        build()
+
+    cfg = get_config(a.workload)
+    bits = a.bits if a.bits is not None else cfg.bits[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    n_inst, H, N, D = cfg.n_inst, cfg.n_kv_heads, cfg.seq_len, cfg.head_dim
+
+    t_gen = time.time()
+    K = torch.empty(n_inst, H, N, D, dtype=dt, device=dev)
+    V = torch.empty_like(K)
+    for i in range(n_inst):
+        layer, seq = divmod(i, cfg.batch)
+        for h in range(H):
+            k, v = gen_head_kv(cfg, layer, seq, h, device=dev)
+            K[i, h].copy_(k)
+            V[i, h].copy_(v)
+            del k, v
+    q = torch.stack([gen_queries(cfg, *divmod(i, cfg.batch), device=dev)
+                     for i in range(n_inst)]).contiguous()
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+    print(f"# generated {n_inst}x{H}x{N}x{D} {cfg.dtype} K/V in {t_gen:.1f}s",
+          file=sys.stderr, flush=True)
+
+    cache = rkv.Cache(n_inst, H, N, cfg.dtype, cfg.stride_base, cfg.k, bits, cfg.group,
+                      double_after=cfg.double_after, device=dev)
+    n_refs = cache.n_refs
+    ws_enc = torch.empty(max(1, rkv.rkv_encode_workspace(cache)), dtype=torch.uint8,
+                         device=dev)
+    scale = 1.0 / math.sqrt(D)
+    ns_all = max(1, min((N + 31) // 32, 4096 // max(1, n_inst * H)))
+    ws_dec = torch.empty(rkv.rkv_decode_workspace(cache, cfg.n_q_heads, ns_all),
+                         dtype=torch.uint8, device=dev)
+    out = torch.empty(n_inst, cfg.n_q_heads, D, dtype=torch.float32, device=dev)
+
+    def step():
+        rkv.rkv_encode(K, V, cache, ws=ws_enc)
+        if cfg.decode:
+            rkv.rkv_decode_attn(q, cfg.n_q_heads, cache, scale, out=out, n_split=ns_all,
+                                ws=ws_dec)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    t_steps = time.perf_counter() - t0
+    ms_per_step = t_steps / a.steps * 1e3
+    print(f"# step {ms_per_step:.3f} ms", file=sys.stderr, flush=True)
+
+    # ---- per-kernel timing with HIP events on the launch stream
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def timed(fn, reps, flush_between=False):
+        ts = []
+        for _ in range(reps):
+            if flush_between:
+                flush.fill_(1)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts)), float(np.mean(ts))
+
+    sel_med, sel_mean = timed(lambda: rkv.rkv_select_refs(K, V, cache, ws=ws_enc), a.kernel_reps)
+    qz_med, qz_mean = timed(lambda: rkv.rkv_quantize(K, V, cache), a.kernel_reps)
+
+    T = np.array([rkv.rkv_ref_position(s, cfg.stride_base, cfg.double_after)
+                  for s in range(n_refs)], dtype=np.int64)
+    count_le = np.searchsorted(T, np.arange(N), side="right")
+    alg = algorithmic(cfg, bits, n_refs, count_le)
+
+    dec = None
+    if cfg.decode:
+        layer0 = cache.slice(0, cfg.batch)
+        q0 = q[: cfg.batch].contiguous()
+        ns_layer = max(1, min((N + 31) // 32, 2048 // (cfg.batch * H)))
+        ws_l = torch.empty(rkv.rkv_decode_workspace(layer0, cfg.n_q_heads, ns_layer),
+                           dtype=torch.uint8, device=dev)
+        out_l = torch.empty(cfg.batch, cfg.n_q_heads, D, dtype=torch.float32, device=dev)
+        dmed, dmean = timed(lambda: rkv.rkv_decode_attn(q0, cfg.n_q_heads, layer0, scale,
+                                                        out=out_l, n_split=ns_layer,
+                                                        ws=ws_l),
+                            max(a.kernel_reps, 10), flush_between=True)
+        gbps = alg["decode_layer_bytes"] / dmean / 1e9
+        dec = {"us_per_layer": dmean * 1e6, "GBps": gbps, "frac_peak": gbps / HBM_PEAK_GBPS,
+               "bytes_per_layer": alg["decode_layer_bytes"], "n_split": ns_layer,
+               "note": "QK table + split-K decode + combine of one layer's batch; "
+                       "Infinity Cache flushed between repetitions"}
+
+    qz_gbps = alg["quantize_bytes"] / qz_mean / 1e9
+    sel_tflops = alg["select_flops"] / sel_mean / 1e12
+    kernels = {
+        "rkv_quantize": {"ms": qz_mean * 1e3, "GBps": qz_gbps, "frac_hbm": qz_gbps / HBM_PEAK_GBPS,
+                         "bytes": alg["quantize_bytes"]},
+        "rkv_select_refs": {"ms": sel_mean * 1e3, "TFLOPs": sel_tflops,
+                            "frac_mfma_bf16": sel_tflops / BF16_MFMA_PEAK_TFLOPS,
+                            "flops": alg["select_flops"],
+                            "note": "reference store + distance/top-k (two MFMA passes "
+                                    "over the causal candidates; flops counted once)"},
+    }
+    # dominant kernel of the step by time
+    if qz_mean >= sel_mean:
+        roof = {"bound": "hbm", "kernel": "k_quantize", "achieved": qz_gbps,
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": qz_gbps / HBM_PEAK_GBPS,
+                "traffic": None}
+    else:
+        roof = {"bound": "mfma", "kernel": "rkv_select_refs", "achieved": sel_tflops,
+                "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": sel_tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": None}
+
+    if a.copy_calib:
+        src = torch.empty(a.copy_calib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(3)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    head_tokens = alg["head_tokens"]
+    value = head_tokens / (ms_per_step * 1e-3)
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "head-tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic: seeded prototype-mixture K/V generated on the GPU (no model weights)",
+        "config": {
+            "workload": cfg.name, "layers": cfg.n_layers, "batch": cfg.batch,
+            "kv_heads": H, "q_heads": cfg.n_q_heads, "seq_len": N, "head_dim": D,
+            "stride": cfg.stride_base, "double_after": cfg.double_after, "k": cfg.k,
+            "bits": bits, "group": cfg.group, "n_refs": n_refs,
+            "global_batch": cfg.batch, "parallelism": "single GPU",
+            "step": "encode all layers x sequences x KV heads + decode one token per "
+                    "sequence in every layer",
+            "head_token": "one (sequence, layer, KV head, position) K+V pair",
+        },
+        "positions_per_s": value / (cfg.n_layers * H),
+        "decode_attn": dec,
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if not a.no_cpu:
+        h0 = (K[0, 0].float().cpu().numpy(), V[0, 0].float().cpu().numpy())
+        rec["cpu_baseline"] = cpu_baseline(cfg, bits, h0[0], h0[1], a.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

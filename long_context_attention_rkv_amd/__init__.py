@@ -103,6 +103,26 @@ class Cache:
     def n_refs(self) -> int:
         return int(self.c.n_refs)
 
+    def slice(self, i0: int, n: int) -> "Cache":
+        """A view of instances [i0, i0+n): same shape, buffer pointers offset."""
+        c = self.c
+        if not (0 <= i0 and n >= 1 and i0 + n <= c.n_inst):
+            raise ValueError("instance range out of bounds")
+        v = Cache.__new__(Cache)
+        v.dtype, v.torch_dtype = self.dtype, self.torch_dtype
+        s = L.RkvCache()
+        C.pointer(s)[0] = c
+        s.n_inst = n
+        v.c = s
+        v.sizes = {k: sz // c.n_inst * n for k, sz in self.sizes.items()}
+        v.buffers = {}
+        for name in self.BUFFERS:
+            per = self.sizes[name] // c.n_inst
+            full = self.buffers[name]
+            v.buffers[name] = full[i0 * per:(i0 + n) * per] if per else full[:1]
+            setattr(s, name, v.buffers[name].data_ptr() if per else None)
+        return v
+
     def nbytes(self) -> int:
         return sum(self.sizes.values())
 
