@@ -171,7 +171,7 @@ def main():
     ws_enc = torch.empty(max(1, rkv.rkv_encode_workspace(cache)), dtype=torch.uint8,
                          device=dev)
     scale = 1.0 / math.sqrt(D)
-    ns_all = max(1, min((N + 31) // 32, 4096 // max(1, n_inst * H)))
+    ns_all = max(1, min((N + 31) // 32, 512 // max(1, n_inst * H)))
     ws_dec = torch.empty(rkv.rkv_decode_workspace(cache, cfg.n_q_heads, ns_all),
                          dtype=torch.uint8, device=dev)
     out = torch.empty(n_inst, cfg.n_q_heads, D, dtype=torch.float32, device=dev)
@@ -223,7 +223,7 @@ def main():
     if cfg.decode:
         layer0 = cache.slice(0, cfg.batch)
         q0 = q[: cfg.batch].contiguous()
-        ns_layer = max(1, min((N + 31) // 32, 2048 // (cfg.batch * H)))
+        ns_layer = max(1, min((N + 31) // 32, 512 // (cfg.batch * H)))
         ws_l = torch.empty(rkv.rkv_decode_workspace(layer0, cfg.n_q_heads, ns_layer),
                            dtype=torch.uint8, device=dev)
         out_l = torch.empty(cfg.batch, cfg.n_q_heads, D, dtype=torch.float32, device=dev)

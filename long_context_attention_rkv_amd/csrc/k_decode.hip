@@ -15,77 +15,51 @@
 // (a reference position i contributes QK[slot(i)] and W[slot(i)] += p_i).
 //
 // Kernels:
-//   k_qk_table  QK[inst][hq][slot] in fp32.
-//   k_decode    one wave per (instance, KV head, split of the sequence):
-//               streams the codes of its positions; q.codes and P.codes on
-//               16x16x32 f16 MFMAs (codes are exact small integers in f16),
-//               scales applied in fp32, online softmax per query head,
-//               W accumulated in LDS.  Writes (m, l, O, W) per query head.
-//   k_combine   merges the splits and adds W . Vref.
+//   k_qk_table QK for every reference and query head.
+//   k_decode   one block of 4 waves per (instance, KV head, split of the
+//              sequence), which it walks in chunks of 1024 positions.
+//              Phase A: the waves stream the K codes of 32-token tiles,
+//              q.codes on 16x16x32 f16 MFMAs (codes are exact small
+//              integers in f16), scales in fp32, the reference term from the
+//              QK table in LDS; every logit goes to LDS.  The block takes the
+//              chunk maximum per query head (rescaling what it holds only if
+//              the maximum grew).  Phase B: the waves stream the V codes,
+//              p = exp(logit - max) <= 1, P.codes on the MFMA, and W in LDS
+//              as unsigned 64-bit fixed point (units of 2^-32: integer LDS
+//              atomics are far faster than float ones here).  The block
+//              writes (m, l, O, W) per query head.
+//   k_combine  one block per (instance, KV head): merges the splits, adds
+//              W . Vref (each Vref row read once for all query heads) and
+//              normalises.
 #include <float.h>
 
 #include "rkv_common.h"
 
 namespace rkv {
 
-// ------------------------------------------------------------------ QK table
-template <typename T>
-__global__ __launch_bounds__(256) void k_qk_table(const T* __restrict__ q,
-                                                  const T* __restrict__ ref_kv,
-                                                  float* __restrict__ qk, int G, int H,
-                                                  int64_t n_refs) {
-  __shared__ float qs[16][128];
-  const int kvh = blockIdx.x;
-  const int64_t inst = blockIdx.y;
-  const int hq0 = kvh * G;
-  const int Hq = H * G;
-  for (int e = threadIdx.x; e < G * 128; e += 256)
-    qs[e / 128][e % 128] = (float)q[(inst * Hq + hq0) * 128 + e];
-  __syncthreads();
-  const T* kref = ref_kv + ((inst * H + kvh) * 2 + 0) * n_refs * 128;
-  for (int64_t j = threadIdx.x; j < n_refs; j += 256) {
-    float acc[16];
-#pragma unroll
-    for (int h = 0; h < 16; ++h) acc[h] = 0.f;
-    for (int t = 0; t < 128; t += 8) {
-      float x[8];
-      load8(kref + j * 128 + t, x);
-#pragma unroll
-      for (int h = 0; h < 16; ++h) {
-        if (h < G) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h] = __builtin_fmaf(qs[h][t + e], x[e], acc[h]);
-        }
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < 16; ++h)
-      if (h < G) qk[(inst * Hq + hq0 + h) * n_refs + j] = acc[h];
-  }
-}
-
-// ------------------------------------------------------------------ codes
-// Decode 8 codes of one lane into an f16x8 MFMA operand.  The element order
-// is a fixed permutation of the 8 code positions (perm_of<BITS>); the other
-// operand is built in the same order.
+// Element order of the f16x8 operand decoded from 8 codes (see decode_codes).
 template <int BITS>
-__device__ inline int perm_of(int e) {
-  if constexpr (BITS == 8) {
-    constexpr int p[8] = {0, 2, 1, 3, 4, 6, 5, 7};
-    return p[e];
-  } else {
-    constexpr int p[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-    return p[e];
-  }
+__host__ __device__ constexpr int perm_of(int e) {
+  return BITS == 8 ? ((e & 4) | ((e & 1) << 1) | ((e >> 1) & 1))   // 0 2 1 3 4 6 5 7
+                   : (((e & 1) << 2) | (e >> 1));                  // 0 4 1 5 2 6 3 7
+}
+template <int BITS>
+__host__ __device__ constexpr int invperm_of(int o) {
+  return BITS == 8 ? perm_of<8>(o)                                   // an involution
+                   : (((o & 3) << 1) | (o >> 2));                    // 0 2 4 6 1 3 5 7
 }
 
 __device__ inline f16x2 as_h2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
+__device__ inline uint32_t h2_bits(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
+// 8 two's-complement codes (BITS each) -> f16x8 exact integers, in
+// perm_of<BITS> order.  Offset-binary plus the f16 exponent of 1024 puts each
+// code in a mantissa; one packed subtract removes the offset.
 template <int BITS>
 __device__ inline f16x8 decode_codes(uint32_t w0, uint32_t w1) {
   f16x2 p[4];
   if constexpr (BITS == 4) {
-    const uint32_t t = w0 ^ 0x88888888u;  // two's complement -> offset binary
+    const uint32_t t = w0 ^ 0x88888888u;
     const f16x2 off = {(_Float16)-1032.f, (_Float16)-1032.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) p[j] = as_h2(((t >> (4 * j)) & 0x000F000Fu) | 0x64006400u) + off;
@@ -112,22 +86,6 @@ __device__ inline f16x8 decode_codes(uint32_t w0, uint32_t w1) {
   return r;
 }
 
-// Load the BITS bytes of 8 consecutive codes starting at byte p.
-template <int BITS>
-__device__ inline void load_code_words(const uint8_t* p, uint32_t& w0, uint32_t& w1) {
-  if constexpr (BITS == 4) {
-    w0 = *reinterpret_cast<const uint32_t*>(p);
-    w1 = 0;
-  } else if constexpr (BITS == 8) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    w0 = v.x;
-    w1 = v.y;
-  } else {
-    w0 = *reinterpret_cast<const uint16_t*>(p);
-    w1 = 0;
-  }
-}
-
 __device__ inline float quad_max(float v) {
 #pragma unroll
   for (int off = 8; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -139,29 +97,113 @@ __device__ inline float quad_sum(float v) {
   return v;
 }
 
+template <int NW>
+__device__ inline void load_words(const void* p, uint32_t (&w)[NW]) {
+  if constexpr (NW == 1) {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (NW == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int c = 0; c < NW / 4; ++c) {
+      const uint4 v = reinterpret_cast<const uint4*>(p)[c];
+      w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
+    }
+  }
+}
+
+// Unsigned fixed point with 32 fractional bits, for 0 <= x < 2^31.
+__device__ inline unsigned long long to_fixed32(float x) {
+  const float y = x * 4294967296.0f;           // exact scaling
+  const float hi = floorf(y * 0x1p-32f);
+  const uint32_t h = (uint32_t)hi;
+  const uint32_t l = (uint32_t)(y - hi * 4294967296.0f);
+  return ((unsigned long long)h << 32) | l;
+}
+__device__ inline float from_fixed32(unsigned long long v) {
+  return (float)((double)v * 0x1p-32);
+}
+
 constexpr int kDecTile = 32;
+constexpr float kLazyRescale = 8.0f;
 
 // Partial record per (instance, query head, split): m, l, 2 pad, O[128], W[nrp].
 __host__ __device__ inline int64_t part_rec_floats(int64_t n_refs) {
   return 132 + ((n_refs + 3) / 4) * 4;
 }
 
-template <typename T, int BITS, int NG>
-__global__ __launch_bounds__(64) void k_decode(
-    const T* __restrict__ q, const uint16_t* __restrict__ idx, const uint8_t* __restrict__ codes_k,
-    const uint8_t* __restrict__ codes_v, const uint16_t* __restrict__ scales,
-    const float* __restrict__ qk, float* __restrict__ part, float alpha, int64_t N,
-    int64_t n_refs, Sched sc, int k, int G, int H, int n_split) {
+// ------------------------------------------------------------------ QK table
+// QK[inst][hq][slot] = q_hq . Kref_slot in fp32; one thread per reference,
+// whole row loaded before the dot products.  Rows of the table are padded to
+// a multiple of 4 (nrp) with zeros.
+template <typename T>
+__global__ __launch_bounds__(256) void k_qk_table(const T* __restrict__ q,
+                                                  const T* __restrict__ ref_kv,
+                                                  float* __restrict__ qk, int G, int H,
+                                                  int64_t n_refs) {
+  __shared__ float qs[16 * 128];
+  const int kvh = blockIdx.y;
+  const int64_t inst = blockIdx.z;
+  const int Hq = H * G;
+  const int64_t nrp = ((n_refs + 3) / 4) * 4;
+  const T* qh = q + (inst * Hq + kvh * G) * 128;
+  for (int e = threadIdx.x; e < G * 128; e += 256) qs[e] = (float)qh[e];
+  __syncthreads();
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= nrp) return;
+  float* out = qk + (inst * Hq + kvh * G) * nrp + j;
+  if (j >= n_refs) {
+    for (int h = 0; h < G; ++h) out[h * nrp] = 0.f;
+    return;
+  }
+  const T* row = ref_kv + ((inst * H + kvh) * 2 + 0) * n_refs * 128 + j * 128;
+  float x[128];
+#pragma unroll
+  for (int t = 0; t < 128; t += 8) {
+    float v[8];
+    load8(row + t, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[t + e] = v[e];
+  }
+  for (int h = 0; h < G; ++h) {
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < 128; ++t) acc = __builtin_fmaf(qs[h * 128 + t], x[t], acc);
+    out[h * nrp] = acc;
+  }
+}
+
+constexpr int kChunkTiles = 32;   // tiles (x32 tokens) per softmax chunk of a block
+
+template <typename T, int BITS, int NG, int KM>
+__global__ __launch_bounds__(256, 2) void k_decode(
+    const T* __restrict__ q, const T* __restrict__ ref_kv, const uint16_t* __restrict__ idx,
+    const uint8_t* __restrict__ codes_k, const uint8_t* __restrict__ codes_v,
+    const uint16_t* __restrict__ scales, const float* __restrict__ qk, float* __restrict__ part,
+    float alpha, int64_t N, int64_t n_refs, Sched sc, int k, int G, int H, int n_split) {
   constexpr int HPL = 4 / NG;  // query heads per lane in the score layout
-  constexpr int GS = 128 / NG;  // group size
+  constexpr int GS = 128 / NG;  // dims per scale group
+  constexpr int CT = kChunkTiles * kDecTile;  // tokens per chunk
   extern __shared__ float lds[];
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
-  float* qk_s = lds;                 // [G][nrp]
-  float* w_s = lds + G * nrp;        // [G][nrp]
-  float* pst = w_s + G * nrp;        // [16][kDecTile]
-  float* sst = pst + 16 * kDecTile;  // [NG][kDecTile]
+  // Per-head LDS rows are nrp + 8 floats apart: the G heads of one token touch
+  // the same slot, and this puts their words in different banks.
+  const int64_t ls = nrp + 8;
+  float* qk_s = lds;                                              // [G][ls]
+  unsigned long long* w_s =
+      reinterpret_cast<unsigned long long*>(qk_s + G * ls);       // [G][ls] fixed point
+  float* lg_s = reinterpret_cast<float*>(w_s + G * ls);           // [G][CT] logits of a chunk
+  float* o_s = lg_s + G * CT;                                     // [G][128]
+  float* m_s = o_s + G * 128;                                     // [16] block max per head
+  float* wm_s = m_s + 16;                                         // [4][16] wave maxima
+  float* sc_s = wm_s + 64;                                        // [16] rescale factors
+  _Float16* pst_all = reinterpret_cast<_Float16*>(sc_s + 16);     // [4][16][32]
+  _Float16* sst_all = pst_all + 4 * 16 * kDecTile;                // [4][NG][32]
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
   const int n = lane & 15;
   const int quad = lane >> 4;
   const int split = blockIdx.x;
@@ -173,58 +215,98 @@ __global__ __launch_bounds__(64) void k_decode(
   const int64_t tps = (tiles + n_split - 1) / n_split;
   const int64_t t0 = split * tps;
   const int64_t t1 = (t0 + tps < tiles) ? t0 + tps : tiles;
+  const T* qh = q + (inst * Hq + kvh * G) * 128;
 
-  // ---- stage the QK table, clear W and the P staging
-  const float* qk_g = qk + (inst * Hq + kvh * G) * n_refs;
-  for (int64_t e = lane; e < (int64_t)G * nrp; e += 64) {
-    const int64_t h = e / nrp, j = e - h * nrp;
-    qk_s[e] = j < n_refs ? qk_g[h * n_refs + j] : 0.f;
-    w_s[e] = 0.f;
+  // ---- prologue: QK table into LDS, clears
+  {
+    const float4* src = reinterpret_cast<const float4*>(qk + (inst * Hq + kvh * G) * nrp);
+    for (int64_t e = tid; e < G * nrp / 4; e += 256) {
+      const int64_t h = e / (nrp / 4), c = e - h * (nrp / 4);
+      *reinterpret_cast<float4*>(qk_s + h * ls + 4 * c) = src[e];
+    }
+    for (int64_t e = tid; e < G * ls; e += 256) w_s[e] = 0ull;
+    for (int e = tid; e < G * 128; e += 256) o_s[e] = 0.f;
+    for (int e = tid; e < 4 * 16 * kDecTile; e += 256) pst_all[e] = (_Float16)0.f;
+    if (tid < 16) m_s[tid] = -INFINITY;
   }
-  for (int e = lane; e < 16 * kDecTile; e += 64) pst[e] = 0.f;
 
-  // ---- A operand of the score MFMA: rows (h, g), dims of step s in lane order
+  // ---- A operand of the score MFMA: rows (h, g); lane quad covers dims
+  //      32*quad .. +31, step s dims 32*quad + 8*s + perm(e).
   f16x8 aq[4];
   {
-    const int m = n;  // row
-    const int h = m / NG, g = m % NG;
+    const int h = n / NG, g = n % NG;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int dim = 32 * s + 8 * quad + perm_of<BITS>(e);
+        const int dim = 32 * quad + 8 * s + perm_of<BITS>(e);
         float v = 0.f;
-        if (h < G && dim / GS == g) v = (float)q[(inst * Hq + kvh * G + h) * 128 + dim];
+        if (h < G && dim / GS == g) v = (float)qh[h * 128 + dim];
         aq[s][e] = (_Float16)v;
       }
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
+  __syncthreads();
 
-  float m_mine[HPL], l_mine[HPL];
+  _Float16* pst = pst_all + w * 16 * kDecTile;
+  _Float16* sst = sst_all + w * NG * kDecTile;
+  const uint8_t* ck = codes_k + ih * N * (16 * BITS) + n * (16 * BITS) + quad * (4 * BITS);
+  const uint16_t* sc16 = scales + ih * N * 2 * NG + n * 2 * NG;
+  const uint16_t* ix = idx + ih * N * k;
+  const uint8_t* cv = codes_v + ih * tiles * 128 * (4 * BITS) + n * (4 * BITS) + quad * BITS;
+  const int h0 = quad * HPL;
+
+  float l_mine[HPL];
 #pragma unroll
-  for (int hh = 0; hh < HPL; ++hh) {
-    m_mine[hh] = -INFINITY;
-    l_mine[hh] = 0.f;
-  }
+  for (int hh = 0; hh < HPL; ++hh) l_mine[hh] = 0.f;
   f32x4 o[8];
 #pragma unroll
   for (int b = 0; b < 8; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint8_t* ck = codes_k + ih * N * (16 * BITS);
-  const uint16_t* sc16 = scales + ih * N * 2 * NG;
-  const uint16_t* ix = idx + ih * N * k;
-  const uint8_t* cv = codes_v + ih * tiles * 128 * (4 * BITS);
-  const int h0 = quad * HPL;
+  auto load_slots_of = [&](int64_t tok, uint32_t (&iw)[KM / 2]) {
+    if (k == KM) {
+      load_words<KM / 2>(ix + tok * KM, iw);
+    } else {
+#pragma unroll
+      for (int j = 0; j < KM / 2; ++j) {
+        const uint32_t lo = 2 * j < k ? ix[tok * k + 2 * j] : 0;
+        const uint32_t hi = 2 * j + 1 < k ? ix[tok * k + 2 * j + 1] : 0;
+        iw[j] = lo | (hi << 16);
+      }
+    }
+  };
 
-  for (int64_t t = t0; t < t1; ++t) {
+  struct ARegs {
+    uint32_t kw[2][BITS];     // K codes, dims 32*quad .. +31 of tokens 16b+n
+    uint32_t sw[2][NG];       // K then V scales of those tokens
+    uint32_t iw[2][KM / 2];   // their reference slots
+  };
+  struct BRegs {
+    uint32_t vw[8][BITS == 8 ? 2 : 1];  // V codes: dim 16*blk+n, tokens 8*quad .. +7
+    uint32_t sw[2][NG];
+    uint32_t iw[2][KM / 2];
+  };
+  auto loadA = [&](int64_t t, ARegs& r) {
     const int64_t tb = t * kDecTile;
-    float logit[2][HPL];
-    int64_t slot_b[2];
-    int keff_b[2];
-    float sv_b[2][NG];
-    // ---------------- scores of the two 16-token blocks
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t tok = tb + 16 * b + n;
+      if (tok < N) {
+        load_words<BITS>(ck + (tb + 16 * b) * (16 * BITS), r.kw[b]);
+        load_words<NG>(sc16 + (tb + 16 * b) * 2 * NG, r.sw[b]);
+        load_slots_of(tok, r.iw[b]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < BITS; ++j) r.kw[b][j] = 0;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) r.sw[b][j] = 0;
+#pragma unroll
+        for (int j = 0; j < KM / 2; ++j) r.iw[b][j] = 0;
+      }
+    }
+  };
+  auto computeA = [&](int64_t t, int64_t c0, const ARegs& r, float (&wmax)[HPL]) {
+    const int64_t tb = t * kDecTile;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int64_t tok = tb + 16 * b + n;
@@ -232,211 +314,395 @@ __global__ __launch_bounds__(64) void k_decode(
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        uint32_t w0 = 0, w1 = 0;
-        if (valid) load_code_words<BITS>(ck + tok * (16 * BITS) + (4 * s + quad) * BITS, w0, w1);
+        uint32_t w0, w1;
+        if constexpr (BITS == 4) {
+          w0 = r.kw[b][s]; w1 = 0;
+        } else if constexpr (BITS == 8) {
+          w0 = r.kw[b][2 * s]; w1 = r.kw[b][2 * s + 1];
+        } else {
+          w0 = (r.kw[b][s >> 1] >> (16 * (s & 1))) & 0xFFFFu; w1 = 0;
+        }
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], decode_codes<BITS>(w0, w1), acc, 0, 0, 0);
       }
-      float sk[NG];
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        sk[g] = valid ? half_bits_to_f32(sc16[(tok * 2 + 0) * NG + g]) : 0.f;
-        sv_b[b][g] = valid ? half_bits_to_f32(sc16[(tok * 2 + 1) * NG + g]) : 0.f;
-      }
-      const int64_t slot = valid ? sched_slot(tok, sc) : -1;
-      const int keff = valid ? (int)min((int64_t)k, sched_count_le(tok, sc)) : 0;
-      slot_b[b] = slot;
-      keff_b[b] = keff;
-      const uint16_t* irow = ix + (valid ? tok : 0) * k;
-#pragma unroll
-      for (int hh = 0; hh < HPL; ++hh) {
-        const int h = h0 + hh;
-        float lg = -INFINITY;
-        if (valid && h < G) {
-          const float* qrow = qk_s + h * nrp;
-          float sc_ = 0.f;
-          if (slot >= 0) {
-            sc_ = qrow[slot];
-          } else {
-            float rs = 0.f;
-            for (int j = 0; j < keff; ++j) rs += qrow[irow[j]];
-            float res = 0.f;
-#pragma unroll
-            for (int g = 0; g < NG; ++g) res = __builtin_fmaf(sk[g], acc[hh * NG + g], res);
-            sc_ = res + rs / (float)keff;
-          }
-          lg = alpha * sc_;
-        }
-        logit[b][hh] = lg;
-      }
-    }
-    // ---------------- online softmax per head (this lane's heads)
-    float scale_mine[HPL];
-    float p[2][HPL];
-#pragma unroll
-    for (int hh = 0; hh < HPL; ++hh) {
-      const float tm = quad_max(fmaxf(logit[0][hh], logit[1][hh]));
-      const float mnew = fmaxf(m_mine[hh], tm);
-      const bool live = mnew > -INFINITY;
-      scale_mine[hh] = live ? __expf(m_mine[hh] - mnew) : 1.f;
-      p[0][hh] = live ? __expf(logit[0][hh] - mnew) : 0.f;
-      p[1][hh] = live ? __expf(logit[1][hh] - mnew) : 0.f;
-      l_mine[hh] = l_mine[hh] * scale_mine[hh] + quad_sum(p[0][hh] + p[1][hh]);
-      m_mine[hh] = mnew;
-    }
-    // rescale O (rows 4*quad + j of the PV layout) and W (this quad's heads)
-    float so[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int src = 16 * min((4 * quad + j) / HPL, 3);
-      so[j] = __shfl(scale_mine[j % HPL], src);
-    }
-    const bool any_rescale = __any(so[0] != 1.f || so[1] != 1.f || so[2] != 1.f || so[3] != 1.f);
-    if (any_rescale) {
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[b][j] *= so[j];
-      }
-#pragma unroll
-      for (int hh = 0; hh < HPL; ++hh) {
-        const int h = h0 + hh;
-        if (h < G && scale_mine[hh] != 1.f) {
-          for (int64_t j = n; j < n_refs; j += 16) w_s[h * nrp + j] *= scale_mine[hh];
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    // ---------------- W accumulation and P staging
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int64_t tok = tb + 16 * b + n;
-      const uint16_t* irow = ix + (tok < N ? tok : 0) * k;
+      const int32_t slot = valid ? sched_slot((int32_t)tok, sc) : -1;
+      const int keff = valid ? min(k, sched_count_le((int32_t)tok, sc)) : 0;
+      const float inv_keff = keff > 0 ? 1.0f / (float)keff : 0.f;
+      const int u = (int)(tok - c0 * kDecTile);
 #pragma unroll
       for (int hh = 0; hh < HPL; ++hh) {
         const int h = h0 + hh;
         if (h < G) {
-          const float pv = p[b][hh];
-          float* wrow = w_s + h * nrp;
-          if (slot_b[b] >= 0) {
-            atomicAdd(wrow + slot_b[b], pv);
-            pst[h * kDecTile + 16 * b + n] = 0.f;
-          } else {
-            if (keff_b[b] > 0) {
-              const float pw = pv / (float)keff_b[b];
-              for (int j = 0; j < keff_b[b]; ++j) atomicAdd(wrow + irow[j], pw);
+          float lg = -INFINITY;
+          if (valid) {
+            const float* qrow = qk_s + h * ls;
+            float sc_;
+            if (slot >= 0) {
+              sc_ = qrow[slot];
+            } else {
+              float rs = 0.f;
+#pragma unroll
+              for (int j = 0; j < KM; ++j)
+                if (j < keff) rs += qrow[(r.iw[b][j >> 1] >> (16 * (j & 1))) & 0xFFFFu];
+              float res = 0.f;
+#pragma unroll
+              for (int g = 0; g < NG; ++g) {
+                const float sk = half_bits_to_f32((uint16_t)(r.sw[b][g >> 1] >> (16 * (g & 1))));
+                res = __builtin_fmaf(sk, acc[hh * NG + g], res);
+              }
+              sc_ = res + rs * inv_keff;
             }
-            pst[h * kDecTile + 16 * b + n] = pv;
+            lg = alpha * sc_;
+          }
+          lg_s[h * CT + u] = lg;
+          wmax[hh] = fmaxf(wmax[hh], lg);
+        }
+      }
+    }
+  };
+  auto loadB = [&](int64_t t, BRegs& r) {
+    const int64_t tb = t * kDecTile;
+    const uint8_t* cvt = cv + t * 128 * (4 * BITS);
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      const uint8_t* pp = cvt + 16 * blk * (4 * BITS);
+      if constexpr (BITS == 8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(pp);
+        r.vw[blk][0] = v.x;
+        r.vw[blk][1] = v.y;
+      } else if constexpr (BITS == 4) {
+        r.vw[blk][0] = *reinterpret_cast<const uint32_t*>(pp);
+      } else {
+        r.vw[blk][0] = *reinterpret_cast<const uint16_t*>(pp);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t tok = tb + 16 * b + n;
+      if (tok < N) {
+        load_slots_of(tok, r.iw[b]);
+        load_words<NG>(sc16 + (tb + 16 * b) * 2 * NG, r.sw[b]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < KM / 2; ++j) r.iw[b][j] = 0;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) r.sw[b][j] = 0;
+      }
+    }
+  };
+  auto computeB = [&](int64_t t, int64_t c0, const BRegs& r, const float (&mh)[HPL]) {
+    const int64_t tb = t * kDecTile;
+    float psum[HPL];
+#pragma unroll
+    for (int hh = 0; hh < HPL; ++hh) psum[hh] = 0.f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t tok = tb + 16 * b + n;
+      const bool valid = tok < N;
+      const int32_t slot = valid ? sched_slot((int32_t)tok, sc) : -1;
+      const int keff = valid ? min(k, sched_count_le((int32_t)tok, sc)) : 0;
+      const int u = 16 * b + n;
+      const int pos = 8 * (u >> 3) + invperm_of<BITS>(u & 7);
+      const int uc = (int)(tok - c0 * kDecTile);
+#pragma unroll
+      for (int hh = 0; hh < HPL; ++hh) {
+        const int h = h0 + hh;
+        if (h < G) {
+          const float lg = lg_s[h * CT + uc];
+          const float pv = (valid && lg > -INFINITY) ? __expf(lg - mh[hh]) : 0.f;
+          psum[hh] += pv;
+          unsigned long long* wrow = w_s + h * ls;
+          if (slot >= 0) {
+            if (pv > 0.f) atomicAdd(wrow + slot, to_fixed32(pv));
+            pst[h * kDecTile + pos] = (_Float16)0.f;
+          } else {
+            if (keff > 0 && pv > 0.f) {
+              const unsigned long long pw = to_fixed32(pv / (float)keff);
+#pragma unroll
+              for (int j = 0; j < KM; ++j)
+                if (j < keff) atomicAdd(wrow + ((r.iw[b][j >> 1] >> (16 * (j & 1))) & 0xFFFFu), pw);
+            }
+            pst[h * kDecTile + pos] = (_Float16)pv;
           }
         }
       }
       if (quad == 0) {
 #pragma unroll
-        for (int g = 0; g < NG; ++g) sst[g * kDecTile + 16 * b + n] = sv_b[b][g];
+        for (int g = 0; g < NG; ++g)
+          sst[g * kDecTile + pos] =
+              __builtin_bit_cast(_Float16, (uint16_t)(r.sw[b][(NG + g) >> 1] >> (16 * ((NG + g) & 1))));
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int hh = 0; hh < HPL; ++hh)
+      if (h0 + hh < G) l_mine[hh] += quad_sum(psum[hh]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): LDS writes landed
     __builtin_amdgcn_wave_barrier();
-    // ---------------- P.V on the MFMA, one A operand per scale group
     f16x8 ap[NG];
+    {
+      const uint4 pr = *reinterpret_cast<const uint4*>(pst + n * kDecTile + 8 * quad);
+      const uint32_t pw4[4] = {pr.x, pr.y, pr.z, pr.w};
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
+      for (int g = 0; g < NG; ++g) {
+        const uint4 sr = *reinterpret_cast<const uint4*>(sst + g * kDecTile + 8 * quad);
+        const uint32_t sw4[4] = {sr.x, sr.y, sr.z, sr.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tk = 8 * quad + perm_of<BITS>(e);
-        ap[g][e] = (_Float16)(pst[n * kDecTile + tk] * sst[g * kDecTile + tk]);
+        for (int j = 0; j < 4; ++j) {
+          const f16x2 prod = as_h2(pw4[j]) * as_h2(sw4[j]);
+          ap[g][2 * j] = prod[0];
+          ap[g][2 * j + 1] = prod[1];
+        }
       }
     }
-    const uint8_t* cvt = cv + t * 128 * (4 * BITS);
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
-      const int dim = 16 * blk + n;
-      uint32_t w0, w1;
-      load_code_words<BITS>(cvt + dim * (4 * BITS) + quad * BITS, w0, w1);
-      o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[(16 * blk) / GS], decode_codes<BITS>(w0, w1),
-                                                   o[blk], 0, 0, 0);
+      const uint32_t w0 = r.vw[blk][0];
+      const uint32_t w1 = BITS == 8 ? r.vw[blk][BITS == 8 ? 1 : 0] : 0;
+      o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[(16 * blk) / GS],
+                                                   decode_codes<BITS>(w0, w1), o[blk], 0, 0, 0);
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
-  }
+  };
 
-  // ---- write the partial record of every query head of this KV head
-  const int64_t rec = part_rec_floats(n_refs);
+  for (int64_t c0 = t0; c0 < t1; c0 += kChunkTiles) {
+    const int64_t c1 = (c0 + kChunkTiles < t1) ? c0 + kChunkTiles : t1;
+    // ================= phase A: logits of the chunk into LDS (next tile prefetched)
+    float wmax[HPL];
 #pragma unroll
-  for (int hh = 0; hh < HPL; ++hh) {
-    const int h = h0 + hh;
-    if (h < G && n == 0) {
-      float* r = part + ((inst * Hq + kvh * G + h) * n_split + split) * rec;
-      r[0] = m_mine[hh];
-      r[1] = l_mine[hh];
-    }
-  }
-#pragma unroll
-  for (int blk = 0; blk < 8; ++blk) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int h = 4 * quad + j;
-      if (h < G) {
-        float* r = part + ((inst * Hq + kvh * G + h) * n_split + split) * rec;
-        r[4 + 16 * blk + n] = o[blk][j];
+    for (int hh = 0; hh < HPL; ++hh) wmax[hh] = -INFINITY;
+    {
+      ARegs cur, nxt;
+      int64_t t = c0 + w;
+      if (t < c1) loadA(t, nxt);
+      while (t < c1) {
+        cur = nxt;
+        if (t + 4 < c1) loadA(t + 4, nxt);
+        computeA(t, c0, cur, wmax);
+        t += 4;
       }
     }
+#pragma unroll
+    for (int hh = 0; hh < HPL; ++hh) {
+      const float m = quad_max(wmax[hh]);
+      if (n == 0 && h0 + hh < G) wm_s[w * 16 + h0 + hh] = m;
+    }
+    __syncthreads();
+    if (tid < 16) {
+      float f = 1.f;
+      if (tid < G) {
+        const float mo = m_s[tid];
+        const float mn = fmaxf(mo, fmaxf(fmaxf(wm_s[tid], wm_s[16 + tid]),
+                                         fmaxf(wm_s[32 + tid], wm_s[48 + tid])));
+        f = (mn > mo) ? (mo > -INFINITY ? __expf(mo - mn) : 0.f) : 1.f;
+        m_s[tid] = mn;
+      }
+      sc_s[tid] = f;
+    }
+    __syncthreads();
+    {
+      // rescale what was accumulated against the old maximum
+      bool any = false;
+      for (int h = 0; h < G; ++h) any |= sc_s[h] != 1.f;
+      if (any) {
+        for (int64_t e = tid; e < (int64_t)G * nrp; e += 256) {
+          const int64_t h = e / nrp, j = e - h * nrp;
+          const float f = sc_s[h];
+          if (f != 1.f) w_s[h * ls + j] = (unsigned long long)((double)w_s[h * ls + j] * (double)f);
+        }
+#pragma unroll
+        for (int hh = 0; hh < HPL; ++hh)
+          if (h0 + hh < G) l_mine[hh] *= sc_s[h0 + hh];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float f = (4 * quad + j < G) ? sc_s[4 * quad + j] : 1.f;
+#pragma unroll
+          for (int b = 0; b < 8; ++b) o[b][j] *= f;
+        }
+      }
+    }
+    __syncthreads();
+    // ================= phase B: p, W, P.V
+    float mh[HPL];
+#pragma unroll
+    for (int hh = 0; hh < HPL; ++hh) mh[hh] = (h0 + hh < G) ? m_s[h0 + hh] : 0.f;
+    {
+      BRegs cur, nxt;
+      int64_t t = c0 + w;
+      if (t < c1) loadB(t, nxt);
+      while (t < c1) {
+        cur = nxt;
+        if (t + 4 < c1) loadB(t + 4, nxt);
+        computeB(t, c0, cur, mh);
+        t += 4;
+      }
+    }
+    __syncthreads();
   }
-  for (int64_t e = lane; e < (int64_t)G * nrp; e += 64) {
+
+  // ---- merge the four waves (same maximum), write the partial records
+  float* lw = wm_s;  // reuse [4][16]
+#pragma unroll
+  for (int hh = 0; hh < HPL; ++hh)
+    if (h0 + hh < G && n == 0) lw[w * 16 + h0 + hh] = l_mine[hh];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = 4 * quad + j;
+    if (h < G) {
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) atomicAdd(&o_s[h * 128 + 16 * blk + n], o[blk][j]);
+    }
+  }
+  __syncthreads();
+  const int64_t rec = part_rec_floats(n_refs);
+  for (int64_t e = tid; e < (int64_t)G * nrp; e += 256) {
     const int64_t h = e / nrp, j = e - h * nrp;
-    float* r = part + ((inst * Hq + kvh * G + h) * n_split + split) * rec;
-    r[132 + j] = w_s[e];
+    part[((inst * Hq + kvh * G + h) * n_split + split) * rec + 132 + j] = from_fixed32(w_s[h * ls + j]);
+  }
+  if (tid < G) {
+    float* r = part + ((inst * Hq + kvh * G + tid) * n_split + split) * rec;
+    r[0] = m_s[tid];
+    r[1] = lw[tid] + lw[16 + tid] + lw[32 + tid] + lw[48 + tid];
+  }
+  for (int e = tid; e < G * 128; e += 256) {
+    const int h = e / 128;
+    part[((inst * Hq + kvh * G + h) * n_split + split) * rec + 4 + (e % 128)] = o_s[e];
   }
 }
 
 // ------------------------------------------------------------------ combine
+// One block per (instance, KV head, 32-dim chunk): merge the splits of its
+// G query heads, then add W . Vref for the chunk's dims.
+constexpr int kCombChunks = 4;
+
 template <typename T>
-__global__ __launch_bounds__(128) void k_combine(const float* __restrict__ part,
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
                                                  const T* __restrict__ ref_kv,
                                                  float* __restrict__ out, int G, int H,
                                                  int64_t n_refs, int n_split) {
-  extern __shared__ float wt[];
-  const int hq = blockIdx.x;
+  extern __shared__ float cs[];
+  const int64_t nrp = ((n_refs + 3) / 4) * 4;
+  float* wt = cs;                   // [G][nrp]
+  float* fs = wt + G * nrp;         // [G][n_split] split factors
+  float* red = fs + G * n_split;    // [8][G][32] partial W.Vref sums
+  float* ls_ = red + 8 * G * 32;    // [G] l
+  const int kvh = blockIdx.x;
   const int64_t inst = blockIdx.y;
+  const int chunk = blockIdx.z;
   const int Hq = H * G;
-  const int kvh = hq / G;
-  const int t = threadIdx.x;
+  const int tid = threadIdx.x;
   const int64_t rec = part_rec_floats(n_refs);
-  const float* base = part + (inst * Hq + hq) * n_split * rec;
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, base[s * rec]);
-  float l = 0.f, o = 0.f;
-  for (int s = 0; s < n_split; ++s) {
-    const float ms = base[s * rec];
-    const float f = ms > -INFINITY ? __expf(ms - M) : 0.f;
-    l += f * base[s * rec + 1];
-    o += f * base[s * rec + 4 + t];
-  }
-  for (int64_t j = t; j < n_refs; j += 128) {
-    float w = 0.f;
+  const float* base = part + (inst * Hq + kvh * G) * n_split * rec;  // head h at + h*n_split*rec
+  if (tid < G) {
+    const float* b = base + tid * n_split * rec;
+    float M = -INFINITY;
+    for (int s = 0; s < n_split; ++s) M = fmaxf(M, b[s * rec]);
+    float l = 0.f;
     for (int s = 0; s < n_split; ++s) {
-      const float ms = base[s * rec];
-      const float f = ms > -INFINITY ? __expf(ms - M) : 0.f;
-      w += f * base[s * rec + 132 + j];
+      const float m = b[s * rec];
+      const float f = m > -INFINITY ? __expf(m - M) : 0.f;
+      fs[tid * n_split + s] = f;
+      l += f * b[s * rec + 1];
     }
-    wt[j] = w;
+    ls_[tid] = l;
   }
   __syncthreads();
-  const T* vref = ref_kv + ((inst * H + kvh) * 2 + 1) * n_refs * 128;
-  for (int64_t j = 0; j < n_refs; ++j) o = __builtin_fmaf(wt[j], (float)vref[j * 128 + t], o);
-  out[(inst * Hq + hq) * 128 + t] = o / l;
+  // merged W, float4 at a time
+  for (int64_t e = tid; e < (int64_t)G * (nrp / 4); e += 256) {
+    const int h = (int)(e / (nrp / 4));
+    const int64_t c = e - (int64_t)h * (nrp / 4);
+    const float* b = base + h * n_split * rec + 132 + 4 * c;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int s = 0;
+    for (; s + 8 <= n_split; s += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(b + (s + u) * rec);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float f = fs[h * n_split + s + u];
+        acc.x += f * v[u].x; acc.y += f * v[u].y; acc.z += f * v[u].z; acc.w += f * v[u].w;
+      }
+    }
+    for (; s < n_split; ++s) {
+      const float f = fs[h * n_split + s];
+      const float4 v = *reinterpret_cast<const float4*>(b + s * rec);
+      acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
+    }
+    *reinterpret_cast<float4*>(wt + h * nrp + 4 * c) = acc;
+  }
+  __syncthreads();
+  // W . Vref on dims chunk*32 + t: thread (t, g) sums references j = g mod 8
+  const int t = tid & 31;
+  const int g = tid >> 5;
+  const int dim = chunk * 32 + t;
+  const T* vref = ref_kv + ((inst * H + kvh) * 2 + 1) * n_refs * 128 + dim;
+  float a[16];
+#pragma unroll
+  for (int h = 0; h < 16; ++h) a[h] = 0.f;
+  int64_t j = g;
+  for (; j + 8 * 7 < n_refs; j += 8 * 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (float)vref[(j + 8 * u) * 128];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+#pragma unroll
+      for (int h = 0; h < 16; ++h)
+        if (h < G) a[h] = __builtin_fmaf(wt[h * nrp + j + 8 * u], v[u], a[h]);
+    }
+  }
+  for (; j < n_refs; j += 8) {
+    const float v = (float)vref[j * 128];
+#pragma unroll
+    for (int h = 0; h < 16; ++h)
+      if (h < G) a[h] = __builtin_fmaf(wt[h * nrp + j], v, a[h]);
+  }
+#pragma unroll
+  for (int h = 0; h < 16; ++h)
+    if (h < G) red[(g * G + h) * 32 + t] = a[h];
+  __syncthreads();
+  for (int e = tid; e < G * 32; e += 256) {
+    const int h = e / 32, tt = e % 32;
+    float s = 0.f;
+    for (int x = 0; x < 8; ++x) s += red[(x * G + h) * 32 + tt];
+    const float* b = base + h * n_split * rec + 4 + chunk * 32 + tt;
+    float o = 0.f;
+    for (int x = 0; x < n_split; ++x) o += fs[h * n_split + x] * b[x * rec];
+    out[(inst * Hq + kvh * G + h) * 128 + chunk * 32 + tt] = (o + s) / ls_[h];
+  }
 }
 
 // ------------------------------------------------------------------ launchers
-size_t decode_ws_bytes(int64_t n_inst, int H, int n_q_heads, int n_split, int64_t n_refs) {
-  const size_t qkb = (size_t)n_inst * n_q_heads * n_refs * 4;
-  const size_t qka = (qkb + 255) / 256 * 256;
-  const size_t pb = (size_t)n_inst * n_q_heads * n_split * part_rec_floats(n_refs) * 4;
-  (void)H;
-  return qka + pb;
+static size_t qk_bytes(int64_t n_inst, int n_q_heads, int64_t n_refs) {
+  const size_t b = (size_t)n_inst * n_q_heads * (((n_refs + 3) / 4) * 4) * 4;
+  return (b + 255) / 256 * 256;
 }
 
-template <typename T, int BITS, int NG>
+size_t decode_ws_bytes(int64_t n_inst, int H, int n_q_heads, int n_split, int64_t n_refs) {
+  (void)H;
+  return qk_bytes(n_inst, n_q_heads, n_refs) +
+         (size_t)n_inst * n_q_heads * n_split * part_rec_floats(n_refs) * 4;
+}
+
+size_t decode_lds_bytes(int G, int NG, int64_t n_refs) {
+  const int64_t nrp = ((n_refs + 3) / 4) * 4;
+  return (size_t)(3 * G * (nrp + 8) + G * kChunkTiles * kDecTile + G * 128 + 96) * 4 +
+         (size_t)(4 * 16 + 4 * NG) * kDecTile * 2;
+}
+
+size_t combine_lds_bytes(int G, int64_t n_refs, int n_split) {
+  const int64_t nrp = ((n_refs + 3) / 4) * 4;
+  return (size_t)(G * nrp + G * n_split + 8 * G * 32 + G) * 4;
+}
+
+// Whether the decode kernels' LDS fits one CU (160 KiB).
+bool decode_fits(int G, int group, int64_t n_refs, int n_split) {
+  const int NG = 128 / group;
+  return decode_lds_bytes(G, NG, n_refs) <= 160 * 1024 &&
+         combine_lds_bytes(G, n_refs, n_split) <= 160 * 1024;
+}
+
+template <typename T, int BITS, int NG, int KM>
 hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
                            const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
                            const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
@@ -444,53 +710,71 @@ hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
                            hipStream_t st) {
   const int G = n_q_heads / H;
   float* qk = (float*)ws;
-  const size_t qkb = (size_t)n_inst * n_q_heads * n_refs * 4;
-  float* part = (float*)((char*)ws + (qkb + 255) / 256 * 256);
-  hipLaunchKernelGGL(k_qk_table<T>, dim3(H, (unsigned)n_inst), dim3(256), 0, st, (const T*)q,
-                     (const T*)ref_kv, qk, G, H, n_refs);
+  float* part = (float*)((char*)ws + qk_bytes(n_inst, n_q_heads, n_refs));
+  const int64_t nrp = ((n_refs + 3) / 4) * 4;
+  hipLaunchKernelGGL(k_qk_table<T>, dim3((unsigned)((nrp + 255) / 256), H, (unsigned)n_inst),
+                     dim3(256), 0, st, (const T*)q, (const T*)ref_kv, qk, G, H, n_refs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t nrp = ((n_refs + 3) / 4) * 4;
-  const size_t lds = ((size_t)2 * G * nrp + 16 * kDecTile + NG * kDecTile) * 4;
-  auto kern = k_decode<T, BITS, NG>;
+  const size_t lds = decode_lds_bytes(G, NG, n_refs);
+  auto kern = k_decode<T, BITS, NG, KM>;
   if (lds > 64 * 1024) {
-    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds);
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3(n_split, H, (unsigned)n_inst), dim3(64), lds, st, (const T*)q,
-                     idx, ck, cv, sc16, qk, part, alpha, N, n_refs, sc, k, G, H, n_split);
+  hipLaunchKernelGGL(kern, dim3(n_split, H, (unsigned)n_inst), dim3(256), lds, st, (const T*)q,
+                     (const T*)ref_kv, idx, ck, cv, sc16, qk, part, alpha, N, n_refs, sc, k, G, H,
+                     n_split);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_combine<T>, dim3(n_q_heads, (unsigned)n_inst), dim3(128),
-                     (size_t)nrp * 4, st, part, (const T*)ref_kv, out, G, H, n_refs, n_split);
+  const size_t clds = combine_lds_bytes(G, n_refs, n_split);
+  if (clds > 64 * 1024) {
+    e = hipFuncSetAttribute((const void*)k_combine<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)clds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_combine<T>, dim3(H, (unsigned)n_inst, kCombChunks), dim3(256), clds, st,
+                     part, (const T*)ref_kv, out, G, H, n_refs, n_split);
   return hipGetLastError();
 }
 
-template <typename T, int BITS>
-hipError_t launch_decode_g(int group, const void* q, int n_q_heads, const uint16_t* idx,
+template <typename T, int BITS, int NG>
+hipError_t launch_decode_k(int k, const void* q, int n_q_heads, const uint16_t* idx,
                            const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
                            const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
-                           int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc, int k,
+                           int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
+                           hipStream_t st) {
+  if (k <= 4)
+    return launch_decode_t<T, BITS, NG, 4>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
+  if (k <= 8)
+    return launch_decode_t<T, BITS, NG, 8>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
+  return launch_decode_t<T, BITS, NG, 16>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
+}
+
+template <typename T, int BITS>
+hipError_t launch_decode_g(int group, int k, const void* q, int n_q_heads, const uint16_t* idx,
+                           const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
+                           const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
+                           int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
                            hipStream_t st) {
   if (group == 32)
-    return launch_decode_t<T, BITS, 4>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
+    return launch_decode_k<T, BITS, 4>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, st);
   if (group == 64)
-    return launch_decode_t<T, BITS, 2>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
-  return launch_decode_t<T, BITS, 1>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
+    return launch_decode_k<T, BITS, 2>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, st);
+  return launch_decode_k<T, BITS, 1>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, st);
 }
 
 template <typename T>
-hipError_t launch_decode_b(int bits, int group, const void* q, int n_q_heads, const uint16_t* idx,
-                           const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
-                           const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
-                           int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc, int k,
-                           hipStream_t st) {
+hipError_t launch_decode_b(int bits, int group, int k, const void* q, int n_q_heads,
+                           const uint16_t* idx, const void* ref_kv, const uint8_t* ck,
+                           const uint8_t* cv, const uint16_t* sc16, float alpha, float* out,
+                           int n_split, void* ws, int64_t n_inst, int H, int64_t N,
+                           int64_t n_refs, Sched sc, hipStream_t st) {
   if (bits == 2)
-    return launch_decode_g<T, 2>(group, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
+    return launch_decode_g<T, 2>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, st);
   if (bits == 4)
-    return launch_decode_g<T, 4>(group, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
-  return launch_decode_g<T, 8>(group, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
+    return launch_decode_g<T, 4>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, st);
+  return launch_decode_g<T, 8>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, st);
 }
 
 hipError_t launch_decode(int dtype, int bits, const void* q, int n_q_heads, const uint16_t* idx,
@@ -499,8 +783,8 @@ hipError_t launch_decode(int dtype, int bits, const void* q, int n_q_heads, cons
                          void* ws, int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
                          int k, int group, hipStream_t st) {
   if (dtype == 0)
-    return launch_decode_b<float>(bits, group, q, n_q_heads, idx, ref_kv, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
-  return launch_decode_b<__bf16>(bits, group, q, n_q_heads, idx, ref_kv, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
+    return launch_decode_b<float>(bits, group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, n_refs, sc, st);
+  return launch_decode_b<__bf16>(bits, group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, n_refs, sc, st);
 }
 
 }  // namespace rkv

@@ -87,19 +87,79 @@ __device__ inline void store_codes(uint8_t* p, const int (&c)[8]) {
 }
 
 // Fixed-order fp32 mean of the selected reference rows (8 dims of them).
-template <typename T>
-__device__ inline void ref_mean8(const T* __restrict__ refs, const uint16_t* __restrict__ irow,
-                                 int keff, float (&m)[8]) {
-  float acc[8];
-  load8(refs + (int64_t)irow[0] * 128, acc);
-  for (int j = 1; j < keff; ++j) {
-    float r[8];
-    load8(refs + (int64_t)irow[j] * 128, r);
+// All k_eff row loads are issued before the first add; the adds then run in
+// ascending slot order.
+template <int KM>
+__device__ inline void load_slots(const uint16_t* __restrict__ irow, int k, uint32_t (&sl)[KM]) {
+  if (k == KM) {
+    if constexpr (KM == 4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(irow);
+      sl[0] = v.x & 0xFFFF; sl[1] = v.x >> 16; sl[2] = v.y & 0xFFFF; sl[3] = v.y >> 16;
+    } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = acc[e] + r[e];
+      for (int c = 0; c < KM / 8; ++c) {
+        const uint4 v = *reinterpret_cast<const uint4*>(irow + 8 * c);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sl[8 * c + 2 * e] = w[e] & 0xFFFF;
+          sl[8 * c + 2 * e + 1] = w[e] >> 16;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KM; ++j) sl[j] = j < k ? irow[j] : 0;
+  }
+}
+
+template <typename T>
+struct Raw8 {
+  uint4 v[sizeof(T) / 2];
+};
+
+template <typename T>
+__device__ inline void load_raw8(const T* p, Raw8<T>& r) {
+#pragma unroll
+  for (int c = 0; c < (int)(sizeof(T) / 2); ++c) r.v[c] = reinterpret_cast<const uint4*>(p)[c];
+}
+
+__device__ inline void widen8(const Raw8<__bf16>& r, float (&x)[8]) {
+  x[0] = bf16_lo(r.v[0].x); x[1] = bf16_hi(r.v[0].x);
+  x[2] = bf16_lo(r.v[0].y); x[3] = bf16_hi(r.v[0].y);
+  x[4] = bf16_lo(r.v[0].z); x[5] = bf16_hi(r.v[0].z);
+  x[6] = bf16_lo(r.v[0].w); x[7] = bf16_hi(r.v[0].w);
+}
+
+__device__ inline void widen8(const Raw8<float>& r, float (&x)[8]) {
+  x[0] = __uint_as_float(r.v[0].x); x[1] = __uint_as_float(r.v[0].y);
+  x[2] = __uint_as_float(r.v[0].z); x[3] = __uint_as_float(r.v[0].w);
+  x[4] = __uint_as_float(r.v[1].x); x[5] = __uint_as_float(r.v[1].y);
+  x[6] = __uint_as_float(r.v[1].z); x[7] = __uint_as_float(r.v[1].w);
+}
+
+template <typename T, int KM>
+__device__ inline void ref_mean8(const T* __restrict__ refs, const uint16_t* __restrict__ irow,
+                                 int k, int keff, float (&m)[8]) {
+  uint32_t sl[KM];
+  load_slots<KM>(irow, k, sl);
+  Raw8<T> raw[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j)
+    if (j < keff) load_raw8(refs + (int64_t)sl[j] * 128, raw[j]);
+  float acc[8];
+  widen8(raw[0], acc);
+#pragma unroll
+  for (int j = 1; j < KM; ++j) {
+    if (j < keff) {
+      float r[8];
+      widen8(raw[j], r);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + r[e];
+    }
   }
   if (is_pow2(keff)) {
-    const float inv = 1.0f / (float)keff;  // exact power of two
+    const float inv = __uint_as_float((uint32_t)(127 - __builtin_ctz(keff)) << 23);  // 1/keff exactly
 #pragma unroll
     for (int e = 0; e < 8; ++e) m[e] = acc[e] * inv;
   } else {
@@ -112,7 +172,7 @@ __device__ inline void ref_mean8(const T* __restrict__ refs, const uint16_t* __r
 constexpr int kQTokens = 16;   // tokens per step (512 threads)
 constexpr int kVTile = 32;     // tokens per transposed V tile
 
-template <typename T, int BITS>
+template <typename T, int BITS, int KM>
 __global__ __launch_bounds__(512) void k_quantize(
     const T* __restrict__ K, const T* __restrict__ V, const uint16_t* __restrict__ idx,
     const T* __restrict__ ref_kv, uint8_t* __restrict__ codes_k,
@@ -130,7 +190,7 @@ __global__ __launch_bounds__(512) void k_quantize(
   const T* refs = ref_kv + (ih * 2 + plane) * n_refs * 128 + 8 * dl;
   constexpr float qmax = BITS ? (float)((1 << (BITS - 1)) - 1) : 0.f;
   const float inv_qmax = BITS ? 1.0f / qmax : 0.f;
-  const float tol = (qmax + 1.f) * 0x1p-22f;
+  const float tol = (qmax + 1.f) * 0x1p-21f;  // >= 2x the error of z * rcp(s)
   const int lanes_per_group = group >> 3;
   const int n_groups = 128 / group;
 
@@ -141,8 +201,8 @@ __global__ __launch_bounds__(512) void k_quantize(
       if (tok < c1) {
         float x[8], m[8], z[8];
         load8(src + tok * 128, x);
-        const int keff = (int)min((int64_t)k, sched_count_le(tok, sc));
-        ref_mean8(refs, idx + (ih * N + tok) * k, keff, m);
+        const int keff = (int)min((int64_t)k, sched_count_le((int32_t)tok, sc));
+        ref_mean8<T, KM>(refs, idx + (ih * N + tok) * k, k, keff, m);
 #pragma unroll
         for (int e = 0; e < 8; ++e) z[e] = x[e] - m[e];
         if constexpr (BITS == 0) {
@@ -158,7 +218,7 @@ __global__ __launch_bounds__(512) void k_quantize(
           const uint16_t sb = exact_scale_bits(a, qmax, inv_qmax);
           const float s = half_bits_to_f32(sb);
           if (s > 0.f) {
-            const float rs = 1.0f / s;
+            const float rs = __builtin_amdgcn_rcpf(s);  // within 1 ulp of 1/s
 #pragma unroll
             for (int e = 0; e < 8; ++e) c[e] = exact_code(z[e], s, rs, qmax, tol);
           }
@@ -201,7 +261,7 @@ __device__ inline int code_at(const uint8_t* row, int t) {
   return v >= (1 << (BITS - 1)) ? v - (1 << BITS) : v;
 }
 
-template <typename T, int BITS>
+template <typename T, int BITS, int KM>
 __global__ __launch_bounds__(512) void k_reconstruct(
     const uint16_t* __restrict__ idx, const T* __restrict__ ref_kv,
     const uint8_t* __restrict__ codes_k, const uint8_t* __restrict__ codes_v,
@@ -216,15 +276,15 @@ __global__ __launch_bounds__(512) void k_reconstruct(
   const T* refs = ref_kv + (ih * 2 + plane) * n_refs * 128 + 8 * dl;
   float* dst = (plane ? Vh : Kh) + (ih * N + tok) * 128 + 8 * dl;
   float out[8];
-  const int64_t slot = sched_slot(tok, sc);
+  const int64_t slot = sched_slot((int32_t)tok, sc);
   if (slot >= 0) {
     load8(refs + slot * 128, out);
     store8(dst, out);
     return;
   }
   float m[8];
-  const int keff = (int)min((int64_t)k, sched_count_le(tok, sc));
-  ref_mean8(refs, idx + (ih * N + tok) * k, keff, m);
+  const int keff = (int)min((int64_t)k, sched_count_le((int32_t)tok, sc));
+  ref_mean8<T, KM>(refs, idx + (ih * N + tok) * k, k, keff, m);
   if constexpr (BITS == 0) {
     const double* r = reinterpret_cast<const double*>(plane ? codes_v : codes_k) +
                       (ih * N + tok) * 128 + 8 * dl;
@@ -260,7 +320,9 @@ hipError_t launch_quantize_t(const void* K, const void* V, const uint16_t* idx,
                              int k, int group, hipStream_t st) {
   const int chunk = 256;
   const int64_t nchunks = (N + chunk - 1) / chunk;
-  hipLaunchKernelGGL((k_quantize<T, BITS>), dim3((unsigned)nchunks, H, (unsigned)n_inst),
+  auto kern = k <= 4 ? k_quantize<T, BITS, 4> : (k <= 8 ? k_quantize<T, BITS, 8>
+                                                       : k_quantize<T, BITS, 16>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)nchunks, H, (unsigned)n_inst),
                      dim3(512), 0, st, (const T*)K, (const T*)V, idx, (const T*)ref_kv, ck,
                      cv, sc16, N, n_refs, sc, k, group, chunk, H);
   return hipGetLastError();
@@ -295,7 +357,9 @@ hipError_t launch_recon_t(const uint16_t* idx, const void* ref_kv, const uint8_t
                           int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc, int k,
                           int group, hipStream_t st) {
   const int64_t blocks = (N + kQTokens - 1) / kQTokens;
-  hipLaunchKernelGGL((k_reconstruct<T, BITS>), dim3((unsigned)blocks, H, (unsigned)n_inst),
+  auto kern = k <= 4 ? k_reconstruct<T, BITS, 4>
+                     : (k <= 8 ? k_reconstruct<T, BITS, 8> : k_reconstruct<T, BITS, 16>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks, H, (unsigned)n_inst),
                      dim3(512), 0, st, idx, (const T*)ref_kv, ck, cv, sc16, Kh, Vh, N, n_refs,
                      sc, k, group, H);
   return hipGetLastError();

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void k_refstore(
   if (r >= total_refs) return;
   const int64_t ih = r / n_refs;
   const int64_t slot = r - ih * n_refs;
-  const int64_t pos = sched_pos(slot, sc);
+  const int64_t pos = sched_pos((int32_t)slot, sc);
   const T* kr = K + (ih * N + pos) * 128;
   const T* vr = V + (ih * N + pos) * 128;
   T* dk = ref_kv + ((ih * 2 + 0) * n_refs + slot) * 128;
@@ -129,7 +129,11 @@ __device__ inline bf16x8 load_key_frag(const T* p, bool valid) {
 }
 
 // One block = 4 waves x 32 tokens of one (instance, head).  Blocks are
-// issued from the end of the sequence (most candidates) backwards.
+// issued from the end of the sequence (most candidates) backwards.  Tiles of
+// 32 reference keys (+ norms) are staged in LDS, double-buffered and loaded
+// one tile ahead by the whole block; each wave reads its A operands from LDS.
+constexpr int kRowPad = 136;  // bf16 per staged key row: 128 + 8 (bank spread)
+
 template <typename T, int KM>
 __global__ __launch_bounds__(256, 2) void k_dist_topk(
     const T* __restrict__ K, const __bf16* __restrict__ refkey,
@@ -137,22 +141,26 @@ __global__ __launch_bounds__(256, 2) void k_dist_topk(
     int64_t n_refs, Sched sc, int k, int H, int n_tiles) {
   __shared__ float sb_e[4][kSurv][64];
   __shared__ uint16_t sb_j[4][kSurv][64];
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) __bf16 kbuf[2][32][kRowPad];
+  __shared__ __attribute__((aligned(16))) float nbuf[2][32];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
   const int tile = n_tiles - 1 - (int)blockIdx.x;
   const int64_t ih = (int64_t)blockIdx.z * H + blockIdx.y;
-  const int64_t row0 = (int64_t)tile * 128 + w * 32;
-  if (row0 >= N) return;
+  const int64_t blk0 = (int64_t)tile * 128;
+  const int64_t row0 = blk0 + w * 32;
+  const bool active = row0 < N;
   const int n = lane & 31;
   const int half = lane >> 5;
   const int64_t i = row0 + n;
   const bool valid_row = i < N;
+  const int64_t blk_last = (blk0 + 127 < N) ? blk0 + 127 : N - 1;
+  const int ntile_blk = (int)((sched_count_le((int32_t)blk_last, sc) + 31) / 32);
   const int64_t last_row = (row0 + 31 < N) ? row0 + 31 : N - 1;
-  const int64_t nc_wave = sched_count_le(last_row, sc);
-  const int64_t nc_first = sched_count_le(row0, sc);
-  const int64_t my_last = valid_row ? sched_count_le(i, sc) - 1 : -1;
-  const int ntile = (int)((nc_wave + 31) / 32);
-  const int full_tiles = (int)(nc_first / 32);
+  const int ntile = active ? (int)((sched_count_le((int32_t)last_row, sc) + 31) / 32) : 0;
+  const int full_tiles = active ? (int)(sched_count_le((int32_t)row0, sc) / 32) : 0;
+  const int64_t my_last = valid_row ? sched_count_le((int32_t)i, sc) - 1 : -1;
 
   // B operand: -2 * bf16(key) of this lane's token, dims 16s + 8*half + [0,8).
   bf16x8 bfrag[8];
@@ -161,30 +169,47 @@ __global__ __launch_bounds__(256, 2) void k_dist_topk(
 #pragma unroll
     for (int s = 0; s < 8; ++s) bfrag[s] = load_key_frag(krow + 16 * s, valid_row);
   }
-  const __bf16* rk = refkey + ih * n_refs * 128 + 8 * half;
+  const __bf16* rk = refkey + ih * n_refs * 128;
   const float* rn = refnorm + ih * n_refs;
 
-  auto tile_scores = [&](int rt, f32x16& acc) {
-    const int r0 = rt * 32;
-    const int slot_a = r0 + n;
-    bf16x8 a[8];
-    if (slot_a < n_refs) {
+  // cooperative staging: 512 chunks of 16 B per tile, 2 per thread
+  auto gload = [&](int rt, uint4 (&v)[2], float& nv) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        a[s] = *reinterpret_cast<const bf16x8*>(rk + (int64_t)slot_a * 128 + 16 * s);
-    } else {
+    for (int c = 0; c < 2; ++c) {
+      const int chunk = tid + 256 * c;
+      const int64_t slot = (int64_t)rt * 32 + (chunk >> 4);
+      v[c] = slot < n_refs ? *reinterpret_cast<const uint4*>(rk + slot * 128 + (chunk & 15) * 8)
+                           : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < 32) {
+      const int64_t slot = (int64_t)rt * 32 + tid;
+      nv = slot < n_refs ? rn[slot] : 0.f;
+    }
+  };
+  auto lstore = [&](int b, const uint4 (&v)[2], float nv) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) a[s] = bf16x8{};
+    for (int c = 0; c < 2; ++c) {
+      const int chunk = tid + 256 * c;
+      *reinterpret_cast<uint4*>(&kbuf[b][chunk >> 4][(chunk & 15) * 8]) = v[c];
+    }
+    if (tid < 32) nbuf[b][tid] = nv;
+  };
+  auto tile_scores = [&](int rt, int b, f32x16& acc) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 nn = *reinterpret_cast<const float4*>(&nbuf[b][8 * q4 + 4 * half]);
+      acc[4 * q4 + 0] = nn.x;
+      acc[4 * q4 + 1] = nn.y;
+      acc[4 * q4 + 2] = nn.z;
+      acc[4 * q4 + 3] = nn.w;
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int sl = r0 + acc_row(r, half);
-      acc[r] = sl < n_refs ? rn[sl] : 0.f;
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kbuf[b][n][16 * s + 8 * half]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[s], acc, 0, 0, 0);
     }
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], bfrag[s], acc, 0, 0, 0);
     if (rt >= full_tiles) {
+      const int r0 = rt * 32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int sl = r0 + acc_row(r, half);
@@ -192,17 +217,35 @@ __global__ __launch_bounds__(256, 2) void k_dist_topk(
       }
     }
   };
+  // Streams every candidate tile of the block through LDS; `epi(rt, acc)`
+  // consumes this wave's scores of tile rt.
+  auto stream = [&](auto&& epi) {
+    uint4 pre[2];
+    float pn = 0.f;
+    gload(0, pre, pn);
+    lstore(0, pre, pn);
+    __syncthreads();
+    for (int rt = 0; rt < ntile_blk; ++rt) {
+      const bool more = rt + 1 < ntile_blk;
+      if (more) gload(rt + 1, pre, pn);
+      if (rt < ntile) {
+        f32x16 acc;
+        tile_scores(rt, rt & 1, acc);
+        epi(rt, acc);
+      }
+      if (more) lstore((rt + 1) & 1, pre, pn);
+      __syncthreads();
+    }
+  };
 
   // ---- pass 1: bucket minima -> tau
   float bk[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) bk[r] = INFINITY;
-  for (int rt = 0; rt < ntile; ++rt) {
-    f32x16 acc;
-    tile_scores(rt, acc);
+  stream([&](int, const f32x16& acc) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) bk[r] = fminf(bk[r], acc[r]);
-  }
+  });
   float tau;
   {
     float top[KM];
@@ -221,9 +264,7 @@ __global__ __launch_bounds__(256, 2) void k_dist_topk(
   float* be = &sb_e[w][0][lane];
   uint16_t* bj = &sb_j[w][0][lane];
   int cnt = 0;
-  for (int rt = 0; rt < ntile; ++rt) {
-    f32x16 acc;
-    tile_scores(rt, acc);
+  stream([&](int rt, const f32x16& acc) {
     const int r0 = rt * 32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -234,7 +275,8 @@ __global__ __launch_bounds__(256, 2) void k_dist_topk(
       }
     }
     if (__any(cnt > kSurv - 16)) lane_compact<KM>(be, bj, cnt, tau, k);
-  }
+  });
+  if (!active) return;
 
   // ---- final: merge the row's two lists (this lane and lane ^ 32)
   const int cnt_b = __shfl_xor(cnt, 32);

@@ -28,6 +28,7 @@ hipError_t launch_decode(int dtype, int bits, const void* q, int n_q_heads, cons
                          void* ws, int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
                          int k, int group, hipStream_t st);
 size_t decode_ws_bytes(int64_t n_inst, int H, int n_q_heads, int n_split, int64_t n_refs);
+bool decode_fits(int G, int group, int64_t n_refs, int n_split);
 }  // namespace rkv
 
 using rkv::Sched;
@@ -39,14 +40,16 @@ thread_local int32_t g_last_hip = 0;
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+constexpr int64_t kMaxPos = int64_t(1) << 30;  // positions must stay below 2^30
+
 bool sched_ok(rkv_stride s) {
-  if (s.base < 1) return false;
-  if (s.double_after < 0) return false;
+  if (s.base < 1 || s.base > (1 << 20)) return false;
+  if (s.double_after < 0 || s.double_after > kMaxPos) return false;
   if (s.double_after > 0 && s.double_after % (2 * (int64_t)s.base) != 0) return false;
   return true;
 }
 
-Sched to_sched(rkv_stride s) { return Sched{s.base, s.double_after}; }
+Sched to_sched(rkv_stride s) { return rkv::make_sched(s.base, s.double_after); }
 
 rkv_status hip_status(hipError_t e) {
   if (e == hipSuccess) return RKV_OK;
@@ -60,6 +63,7 @@ rkv_status check_shape(const rkv_cache* c) {
   if (!c) return RKV_ERR_INVALID_ARG;
   if (c->dtype != RKV_F32 && c->dtype != RKV_BF16) return RKV_ERR_INVALID_ARG;
   if (c->n_inst < 0 || c->n_kv_heads < 1 || c->seq_len < 0) return RKV_ERR_INVALID_ARG;
+  if (c->seq_len > kMaxPos) return RKV_ERR_INVALID_ARG;
   if (c->n_inst > 65535 || c->n_kv_heads > 65535) return RKV_ERR_INVALID_ARG;
   if (!sched_ok(c->stride)) return RKV_ERR_INVALID_ARG;
   if (c->k < 1 || c->k > 16) return RKV_ERR_INVALID_ARG;
@@ -68,7 +72,7 @@ rkv_status check_shape(const rkv_cache* c) {
   if (c->bits != 0) {
     if (c->group != 32 && c->group != 64 && c->group != 128) return RKV_ERR_INVALID_ARG;
   }
-  const int64_t nr = rkv::sched_count(c->seq_len, to_sched(c->stride));
+  const int64_t nr = rkv::sched_count((int32_t)c->seq_len, to_sched(c->stride));
   if (nr > 65535) return RKV_ERR_RANGE;
   return RKV_OK;
 }
@@ -76,7 +80,7 @@ rkv_status check_shape(const rkv_cache* c) {
 rkv_status check_ready(const rkv_cache* c) {
   rkv_status s = check_shape(c);
   if (s != RKV_OK) return s;
-  if (c->n_refs != rkv::sched_count(c->seq_len, to_sched(c->stride))) return RKV_ERR_INVALID_ARG;
+  if (c->n_refs != rkv::sched_count((int32_t)c->seq_len, to_sched(c->stride))) return RKV_ERR_INVALID_ARG;
   if (c->n_inst == 0 || c->seq_len == 0) return RKV_OK;
   if (!c->ref_idx || !c->codes_k || !c->codes_v || !c->ref_kv) return RKV_ERR_INVALID_ARG;
   if (c->bits != 0 && !c->scales) return RKV_ERR_INVALID_ARG;
@@ -110,19 +114,21 @@ size_t encode_ws(const rkv_cache* c) {
 extern "C" {
 
 int64_t rkv_num_refs(int64_t seq_len, rkv_stride stride) {
-  if (!sched_ok(stride) || seq_len < 0) return -1;
-  return rkv::sched_count(seq_len, to_sched(stride));
+  if (!sched_ok(stride) || seq_len < 0 || seq_len > kMaxPos) return -1;
+  return rkv::sched_count((int32_t)seq_len, to_sched(stride));
 }
 
 int64_t rkv_ref_position(int64_t slot, rkv_stride stride) {
   if (!sched_ok(stride) || slot < 0) return -1;
-  return rkv::sched_pos(slot, to_sched(stride));
+  const Sched sc = to_sched(stride);
+  if (slot >= rkv::sched_count((int32_t)kMaxPos, sc)) return -1;  // position beyond 2^30
+  return rkv::sched_pos((int32_t)slot, sc);
 }
 
 rkv_status rkv_cache_init(rkv_cache* c) {
   rkv_status s = check_shape(c);
   if (s != RKV_OK) return s;
-  c->n_refs = rkv::sched_count(c->seq_len, to_sched(c->stride));
+  c->n_refs = rkv::sched_count((int32_t)c->seq_len, to_sched(c->stride));
   return RKV_OK;
 }
 
@@ -130,7 +136,7 @@ rkv_status rkv_cache_sizes(const rkv_cache* c, size_t sizes[5]) {
   if (!sizes) return RKV_ERR_INVALID_ARG;
   rkv_status s = check_shape(c);
   if (s != RKV_OK) return s;
-  if (c->n_refs != rkv::sched_count(c->seq_len, to_sched(c->stride))) return RKV_ERR_INVALID_ARG;
+  if (c->n_refs != rkv::sched_count((int32_t)c->seq_len, to_sched(c->stride))) return RKV_ERR_INVALID_ARG;
   sizes_of(c, sizes);
   return RKV_OK;
 }
@@ -139,7 +145,7 @@ rkv_status rkv_encode_workspace(const rkv_cache* c, size_t* bytes) {
   if (!bytes) return RKV_ERR_INVALID_ARG;
   rkv_status s = check_shape(c);
   if (s != RKV_OK) return s;
-  if (c->n_refs != rkv::sched_count(c->seq_len, to_sched(c->stride))) return RKV_ERR_INVALID_ARG;
+  if (c->n_refs != rkv::sched_count((int32_t)c->seq_len, to_sched(c->stride))) return RKV_ERR_INVALID_ARG;
   *bytes = encode_ws(c);
   return RKV_OK;
 }
@@ -208,7 +214,7 @@ rkv_status rkv_decode_workspace(const rkv_cache* c, int32_t n_q_heads, int32_t n
   if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0 || n_split < 1 || n_split > 4096)
     return RKV_ERR_INVALID_ARG;
   *bytes = rkv::decode_ws_bytes(c->n_inst, c->n_kv_heads, n_q_heads, n_split,
-                                rkv::sched_count(c->seq_len, to_sched(c->stride)));
+                                rkv::sched_count((int32_t)c->seq_len, to_sched(c->stride)));
   return RKV_OK;
 }
 
@@ -222,6 +228,7 @@ rkv_status rkv_decode_attn(const void* q, int32_t n_q_heads, const rkv_cache* c,
   if (c->bits == 0) return RKV_ERR_UNSUPPORTED;
   const int G = n_q_heads / c->n_kv_heads;
   if (G * (c->head_dim / c->group) > 16) return RKV_ERR_UNSUPPORTED;
+  if (!rkv::decode_fits(G, c->group, c->n_refs, n_split)) return RKV_ERR_UNSUPPORTED;
   if (c->n_inst == 0) return RKV_OK;
   if (!q || !out) return RKV_ERR_INVALID_ARG;
   if (c->seq_len == 0) return RKV_ERR_INVALID_ARG;

@@ -13,56 +13,91 @@
 
 namespace rkv {
 
-struct Sched {
-  int64_t base;
-  int64_t A;  // 0 = fixed stride
+// Division by a constant d >= 1 for 0 <= n < 2^31 with one 32x32->64
+// multiply: l = ceil(log2 d), m = floor(2^(31+l)/d) + 1, n/d = (n*m) >> (31+l)
+// (Granlund-Montgomery: m*d lies in (2^(31+l), 2^(31+l) + 2^l]).
+struct FastDiv {
+  uint32_t d, m, s;
 };
 
-// References in [0, n).
-__host__ __device__ inline int64_t sched_count(int64_t n, Sched s) {
+__host__ __device__ inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const uint64_t m = ((1ull << (31 + l)) / d) + 1;
+  return FastDiv{d, (uint32_t)m, 31 + l};
+}
+
+__host__ __device__ inline uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)n * f.m) >> f.s);
+}
+
+__host__ __device__ inline int bit_width(uint32_t x) {
+#ifdef __HIP_DEVICE_COMPILE__
+  return x ? 32 - __clz(x) : 0;
+#else
+  return x ? 32 - __builtin_clz(x) : 0;
+#endif
+}
+
+// Schedule constants (positions < 2^31).  A = 0: fixed stride.
+struct Sched {
+  int32_t base;
+  int32_t A;
+  int32_t c0;      // references below A: A / base
+  int32_t per;     // references per doubling band: A / (2 base)
+  FastDiv fb;      // / base
+  FastDiv fa;      // / A
+  FastDiv fp;      // / per
+};
+
+inline Sched make_sched(int64_t base, int64_t A) {
+  Sched s;
+  s.base = (int32_t)base;
+  s.A = (int32_t)A;
+  s.c0 = A ? (int32_t)(A / base) : 0;
+  s.per = A ? (int32_t)(A / (2 * base)) : 1;
+  s.fb = make_fastdiv((uint32_t)base);
+  s.fa = make_fastdiv(A ? (uint32_t)A : 1u);
+  s.fp = make_fastdiv((uint32_t)s.per);
+  return s;
+}
+
+// References in [0, n), 0 <= n < 2^31.
+__host__ __device__ inline int32_t sched_count(int32_t n, const Sched& s) {
   if (n <= 0) return 0;
-  if (s.A == 0 || n <= s.A) return (n + s.base - 1) / s.base;
-  int64_t c = s.A / s.base;
-  const int64_t per_band = s.A / (2 * s.base);
-  int64_t lo = s.A;
-  int band = 1;
-  for (;;) {
-    const int64_t st = s.base << band;
-    if (n <= 2 * lo) return c + (n - lo + st - 1) / st;
-    c += per_band;
-    lo *= 2;
-    ++band;
-  }
+  if (s.A == 0 || n <= s.A) return (int32_t)fdiv((uint32_t)(n + s.base - 1), s.fb);
+  const int b = bit_width(fdiv((uint32_t)(n - 1), s.fa));  // band of position n-1
+  const int32_t lo = s.A << (b - 1);
+  const uint32_t st = (uint32_t)s.base << b;
+  return s.c0 + (b - 1) * s.per +
+         (int32_t)(fdiv((uint32_t)(n - lo) + st - 1, s.fb) >> b);
 }
 
 // References at positions <= i.
-__host__ __device__ inline int64_t sched_count_le(int64_t i, Sched s) {
+__host__ __device__ inline int32_t sched_count_le(int32_t i, const Sched& s) {
   return sched_count(i + 1, s);
 }
 
 // Position of reference `slot`.
-__host__ __device__ inline int64_t sched_pos(int64_t slot, Sched s) {
-  if (s.A == 0) return slot * s.base;
-  const int64_t c0 = s.A / s.base;
-  if (slot < c0) return slot * s.base;
-  const int64_t per = s.A / (2 * s.base);
-  const int64_t m = slot - c0;
-  const int band = (int)(m / per) + 1;
-  return (s.A << (band - 1)) + (m % per) * (s.base << band);
+__host__ __device__ inline int32_t sched_pos(int32_t slot, const Sched& s) {
+  if (s.A == 0 || slot < s.c0) return slot * s.base;
+  const uint32_t m = (uint32_t)(slot - s.c0);
+  const uint32_t bq = fdiv(m, s.fp);
+  const int band = (int)bq + 1;
+  return (s.A << (band - 1)) + (int32_t)(m - bq * (uint32_t)s.per) * (s.base << band);
 }
 
 // Slot of position i if it is a reference, else -1.
-__host__ __device__ inline int64_t sched_slot(int64_t i, Sched s) {
-  if (s.A == 0 || i < s.A) return (i % s.base == 0) ? i / s.base : -1;
-  int64_t lo = s.A;
-  int band = 1;
-  while (i >= 2 * lo) {
-    lo *= 2;
-    ++band;
+__host__ __device__ inline int32_t sched_slot(int32_t i, const Sched& s) {
+  if (s.A == 0 || i < s.A) {
+    const uint32_t q = fdiv((uint32_t)i, s.fb);
+    return (uint32_t)i == q * (uint32_t)s.base ? (int32_t)q : -1;
   }
-  const int64_t st = s.base << band;
-  if ((i - lo) % st != 0) return -1;
-  return s.A / s.base + (band - 1) * (s.A / (2 * s.base)) + (i - lo) / st;
+  const int b = bit_width(fdiv((uint32_t)i, s.fa));
+  const uint32_t off = (uint32_t)(i - (s.A << (b - 1)));
+  const uint32_t q = fdiv(off, s.fb) >> b;
+  if (off != q * ((uint32_t)s.base << b)) return -1;
+  return s.c0 + (b - 1) * s.per + (int32_t)q;
 }
 
 // ---------------------------------------------------------------- numbers

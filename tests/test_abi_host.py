@@ -54,6 +54,29 @@ def test_num_refs_and_positions_match_the_oracle_schedule(lib, n, base, A):
         assert lib.rkv_ref_position(s, _st(base, A)) == p
 
 
+@pytest.mark.parametrize("n,base,A", [(1_000_003, 7, 0), (1 << 20, 3, 3072), (600_000, 16, 4096),
+                                      (300_000, 5, 40), (262_144, 1, 2), (131072, 16, 4096)])
+def test_num_refs_and_positions_at_scale(lib, n, base, A):
+    """The library's constant-division schedule against a plain walk."""
+    T = oracle.ref_positions(n, base, A) if n <= 300_000 else None
+    if T is None:
+        pos, j = [], 0
+        while j < n:
+            s = base
+            if A and j >= A:
+                b = 0
+                while j >= A << b:
+                    b += 1
+                s = base << b
+            if j % s == 0:
+                pos.append(j)
+            j += 1 if (A and j >= A) or base > 1 else 1
+        T = np.array(pos)
+    assert lib.rkv_num_refs(n, _st(base, A)) == T.shape[0]
+    for s in list(range(0, T.shape[0], max(1, T.shape[0] // 2000))) + [T.shape[0] - 1]:
+        assert lib.rkv_ref_position(s, _st(base, A)) == T[s]
+
+
 def test_schedule_rejects_bad_strides(lib):
     assert lib.rkv_num_refs(100, _st(0)) == -1
     assert lib.rkv_num_refs(100, _st(16, 100)) == -1      # not a multiple of 2*base
