@@ -33,9 +33,18 @@ FLAGS = [
 ]
 
 
+# Per-file additions.  The distance/top-k kernel only orders finite or
+# infinite distances (never NaN), so IEEE NaN quieting is switched off there:
+# min/max/med3 then take their operands directly instead of canonicalising
+# each one first.
+FILE_FLAGS = {
+    "k_select.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -66,48 +66,126 @@ __device__ inline void topk_insert(float (&top)[KM], float v) {
   top[0] = fminf(top[0], v);
 }
 
+// k-th smallest (1 <= k <= KM) of an ascending list: the largest of its
+// first k entries.  Written as a masked max so that it stays in registers
+// (a select chain over t == k - 1 can be folded into a memory-indexed load).
 template <int KM>
 __device__ inline float topk_get(const float (&top)[KM], int k) {
-  float r = top[0];
+  float r = -INFINITY;
 #pragma unroll
-  for (int t = 1; t < KM; ++t) r = (t == k - 1) ? top[t] : r;
+  for (int t = 0; t < KM; ++t) r = fmaxf(r, t < k ? top[t] : -INFINITY);
   return r;
 }
-
-constexpr int kSurv = 32;  // survivor list capacity per lane
 
 // Row of accumulator register r of a 32x32 MFMA tile for lane half `half`.
 __device__ inline int acc_row(int r, int half) { return (r & 3) + 8 * (r >> 2) + 4 * half; }
 
-// Keep this lane's own k best (distance, slot) entries; lists stay in slot
-// order.  Lowers tau to the lane's k-th value.
+// Survivor list capacity per (lane, token set): the lane's k best plus the 8
+// accumulator rows appended between two fullness checks.
 template <int KM>
-__device__ void lane_compact(float* be, uint16_t* bj, int& cnt, float& tau, int k) {
+constexpr int surv_cap() { return KM + 8; }
+
+// Loads a lane's survivor list (stride 64 entries in LDS) into registers;
+// entries past cnt read as +inf.
+template <int CAP>
+__device__ inline void load_list(const float* be, const uint16_t* bj, int cnt, float (&e)[CAP],
+                                 float (&js)[CAP]) {
+#pragma unroll
+  for (int c = 0; c < CAP; ++c) {
+    const float v = be[c * 64];
+    const uint16_t j = bj[c * 64];
+    e[c] = c < cnt ? v : INFINITY;
+    js[c] = (float)j;
+  }
+}
+
+// Cuts a lane's list to its own k best, keeping slot order; among entries
+// equal to the k-th value the earlier (lower) slots stay.  Lowers tau to the
+// k-th value: an entry dropped here is beaten by k kept ones, and every later
+// entry has a higher slot.
+template <int KM, int CAP>
+__device__ __forceinline__ void lane_compact(float* be, uint16_t* bj, int& cnt, float& tau, int k) {
   if (cnt <= k) return;
+  float e[CAP], js[CAP];
+  load_list<CAP>(be, bj, cnt, e, js);
   float top[KM];
 #pragma unroll
   for (int t = 0; t < KM; ++t) top[t] = INFINITY;
-  for (int c = 0; c < cnt; ++c) topk_insert(top, be[c * 64]);
+#pragma unroll
+  for (int c = 0; c < CAP; ++c) topk_insert(top, e[c]);
   const float t = topk_get(top, k);
   int nless = 0;
-  for (int c = 0; c < cnt; ++c) nless += be[c * 64] < t;
-  int quota = k - nless;
-  int out = 0;
-  for (int c = 0; c < cnt; ++c) {
-    const float e = be[c * 64];
-    bool take = e < t;
-    if (e == t && quota > 0) {
-      take = true;
-      --quota;
-    }
+#pragma unroll
+  for (int c = 0; c < CAP; ++c) nless += e[c] < t;
+  const int quota = k - nless;
+  int out = 0, ties = 0;
+#pragma unroll
+  for (int c = 0; c < CAP; ++c) {
+    const bool tie = e[c] == t;
+    const bool take = e[c] < t || (tie && ties < quota);
+    ties += tie;
     if (take) {
-      be[out * 64] = e;
-      bj[out * 64] = bj[c * 64];
+      be[out * 64] = e[c];
+      bj[out * 64] = (uint16_t)js[c];
       ++out;
     }
   }
   cnt = out;
   tau = fminf(tau, t);
+}
+
+// The keff nearest references of one token from the survivor lists of its
+// two lanes (this lane and lane ^ 32, both calling), lowest slot first among
+// equal distances; returns them in ascending slot order, 65535 past keff.
+template <int KM, int CAP>
+__device__ __forceinline__ void row_select(const float* be, const uint16_t* bj, int cnt, int keff,
+                           float (&sel)[KM]) {
+  float e[CAP], js[CAP];
+  load_list<CAP>(be, bj, cnt, e, js);
+  float top[KM];
+#pragma unroll
+  for (int t = 0; t < KM; ++t) top[t] = INFINITY;
+#pragma unroll
+  for (int c = 0; c < CAP; ++c) topk_insert(top, e[c]);
+  float mine[KM];
+#pragma unroll
+  for (int t = 0; t < KM; ++t) mine[t] = top[t];
+#pragma unroll
+  for (int t = 0; t < KM; ++t) topk_insert(top, __shfl_xor(mine[t], 32));
+  const float th = topk_get(top, keff);
+  int nless = 0, nties = 0;
+#pragma unroll
+  for (int c = 0; c < CAP; ++c) {
+    nless += e[c] < th;
+    nties += e[c] == th;
+  }
+  nless += __shfl_xor(nless, 32);
+  const int all_ties = nties + __shfl_xor(nties, 32);
+  const int quota = keff - nless;  // >= 1: th is the keff-th smallest
+  float slot_bound = 65536.f;      // ties at th are taken up to this slot
+  if (__any(all_ties > quota)) {
+    float tl[KM];
+#pragma unroll
+    for (int t = 0; t < KM; ++t) tl[t] = 65536.f;
+#pragma unroll
+    for (int c = 0; c < CAP; ++c) topk_insert(tl, e[c] == th ? js[c] : 65536.f);
+#pragma unroll
+    for (int t = 0; t < KM; ++t) mine[t] = tl[t];
+#pragma unroll
+    for (int t = 0; t < KM; ++t) topk_insert(tl, __shfl_xor(mine[t], 32));
+    slot_bound = topk_get(tl, quota);
+  }
+#pragma unroll
+  for (int t = 0; t < KM; ++t) sel[t] = 65535.f;
+#pragma unroll
+  for (int c = 0; c < CAP; ++c) {
+    const bool take = e[c] < th || (e[c] == th && js[c] <= slot_bound);
+    topk_insert(sel, take ? js[c] : 65535.f);
+  }
+#pragma unroll
+  for (int t = 0; t < KM; ++t) mine[t] = sel[t];
+#pragma unroll
+  for (int t = 0; t < KM; ++t) topk_insert(sel, __shfl_xor(mine[t], 32));
 }
 
 template <typename T>
@@ -128,46 +206,53 @@ __device__ inline bf16x8 load_key_frag(const T* p, bool valid) {
   return b;
 }
 
-// One block = 4 waves x 32 tokens of one (instance, head).  Blocks are
-// issued from the end of the sequence (most candidates) backwards.  Tiles of
-// 32 reference keys (+ norms) are staged in LDS, double-buffered and loaded
-// one tile ahead by the whole block; each wave reads its A operands from LDS.
+// One block = 4 waves x 64 tokens of one (instance, head); each wave holds
+// the B operands of two 32-token sets, so every A fragment read from LDS
+// feeds two independent MFMA chains.  Blocks are issued from the end of the
+// sequence (most candidates) backwards.  Tiles of 32 reference keys (+ norms)
+// are staged in LDS, double-buffered and loaded one tile ahead by the block.
 constexpr int kRowPad = 136;  // bf16 per staged key row: 128 + 8 (bank spread)
+constexpr int kSets = 2;      // 32-token sets per wave
+constexpr int kBlockRows = 4 * 32 * kSets;
 
+// Two blocks per CU while the survivor lists fit (k <= 8), else one.
 template <typename T, int KM>
-__global__ __launch_bounds__(256, 2) void k_dist_topk(
+__global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
     const T* __restrict__ K, const __bf16* __restrict__ refkey,
     const float* __restrict__ refnorm, uint16_t* __restrict__ idx_out, int64_t N,
-    int64_t n_refs, Sched sc, int k, int H, int n_tiles) {
-  __shared__ float sb_e[4][kSurv][64];
-  __shared__ uint16_t sb_j[4][kSurv][64];
+    int64_t n_refs, Sched sc, int k, int H, int n_blocks) {
+  constexpr int CAP = surv_cap<KM>();
+  __shared__ float sb_e[4][kSets][CAP][64];
+  __shared__ uint16_t sb_j[4][kSets][CAP][64];
   __shared__ __attribute__((aligned(16))) __bf16 kbuf[2][32][kRowPad];
   __shared__ __attribute__((aligned(16))) float nbuf[2][32];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int tile = n_tiles - 1 - (int)blockIdx.x;
+  const int blk = n_blocks - 1 - (int)blockIdx.x;
   const int64_t ih = (int64_t)blockIdx.z * H + blockIdx.y;
-  const int64_t blk0 = (int64_t)tile * 128;
-  const int64_t row0 = blk0 + w * 32;
+  const int64_t blk0 = (int64_t)blk * kBlockRows;
+  const int64_t row0 = blk0 + w * 32 * kSets;
   const bool active = row0 < N;
   const int n = lane & 31;
   const int half = lane >> 5;
-  const int64_t i = row0 + n;
-  const bool valid_row = i < N;
-  const int64_t blk_last = (blk0 + 127 < N) ? blk0 + 127 : N - 1;
+  const int64_t blk_last = (blk0 + kBlockRows - 1 < N) ? blk0 + kBlockRows - 1 : N - 1;
   const int ntile_blk = (int)((sched_count_le((int32_t)blk_last, sc) + 31) / 32);
-  const int64_t last_row = (row0 + 31 < N) ? row0 + 31 : N - 1;
+  const int64_t last_row = (row0 + 32 * kSets - 1 < N) ? row0 + 32 * kSets - 1 : N - 1;
   const int ntile = active ? (int)((sched_count_le((int32_t)last_row, sc) + 31) / 32) : 0;
   const int full_tiles = active ? (int)(sched_count_le((int32_t)row0, sc) / 32) : 0;
-  const int64_t my_last = valid_row ? sched_count_le((int32_t)i, sc) - 1 : -1;
-
-  // B operand: -2 * bf16(key) of this lane's token, dims 16s + 8*half + [0,8).
-  bf16x8 bfrag[8];
-  {
-    const T* krow = K + (ih * N + (valid_row ? i : 0)) * 128 + 8 * half;
+  bool valid_row[kSets];
+  int my_last[kSets];
+  // B operands: -2 * bf16(key) of token row0 + 32c + n, dims 16s + 8*half + [0,8).
+  bf16x8 bfrag[kSets][8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) bfrag[s] = load_key_frag(krow + 16 * s, valid_row);
+  for (int c = 0; c < kSets; ++c) {
+    const int64_t i = row0 + 32 * c + n;
+    valid_row[c] = i < N;
+    my_last[c] = valid_row[c] ? sched_count_le((int32_t)i, sc) - 1 : -1;
+    const T* krow = K + (ih * N + (valid_row[c] ? i : 0)) * 128 + 8 * half;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) bfrag[c][s] = load_key_frag(krow + 16 * s, valid_row[c]);
   }
   const __bf16* rk = refkey + ih * n_refs * 128;
   const float* rn = refnorm + ih * n_refs;
@@ -194,129 +279,142 @@ __global__ __launch_bounds__(256, 2) void k_dist_topk(
     }
     if (tid < 32) nbuf[b][tid] = nv;
   };
-  auto tile_scores = [&](int rt, int b, f32x16& acc) {
+  // acc[c][r]: e = |ref|^2 - 2 k.ref of candidate slot rt*32 + acc_row(r, half)
+  // for token row0 + 32c + n; +inf past the token's last candidate.
+  auto tile_scores = [&](int rt, int b, f32x16 (&acc)[kSets]) {
+    f32x16 init;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const float4 nn = *reinterpret_cast<const float4*>(&nbuf[b][8 * q4 + 4 * half]);
-      acc[4 * q4 + 0] = nn.x;
-      acc[4 * q4 + 1] = nn.y;
-      acc[4 * q4 + 2] = nn.z;
-      acc[4 * q4 + 3] = nn.w;
+      init[4 * q4 + 0] = nn.x;
+      init[4 * q4 + 1] = nn.y;
+      init[4 * q4 + 2] = nn.z;
+      init[4 * q4 + 3] = nn.w;
     }
+#pragma unroll
+    for (int c = 0; c < kSets; ++c) acc[c] = init;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kbuf[b][n][16 * s + 8 * half]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[s], acc, 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < kSets; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[c][s], acc[c], 0, 0, 0);
     }
     if (rt >= full_tiles) {
       const int r0 = rt * 32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int sl = r0 + acc_row(r, half);
-        if (sl > my_last) acc[r] = INFINITY;
+      for (int c = 0; c < kSets; ++c) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int sl = r0 + acc_row(r, half);
+          if (sl > my_last[c]) acc[c][r] = INFINITY;
+        }
       }
     }
   };
   // Streams every candidate tile of the block through LDS; `epi(rt, acc)`
-  // consumes this wave's scores of tile rt.
+  // consumes this wave's scores of tile rt.  Global loads run two tiles
+  // ahead: tile rt + 2 is requested while tile rt is scored, and tile rt + 1
+  // (requested one iteration earlier) is written to the free LDS buffer
+  // after it.  The loop is unrolled by two so the two register sets of tiles
+  // in flight alternate without copies.
   auto stream = [&](auto&& epi) {
-    uint4 pre[2];
-    float pn = 0.f;
-    gload(0, pre, pn);
-    lstore(0, pre, pn);
+    uint4 pa[2], pb[2];
+    float na = 0.f, nb = 0.f;
+    gload(0, pa, na);
+    lstore(0, pa, na);
+    if (ntile_blk > 1) gload(1, pb, nb);
     __syncthreads();
-    for (int rt = 0; rt < ntile_blk; ++rt) {
-      const bool more = rt + 1 < ntile_blk;
-      if (more) gload(rt + 1, pre, pn);
+    auto step = [&](int rt, uint4 (&st)[2], float& sn, uint4 (&ld)[2], float& ln) {
+      if (rt + 2 < ntile_blk) gload(rt + 2, ld, ln);
       if (rt < ntile) {
-        f32x16 acc;
+        f32x16 acc[kSets];
         tile_scores(rt, rt & 1, acc);
         epi(rt, acc);
       }
-      if (more) lstore((rt + 1) & 1, pre, pn);
+      if (rt + 1 < ntile_blk) lstore((rt + 1) & 1, st, sn);
       __syncthreads();
+    };
+    for (int rt = 0; rt < ntile_blk; rt += 2) {
+      step(rt, pb, nb, pa, na);
+      if (rt + 1 < ntile_blk) step(rt + 1, pa, na, pb, nb);
     }
   };
 
-  // ---- pass 1: bucket minima -> tau
-  float bk[16];
+  // ---- pass 1: bucket minima -> tau per token
+  float bk[kSets][16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) bk[r] = INFINITY;
-  stream([&](int, const f32x16& acc) {
+  for (int c = 0; c < kSets; ++c)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) bk[r] = fminf(bk[r], acc[r]);
+    for (int r = 0; r < 16; ++r) bk[c][r] = INFINITY;
+  stream([&](int, const f32x16 (&acc)[kSets]) {
+#pragma unroll
+    for (int c = 0; c < kSets; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bk[c][r] = fminf(bk[c][r], acc[c][r]);
   });
-  float tau;
-  {
+  float tau[kSets];
+#pragma unroll
+  for (int c = 0; c < kSets; ++c) {
     float top[KM];
 #pragma unroll
     for (int t = 0; t < KM; ++t) top[t] = INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      topk_insert(top, bk[r]);
-      topk_insert(top, __shfl_xor(bk[r], 32));
+      topk_insert(top, bk[c][r]);
+      topk_insert(top, __shfl_xor(bk[c][r], 32));
     }
-    tau = topk_get(top, k);
-    if (!(tau < INFINITY)) tau = FLT_MAX;
+    tau[c] = topk_get(top, k);
+    if (!(tau[c] < INFINITY)) tau[c] = FLT_MAX;
   }
 
   // ---- pass 2: collect candidates <= tau
-  float* be = &sb_e[w][0][lane];
-  uint16_t* bj = &sb_j[w][0][lane];
-  int cnt = 0;
-  stream([&](int rt, const f32x16& acc) {
+  int cnt[kSets];
+#pragma unroll
+  for (int c = 0; c < kSets; ++c) cnt[c] = 0;
+  stream([&](int rt, const f32x16 (&acc)[kSets]) {
     const int r0 = rt * 32;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (acc[r] <= tau) {
-        be[cnt * 64] = acc[r];
-        bj[cnt * 64] = (uint16_t)(r0 + acc_row(r, half));
-        ++cnt;
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int c = 0; c < kSets; ++c) {
+        float* be = &sb_e[w][c][0][lane];
+        uint16_t* bj = &sb_j[w][c][0][lane];
+#pragma unroll
+        for (int r = 8 * h; r < 8 * h + 8; ++r) {
+          if (acc[c][r] <= tau[c]) {
+            be[cnt[c] * 64] = acc[c][r];
+            bj[cnt[c] * 64] = (uint16_t)(r0 + acc_row(r, half));
+            ++cnt[c];
+          }
+        }
+      }
+      bool full = false;
+#pragma unroll
+      for (int c = 0; c < kSets; ++c) full |= cnt[c] > CAP - 8;
+      if (__any(full)) {
+#pragma unroll
+        for (int c = 0; c < kSets; ++c)
+          lane_compact<KM, CAP>(&sb_e[w][c][0][lane], &sb_j[w][c][0][lane], cnt[c], tau[c], k);
       }
     }
-    if (__any(cnt > kSurv - 16)) lane_compact<KM>(be, bj, cnt, tau, k);
   });
   if (!active) return;
 
-  // ---- final: merge the row's two lists (this lane and lane ^ 32)
-  const int cnt_b = __shfl_xor(cnt, 32);
-  if (half != 0 || !valid_row) return;
-  const float* pe = &sb_e[w][0][lane + 32];
-  const uint16_t* pj = &sb_j[w][0][lane + 32];
-  const int keff = (int)((my_last + 1 < k) ? my_last + 1 : k);
-  float top[KM];
+  // ---- final: each token's keff nearest from its two lanes' lists
 #pragma unroll
-  for (int t = 0; t < KM; ++t) top[t] = INFINITY;
-  for (int c = 0; c < cnt; ++c) topk_insert(top, be[c * 64]);
-  for (int c = 0; c < cnt_b; ++c) topk_insert(top, pe[c * 64]);
-  const float t = topk_get(top, keff);
-  int nless = 0;
-  for (int c = 0; c < cnt; ++c) nless += be[c * 64] < t;
-  for (int c = 0; c < cnt_b; ++c) nless += pe[c * 64] < t;
-  int quota = keff - nless;
-  uint16_t* orow = idx_out + (ih * N + i) * k;
-  int pos = 0, ia = 0, ib = 0;
-  while (ia < cnt || ib < cnt_b) {
-    float e;
-    uint16_t j;
-    const bool from_a = ib >= cnt_b || (ia < cnt && bj[ia * 64] < pj[ib * 64]);
-    if (from_a) {
-      e = be[ia * 64];
-      j = bj[ia * 64];
-      ++ia;
-    } else {
-      e = pe[ib * 64];
-      j = pj[ib * 64];
-      ++ib;
+  for (int c = 0; c < kSets; ++c) {
+    const int keff = (my_last[c] + 1 < k) ? my_last[c] + 1 : k;
+    float sel[KM];
+    row_select<KM, CAP>(&sb_e[w][c][0][lane], &sb_j[w][c][0][lane], cnt[c],
+                        keff < 1 ? 1 : keff, sel);
+    if (half == 0 && valid_row[c]) {
+      uint16_t* orow = idx_out + (ih * N + row0 + 32 * c + n) * k;
+#pragma unroll
+      for (int t = 0; t < KM; ++t)
+        if (t < k) orow[t] = (uint16_t)sel[t];
     }
-    bool take = e < t;
-    if (e == t && quota > 0) {
-      take = true;
-      --quota;
-    }
-    if (take && pos < keff) orow[pos++] = j;
   }
-  for (; pos < k; ++pos) orow[pos] = 0xFFFF;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -346,10 +444,10 @@ template <typename T, int KM>
 hipError_t launch_topk_t(const void* K, const void* refkey, const float* refnorm,
                          uint16_t* idx, int64_t n_inst, int H, int64_t N, int64_t n_refs,
                          Sched sc, int k, hipStream_t st) {
-  const int n_tiles = (int)((N + 127) / 128);
-  hipLaunchKernelGGL((k_dist_topk<T, KM>), dim3(n_tiles, H, (unsigned)n_inst), dim3(256), 0,
+  const int n_blocks = (int)((N + kBlockRows - 1) / kBlockRows);
+  hipLaunchKernelGGL((k_dist_topk<T, KM>), dim3(n_blocks, H, (unsigned)n_inst), dim3(256), 0,
                      st, (const T*)K, (const __bf16*)refkey, refnorm, idx, N, n_refs, sc, k,
-                     H, n_tiles);
+                     H, n_blocks);
   return hipGetLastError();
 }
 
