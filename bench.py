@@ -72,6 +72,32 @@ def algorithmic(cfg, bits, n_refs, T_positions_count_le):
     return out
 
 
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from its committed rocprofv3 summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when there
+    is none for this workload or the kernel's sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith((" ", "|", "#")):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    try:
+        h = hashlib.sha256()
+        for src in fields["source_files"].split():
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != fields["source_sha256"]:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
 def cpu_info():
     model = ""
     try:
@@ -234,6 +260,7 @@ def main():
         gbps = alg["decode_layer_bytes"] / dmean / 1e9
         dec = {"us_per_layer": dmean * 1e6, "GBps": gbps, "frac_peak": gbps / HBM_PEAK_GBPS,
                "bytes_per_layer": alg["decode_layer_bytes"], "n_split": ns_layer,
+               "traffic_k_decode": measured_traffic("k_decode", cfg.name),
                "note": "QK table + split-K decode + combine of one layer's batch; "
                        "Infinity Cache flushed between repetitions"}
 
@@ -248,15 +275,20 @@ def main():
                             "note": "reference store + distance/top-k (two MFMA passes "
                                     "over the causal candidates; flops counted once)"},
     }
-    # dominant kernel of the step by time
+    # dominant kernel of the step by time; `traffic` = measured HBM bytes per
+    # launch (profiles/), null unless taken on the current kernel sources
     if qz_mean >= sel_mean:
         roof = {"bound": "hbm", "kernel": "k_quantize", "achieved": qz_gbps,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": qz_gbps / HBM_PEAK_GBPS,
-                "traffic": None}
+                "traffic": measured_traffic("k_quantize", cfg.name),
+                "algorithmic_bytes": alg["quantize_bytes"]}
     else:
-        roof = {"bound": "mfma", "kernel": "rkv_select_refs", "achieved": sel_tflops,
+        roof = {"bound": "mfma", "kernel": "k_dist_topk", "achieved": sel_tflops,
                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": sel_tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": None}
+                "frac": sel_tflops / BF16_MFMA_PEAK_TFLOPS,
+                "traffic": measured_traffic("k_dist_topk", cfg.name),
+                "algorithmic_flops": alg["select_flops"],
+                "note": "timed as rkv_select_refs = k_refstore (about 1 % of it) + k_dist_topk"}
 
     if a.copy_calib:
         src = torch.empty(a.copy_calib << 20, dtype=torch.uint8, device=dev)

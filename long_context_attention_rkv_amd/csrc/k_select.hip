@@ -16,9 +16,11 @@
 //           the k-th smallest of a row's 32 bucket minima is an upper bound
 //           tau on the row's k-th smallest distance;
 //   pass 2  recomputes the same MFMA tiles (bit-identical values) and appends
-//           candidates <= tau to a per-lane LDS list (about k per row);
-//   final   one lane per row takes the k smallest of the two lists of the
-//           row by (distance, slot), lowest slot first on ties.
+//           candidates <= tau to a per-lane LDS list (about k per row; a
+//           list near capacity is cut to the lane's own k best);
+//   final   the two lanes of a row load their lists into registers and, with
+//           shuffles, take the k smallest by (distance, slot), lowest slot
+//           first on ties, written in ascending slot order.
 #include <float.h>
 
 #include "rkv_common.h"
