@@ -25,7 +25,7 @@
 namespace rkv {
 
 // fp16 nearest to a/qmax, ties to even, saturating at 65504.  a >= 0 finite.
-__device__ inline uint16_t exact_scale_bits(float a, float qmax, float inv_qmax) {
+__device__ __noinline__ uint16_t exact_scale_bits_slow(float a, float qmax, float inv_qmax) {
   if (a == 0.f) return 0;
   uint16_t b = f32_to_half_bits_rne(a * inv_qmax);
   if (b >= 0x7C00) b = 0x7BFF;
@@ -46,6 +46,17 @@ __device__ inline uint16_t exact_scale_bits(float a, float qmax, float inv_qmax)
   return b;
 }
 
+// Same result as exact_scale_bits_slow.  y = a * fl(1/qmax) is within 2 ulp
+// of a/qmax, so its fp16 rounding is the exact one unless the 13 bits below
+// fp16 precision sit within 3 of the half-way pattern 0x1000 (or y is
+// outside the normal fp16 range); only those cases take the exact path.
+__device__ inline uint16_t exact_scale_bits(float a, float qmax, float inv_qmax) {
+  const float y = a * inv_qmax;
+  const int low = (int)(__float_as_uint(y) & 0x1FFFu) - 0x1000;
+  if (y >= 0x1p-14f && y < 65504.f && (low > 3 || low < -3)) return f32_to_half_bits_rne(y);
+  return exact_scale_bits_slow(a, qmax, inv_qmax);
+}
+
 // Integer nearest to z/s (ties to even), clamped to [-qmax, qmax].  s > 0.
 __device__ inline int exact_code(float z, float s, float rs, float qmax, float tol) {
   const float q = z * rs;
@@ -61,6 +72,57 @@ __device__ inline int exact_code(float z, float s, float rs, float qmax, float t
   }
   n = __builtin_amdgcn_fmed3f(n, -qmax, qmax);
   return (int)n;
+}
+
+// Codes of 8 residuals with scale s (rs ~ 1/s within 1 ulp; rs = 0 when
+// s = 0).  t = fl(z*rs + 1.5*2^23) holds the integer nearest to the exact
+// product z*rs (ties to even) in its low mantissa bits; fma(z, rs, M - t) is
+// that rounding's remainder.  When every remainder is clear of 1/2 by more
+// than the product's error, z*rs and z/s round alike; otherwise the lane
+// decides each code exactly.  Returned as M + code (so the low bits are the
+// two's complement code), clamped to [-qmax, qmax].
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+
+__device__ inline void codes8(const float (&z)[8], float s, float rs, float qmax, float tol,
+                              uint32_t (&u)[8]) {
+  float t[8];
+  float emax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    t[e] = __builtin_fmaf(z[e], rs, kMagic);
+    const float r = __builtin_fmaf(z[e], rs, kMagic - t[e]);
+    emax = fmaxf(emax, fabsf(r));
+  }
+  if (emax > 0.5f - tol) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = kMagic + (float)exact_code(z[e], s, rs, qmax, tol);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    u[e] = __float_as_uint(__builtin_amdgcn_fmed3f(t[e], kMagic - qmax, kMagic + qmax));
+}
+
+template <int BITS>
+__device__ inline void store_codes(uint8_t* p, const uint32_t (&c)[8]) {
+  if constexpr (BITS == 4) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) w |= (c[t] & 0xF) << (4 * t);
+    *reinterpret_cast<uint32_t*>(p) = w;
+  } else if constexpr (BITS == 8) {
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      w0 |= (c[t] & 0xFF) << (8 * t);
+      w1 |= (c[t + 4] & 0xFF) << (8 * t);
+    }
+    *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
+  } else {
+    uint32_t w = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) w |= (c[t] & 0x3) << (2 * t);
+    *reinterpret_cast<uint16_t*>(p) = (uint16_t)w;
+  }
 }
 
 template <int BITS>
@@ -172,82 +234,207 @@ __device__ inline void ref_mean8(const T* __restrict__ refs, const uint16_t* __r
 constexpr int kQTokens = 16;   // tokens per step (512 threads)
 constexpr int kVTile = 32;     // tokens per transposed V tile
 
+// Slots of one token when it has all k = KM candidates (one or two 16-byte
+// loads; k = 4 takes 8 bytes).
+template <int KM>
+__device__ inline void load_slots_full(const uint16_t* __restrict__ irow, uint32_t (&sl)[KM]) {
+  if constexpr (KM == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(irow);
+    sl[0] = v.x & 0xFFFF; sl[1] = v.x >> 16; sl[2] = v.y & 0xFFFF; sl[3] = v.y >> 16;
+  } else {
+#pragma unroll
+    for (int c = 0; c < KM / 8; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4*>(irow + 8 * c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sl[8 * c + 2 * e] = w[e] & 0xFFFF;
+        sl[8 * c + 2 * e + 1] = w[e] >> 16;
+      }
+    }
+  }
+}
+
+// Mean of exactly KM selected rows (8 dims each): fixed ascending-slot fp32
+// sum, then one multiply by 1/KM (a power of two, exact) or a division.
+template <typename T, int KM>
+__device__ inline void ref_mean8_full(const T* __restrict__ refs, const uint32_t (&sl)[KM],
+                                      float (&m)[8]) {
+  Raw8<T> raw[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) load_raw8(refs + sl[j] * 128u, raw[j]);
+  float acc[8];
+  widen8(raw[0], acc);
+#pragma unroll
+  for (int j = 1; j < KM; ++j) {
+    float r[8];
+    widen8(raw[j], r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] + r[e];
+  }
+  constexpr float inv = 1.0f / KM;  // KM is 4, 8 or 16: exact
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m[e] = acc[e] * inv;
+}
+
+// Loads of one position issued a step ahead on the fast path: its K or V row
+// (8 dims) and its KM slots.
+template <typename T, int KM>
+struct PosLoads {
+  Raw8<T> x;
+  uint4 sl[(KM + 7) / 8];
+};
+
+template <typename T, int KM>
+__device__ inline void issue_pos_loads(const T* __restrict__ src, const uint16_t* __restrict__ idx_h,
+                                       int tok, PosLoads<T, KM>& p) {
+  load_raw8(src + (uint32_t)tok * 128u, p.x);
+  const uint16_t* irow = idx_h + (uint32_t)tok * KM;
+  if constexpr (KM == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(irow);
+    p.sl[0] = make_uint4(v.x, v.y, 0, 0);
+  } else {
+#pragma unroll
+    for (int c = 0; c < KM / 8; ++c) p.sl[c] = *reinterpret_cast<const uint4*>(irow + 8 * c);
+  }
+}
+
+template <typename T, int KM>
+__device__ inline void unpack_slots(const PosLoads<T, KM>& p, uint32_t (&sl)[KM]) {
+#pragma unroll
+  for (int c = 0; c < (KM + 7) / 8; ++c) {
+    const uint32_t w[4] = {p.sl[c].x, p.sl[c].y, p.sl[c].z, p.sl[c].w};
+#pragma unroll
+    for (int e = 0; e < 4 && 8 * c + 2 * e < KM; ++e) {
+      sl[8 * c + 2 * e] = w[e] & 0xFFFF;
+      sl[8 * c + 2 * e + 1] = w[e] >> 16;
+    }
+  }
+}
+
+// One block = one chunk of positions of one (instance, head); 16 positions
+// per step, 32 lanes per position (16 on the K row, 16 on the V row, 8 dims
+// each).  When every position of the chunk has k = KM candidates (all but
+// the first chunks of a sequence) a position's row and slots are loaded one
+// step ahead and its mean is the unpredicated fast form; otherwise k_eff is
+// taken per position.
 template <typename T, int BITS, int KM>
 __global__ __launch_bounds__(512) void k_quantize(
     const T* __restrict__ K, const T* __restrict__ V, const uint16_t* __restrict__ idx,
     const T* __restrict__ ref_kv, uint8_t* __restrict__ codes_k,
     uint8_t* __restrict__ codes_v, uint16_t* __restrict__ scales, int64_t N,
     int64_t n_refs, Sched sc, int k, int group, int chunk, int H) {
-  __shared__ int8_t vt[128][kVTile + 4];
+  __shared__ int8_t vt[128][kVTile + 1];  // odd pitch: the 16 writing lanes hit 16 banks
   const int tid = threadIdx.x;
-  const int tok_l = tid >> 5;          // token within the step
+  const int tok_l = tid >> 5;          // position within the step
   const int plane = (tid >> 4) & 1;    // 0 = K, 1 = V
   const int dl = tid & 15;             // dims [8*dl, 8*dl+8)
   const int64_t ih = (int64_t)blockIdx.z * H + blockIdx.y;
-  const int64_t c0 = (int64_t)blockIdx.x * chunk;
-  const int64_t c1 = (c0 + chunk < N) ? c0 + chunk : N;
+  const int c0 = (int)blockIdx.x * chunk;
+  const int c1 = (int)((c0 + chunk < N) ? c0 + chunk : N);
+  const int n_groups = 128 / group;
+  const int lanes_per_group = group >> 3;
+  // per-(instance, head) bases; positions below index them with 32-bit offsets
   const T* src = (plane ? V : K) + ih * N * 128 + 8 * dl;
   const T* refs = ref_kv + (ih * 2 + plane) * n_refs * 128 + 8 * dl;
+  const uint16_t* idx_h = idx + ih * N * k;
+  uint8_t* ck_h = codes_k + ih * N * (128 * BITS / 8) + dl * BITS;
+  uint16_t* sc_h = scales + ih * N * 2 * n_groups + plane * n_groups + dl / lanes_per_group;
   constexpr float qmax = BITS ? (float)((1 << (BITS - 1)) - 1) : 0.f;
-  const float inv_qmax = BITS ? 1.0f / qmax : 0.f;
-  const float tol = (qmax + 1.f) * 0x1p-21f;  // >= 2x the error of z * rcp(s)
-  const int lanes_per_group = group >> 3;
-  const int n_groups = 128 / group;
+  constexpr float inv_qmax = BITS ? 1.0f / qmax : 0.f;
+  constexpr float tol = (qmax + 1.f) * 0x1p-21f;  // >= 2x the error of z * rcp(s)
+  const bool fast = k == KM && sched_count_le(c0, sc) >= KM;
 
-  for (int64_t tb = c0; tb < c1; tb += kVTile) {
-    for (int sub = 0; sub < kVTile; sub += kQTokens) {
-      const int64_t tok = tb + sub + tok_l;
-      int c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (tok < c1) {
-        float x[8], m[8], z[8];
-        load8(src + tok * 128, x);
-        const int keff = (int)min((int64_t)k, sched_count_le((int32_t)tok, sc));
-        ref_mean8<T, KM>(refs, idx + (ih * N + tok) * k, k, keff, m);
+  // Residual, scale and codes of position `tok` from its row x and mean m;
+  // writes the K codes and the scale, returns the codes (V lanes stage them).
+  auto finish = [&](int tok, const float (&x)[8], const float (&m)[8], uint32_t (&u)[8]) {
+    float z[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = x[e] - m[e];
-        if constexpr (BITS == 0) {
-          double* dst = reinterpret_cast<double*>(plane ? codes_v : codes_k) +
-                        (ih * N + tok) * 128 + 8 * dl;
+    for (int e = 0; e < 8; ++e) z[e] = x[e] - m[e];
+    if constexpr (BITS == 0) {
+      double* dst = reinterpret_cast<double*>(plane ? codes_v : codes_k) +
+                    (ih * N + tok) * 128 + 8 * dl;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) dst[e] = (double)x[e] - (double)m[e];
-        } else {
-          float a = 0.f;
+      for (int e = 0; e < 8; ++e) dst[e] = (double)x[e] - (double)m[e];
+    } else {
+      float a = 0.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(z[e]));
-          for (int off = 1; off < lanes_per_group; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
-          const uint16_t sb = exact_scale_bits(a, qmax, inv_qmax);
-          const float s = half_bits_to_f32(sb);
-          if (s > 0.f) {
-            const float rs = __builtin_amdgcn_rcpf(s);  // within 1 ulp of 1/s
+      for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(z[e]));
+      a = group_max(a, lanes_per_group);
+      const uint16_t sb = exact_scale_bits(a, qmax, inv_qmax);
+      const float s = half_bits_to_f32(sb);
+      const float rs = s > 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;  // within 1 ulp of 1/s
+      codes8(z, s, rs, qmax, tol, u);
+      if ((dl & (lanes_per_group - 1)) == 0) sc_h[(uint32_t)tok * (2 * n_groups)] = sb;
+      if (plane == 0) store_codes<BITS>(ck_h + (uint32_t)tok * (16 * BITS), u);
+    }
+  };
+  // One step of the fast path: use the loads in `cur`, request the next
+  // step's into `nxt`.
+  auto fast_step = [&](int tok, PosLoads<T, KM>& cur, PosLoads<T, KM>& nxt, uint32_t (&u)[8]) {
+    if (tok + kQTokens < c1) issue_pos_loads<T, KM>(src, idx_h, tok + kQTokens, nxt);
+    if (tok < c1) {
+      uint32_t sl[KM];
+      unpack_slots<T, KM>(cur, sl);
+      float x[8], m[8];
+      ref_mean8_full<T, KM>(refs, sl, m);
+      widen8(cur.x, x);
+      finish(tok, x, m, u);
+    }
+  };
+  auto slow_step = [&](int tok, uint32_t (&u)[8]) {
+    if (tok < c1) {
+      float x[8], m[8];
+      load8(src + (uint32_t)tok * 128u, x);
+      const int keff = min(k, sched_count_le(tok, sc));
+      ref_mean8<T, KM>(refs, idx_h + (uint32_t)tok * k, k, keff, m);
+      finish(tok, x, m, u);
+    }
+  };
+  auto stage_v = [&](int sub, const uint32_t (&u)[8]) {
+    if constexpr (BITS != 0) {
+      if (plane == 1) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) c[e] = exact_code(z[e], s, rs, qmax, tol);
-          }
-          if ((dl & (lanes_per_group - 1)) == 0)
-            scales[((ih * N + tok) * 2 + plane) * n_groups + dl / lanes_per_group] = sb;
-          if (plane == 0)
-            store_codes<BITS>(codes_k + (ih * N + tok) * (128 * BITS / 8) + dl * BITS, c);
-        }
-      }
-      if constexpr (BITS != 0) {
-        if (plane == 1) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) vt[8 * dl + e][sub + tok_l] = (int8_t)c[e];
-        }
+        for (int e = 0; e < 8; ++e) vt[8 * dl + e][sub + tok_l] = (int8_t)u[e];
       }
     }
+  };
+  auto store_v_tile = [&](int tb) {
     if constexpr (BITS != 0) {
       __syncthreads();
       // 512 threads: dim = tid/4, tokens 8*(tid%4) .. +7 of the tile
       const int dim = tid >> 2;
-      const int u = tid & 3;
+      const int uu = tid & 3;
       int cc[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) cc[e] = vt[dim][8 * u + e];
+      for (int e = 0; e < 8; ++e) cc[e] = vt[dim][8 * uu + e];
       const int64_t tile = tb / kVTile;
       store_codes<BITS>(codes_v + ((ih * ((N + kVTile - 1) / kVTile) + tile) * 128 + dim) *
-                                      (kVTile * BITS / 8) + u * BITS,
+                                      (kVTile * BITS / 8) + uu * BITS,
                         cc);
       __syncthreads();
+    }
+  };
+
+  if (fast) {
+    PosLoads<T, KM> pa, pb;
+    if (c0 + tok_l < c1) issue_pos_loads<T, KM>(src, idx_h, c0 + tok_l, pa);
+    for (int tb = c0; tb < c1; tb += kVTile) {
+      uint32_t u0[8] = {0, 0, 0, 0, 0, 0, 0, 0}, u1[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      fast_step(tb + tok_l, pa, pb, u0);
+      stage_v(0, u0);
+      fast_step(tb + kQTokens + tok_l, pb, pa, u1);
+      stage_v(kQTokens, u1);
+      store_v_tile(tb);
+    }
+  } else {
+    for (int tb = c0; tb < c1; tb += kVTile) {
+      for (int sub = 0; sub < kVTile; sub += kQTokens) {
+        uint32_t u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        slow_step(tb + sub + tok_l, u);
+        stage_v(sub, u);
+      }
+      store_v_tile(tb);
     }
   }
 }

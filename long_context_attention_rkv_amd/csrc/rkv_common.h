@@ -141,6 +141,20 @@ __device__ inline void store8(float* p, const float (&x)[8]) {
 
 __device__ inline bool is_pow2(int v) { return (v & (v - 1)) == 0; }
 
+// Lane exchanges inside a DPP row (16 lanes), no LDS traffic.
+#define RKV_DPP_F32(v, ctrl) \
+  __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), (ctrl), 0xF, 0xF, false))
+
+// Maximum over aligned groups of `lanes` consecutive lanes (4, 8 or 16):
+// swaps within quads (xor 1, xor 2), then half-row and row mirrors.
+__device__ inline float group_max(float v, int lanes) {
+  v = fmaxf(v, RKV_DPP_F32(v, 0xB1));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, RKV_DPP_F32(v, 0x4E));    // quad_perm [2,3,0,1]
+  if (lanes >= 8) v = fmaxf(v, RKV_DPP_F32(v, 0x141));   // row_half_mirror
+  if (lanes >= 16) v = fmaxf(v, RKV_DPP_F32(v, 0x140));  // row_mirror
+  return v;
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
