@@ -175,8 +175,33 @@ __global__ __launch_bounds__(256) void k_qk_table(const T* __restrict__ q,
 }
 
 constexpr int kChunkTiles = 32;   // tiles (x32 tokens) per softmax chunk of a block
+constexpr int kLgPad = 16;
 
-template <typename T, int BITS, int NG, int KM>
+// Slot (or -1) and k_eff of position `tok` in the tile starting at `tb`.
+// The tile's references are the slots [cb, ce) (wave-uniform: every lane of
+// the wave works on the same tile), so a lane only compares its position
+// against those few reference positions.
+struct TileRefs {
+  int32_t cb, ce;
+};
+__device__ inline TileRefs tile_refs(int32_t tb, int32_t N, const Sched& sc) {
+  const int32_t te = tb + kDecTile < N ? tb + kDecTile : N;
+  return TileRefs{sched_count(tb, sc), sched_count(te, sc)};
+}
+__device__ inline void pos_info(int32_t tok, const TileRefs& tr, const Sched& sc, int k,
+                                int32_t& slot, int& keff) {
+  int32_t cnt = tr.cb;
+  slot = -1;
+  for (int32_t r = tr.cb; r < tr.ce; ++r) {
+    const int32_t p = sched_pos(r, sc);
+    if (p <= tok) ++cnt;
+    if (p == tok) slot = r;
+  }
+  keff = cnt < k ? cnt : k;
+}
+
+// EX: every row of ref_idx holds exactly KM slots (k == KM).
+template <typename T, int BITS, int NG, int KM, bool EX>
 __global__ __launch_bounds__(256, 2) void k_decode(
     const T* __restrict__ q, const T* __restrict__ ref_kv, const uint16_t* __restrict__ idx,
     const uint8_t* __restrict__ codes_k, const uint8_t* __restrict__ codes_v,
@@ -185,6 +210,9 @@ __global__ __launch_bounds__(256, 2) void k_decode(
   constexpr int HPL = 4 / NG;  // query heads per lane in the score layout
   constexpr int GS = 128 / NG;  // dims per scale group
   constexpr int CT = kChunkTiles * kDecTile;  // tokens per chunk
+  // logit rows padded by 16 floats: the 4 heads of one position (lane quads)
+  // then fall in different banks
+  constexpr int CTP = CT + kLgPad;
   extern __shared__ float lds[];
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
   // Per-head LDS rows are nrp + 8 floats apart: the G heads of one token touch
@@ -194,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(
   unsigned long long* w_s =
       reinterpret_cast<unsigned long long*>(qk_s + G * ls);       // [G][ls] fixed point
   float* lg_s = reinterpret_cast<float*>(w_s + G * ls);           // [G][CT] logits of a chunk
-  float* o_s = lg_s + G * CT;                                     // [G][128]
+  float* o_s = lg_s + G * CTP;                                    // [G][128]
   float* m_s = o_s + G * 128;                                     // [16] block max per head
   float* wm_s = m_s + 16;                                         // [4][16] wave maxima
   float* sc_s = wm_s + 64;                                        // [16] rescale factors
@@ -211,10 +239,11 @@ __global__ __launch_bounds__(256, 2) void k_decode(
   const int64_t inst = blockIdx.z;
   const int64_t ih = inst * H + kvh;
   const int Hq = H * G;
-  const int64_t tiles = (N + kDecTile - 1) / kDecTile;
-  const int64_t tps = (tiles + n_split - 1) / n_split;
-  const int64_t t0 = split * tps;
-  const int64_t t1 = (t0 + tps < tiles) ? t0 + tps : tiles;
+  const int32_t tiles = (int32_t)((N + kDecTile - 1) / kDecTile);
+  const int32_t tps = (tiles + n_split - 1) / n_split;
+  const int32_t t0 = split * tps;
+  const int32_t t1 = (t0 + tps < tiles) ? t0 + tps : tiles;
+  const int32_t N32 = (int32_t)N;
   const T* qh = q + (inst * Hq + kvh * G) * 128;
 
   // ---- prologue: QK table into LDS, clears
@@ -263,14 +292,15 @@ __global__ __launch_bounds__(256, 2) void k_decode(
 #pragma unroll
   for (int b = 0; b < 8; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto load_slots_of = [&](int64_t tok, uint32_t (&iw)[KM / 2]) {
-    if (k == KM) {
-      load_words<KM / 2>(ix + tok * KM, iw);
+  auto load_slots_of = [&](int32_t tok, uint32_t (&iw)[KM / 2]) {
+    if constexpr (EX) {
+      load_words<KM / 2>(ix + (uint32_t)tok * KM, iw);
     } else {
+      const uint16_t* row = ix + (uint32_t)tok * (uint32_t)k;
 #pragma unroll
       for (int j = 0; j < KM / 2; ++j) {
-        const uint32_t lo = 2 * j < k ? ix[tok * k + 2 * j] : 0;
-        const uint32_t hi = 2 * j + 1 < k ? ix[tok * k + 2 * j + 1] : 0;
+        const uint32_t lo = 2 * j < k ? row[2 * j] : 0;
+        const uint32_t hi = 2 * j + 1 < k ? row[2 * j + 1] : 0;
         iw[j] = lo | (hi << 16);
       }
     }
@@ -286,14 +316,14 @@ __global__ __launch_bounds__(256, 2) void k_decode(
     uint32_t sw[2][NG];
     uint32_t iw[2][KM / 2];
   };
-  auto loadA = [&](int64_t t, ARegs& r) {
-    const int64_t tb = t * kDecTile;
+  auto loadA = [&](int32_t t, ARegs& r) {
+    const int32_t tb = t * kDecTile;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int64_t tok = tb + 16 * b + n;
-      if (tok < N) {
-        load_words<BITS>(ck + (tb + 16 * b) * (16 * BITS), r.kw[b]);
-        load_words<NG>(sc16 + (tb + 16 * b) * 2 * NG, r.sw[b]);
+      const int32_t tok = tb + 16 * b + n;
+      if (tok < N32) {
+        load_words<BITS>(ck + (uint32_t)(tb + 16 * b) * (16 * BITS), r.kw[b]);
+        load_words<NG>(sc16 + (uint32_t)(tb + 16 * b) * (2 * NG), r.sw[b]);
         load_slots_of(tok, r.iw[b]);
       } else {
 #pragma unroll
@@ -305,12 +335,14 @@ __global__ __launch_bounds__(256, 2) void k_decode(
       }
     }
   };
-  auto computeA = [&](int64_t t, int64_t c0, const ARegs& r, float (&wmax)[HPL]) {
-    const int64_t tb = t * kDecTile;
+  auto computeA = [&](int32_t t, int32_t c0, const ARegs& r, float (&wmax)[HPL]) {
+    const int32_t tb = t * kDecTile;
+    const TileRefs tr = tile_refs(tb, N32, sc);
+    const bool ftile = EX && tr.cb >= KM;  // wave-uniform
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int64_t tok = tb + 16 * b + n;
-      const bool valid = tok < N;
+      const int32_t tok = tb + 16 * b + n;
+      const bool valid = tok < N32;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -324,14 +356,34 @@ __global__ __launch_bounds__(256, 2) void k_decode(
         }
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], decode_codes<BITS>(w0, w1), acc, 0, 0, 0);
       }
-      const int32_t slot = valid ? sched_slot((int32_t)tok, sc) : -1;
-      const int keff = valid ? min(k, sched_count_le((int32_t)tok, sc)) : 0;
+      int32_t slot;
+      int keff;
+      pos_info(tok, tr, sc, k, slot, keff);
+      if (!valid) { slot = -1; keff = 0; }
       const float inv_keff = keff > 0 ? 1.0f / (float)keff : 0.f;
-      const int u = (int)(tok - c0 * kDecTile);
+      const int u = tok - c0 * kDecTile;
 #pragma unroll
       for (int hh = 0; hh < HPL; ++hh) {
         const int h = h0 + hh;
-        if (h < G) {
+        if (h < G && ftile) {
+          // every position of the tile has k = KM references: no predicates
+          // (positions past N read slot 0 and are masked to -inf)
+          const float* qrow = qk_s + h * ls;
+          float rs = 0.f;
+#pragma unroll
+          for (int j = 0; j < KM; ++j) rs += qrow[(r.iw[b][j >> 1] >> (16 * (j & 1))) & 0xFFFFu];
+          float res = 0.f;
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            const float sk = half_bits_to_f32((uint16_t)(r.sw[b][g >> 1] >> (16 * (g & 1))));
+            res = __builtin_fmaf(sk, acc[hh * NG + g], res);
+          }
+          const float sref = qrow[slot >= 0 ? slot : 0];
+          const float sc_ = slot >= 0 ? sref : res + rs * (1.0f / KM);
+          const float lg = valid ? alpha * sc_ : -INFINITY;
+          lg_s[h * CTP + u] = lg;
+          wmax[hh] = fmaxf(wmax[hh], lg);
+        } else if (h < G) {
           float lg = -INFINITY;
           if (valid) {
             const float* qrow = qk_s + h * ls;
@@ -353,15 +405,15 @@ __global__ __launch_bounds__(256, 2) void k_decode(
             }
             lg = alpha * sc_;
           }
-          lg_s[h * CT + u] = lg;
+          lg_s[h * CTP + u] = lg;
           wmax[hh] = fmaxf(wmax[hh], lg);
         }
       }
     }
   };
-  auto loadB = [&](int64_t t, BRegs& r) {
-    const int64_t tb = t * kDecTile;
-    const uint8_t* cvt = cv + t * 128 * (4 * BITS);
+  auto loadB = [&](int32_t t, BRegs& r) {
+    const int32_t tb = t * kDecTile;
+    const uint8_t* cvt = cv + (uint32_t)t * (128 * 4 * BITS);
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
       const uint8_t* pp = cvt + 16 * blk * (4 * BITS);
@@ -377,10 +429,10 @@ __global__ __launch_bounds__(256, 2) void k_decode(
     }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int64_t tok = tb + 16 * b + n;
-      if (tok < N) {
+      const int32_t tok = tb + 16 * b + n;
+      if (tok < N32) {
         load_slots_of(tok, r.iw[b]);
-        load_words<NG>(sc16 + (tb + 16 * b) * 2 * NG, r.sw[b]);
+        load_words<NG>(sc16 + (uint32_t)(tb + 16 * b) * (2 * NG), r.sw[b]);
       } else {
 #pragma unroll
         for (int j = 0; j < KM / 2; ++j) r.iw[b][j] = 0;
@@ -389,25 +441,42 @@ __global__ __launch_bounds__(256, 2) void k_decode(
       }
     }
   };
-  auto computeB = [&](int64_t t, int64_t c0, const BRegs& r, const float (&mh)[HPL]) {
-    const int64_t tb = t * kDecTile;
+  auto computeB = [&](int32_t t, int32_t c0, const BRegs& r, const float (&mh)[HPL]) {
+    const int32_t tb = t * kDecTile;
+    const TileRefs tr = tile_refs(tb, N32, sc);
+    const bool ftile = EX && tr.cb >= KM;  // wave-uniform
     float psum[HPL];
 #pragma unroll
     for (int hh = 0; hh < HPL; ++hh) psum[hh] = 0.f;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int64_t tok = tb + 16 * b + n;
-      const bool valid = tok < N;
-      const int32_t slot = valid ? sched_slot((int32_t)tok, sc) : -1;
-      const int keff = valid ? min(k, sched_count_le((int32_t)tok, sc)) : 0;
+      const int32_t tok = tb + 16 * b + n;
+      const bool valid = tok < N32;
+      int32_t slot;
+      int keff;
+      pos_info(tok, tr, sc, k, slot, keff);
+      if (!valid) { slot = -1; keff = 0; }
       const int u = 16 * b + n;
       const int pos = 8 * (u >> 3) + invperm_of<BITS>(u & 7);
-      const int uc = (int)(tok - c0 * kDecTile);
+      const int uc = tok - c0 * kDecTile;
 #pragma unroll
       for (int hh = 0; hh < HPL; ++hh) {
         const int h = h0 + hh;
-        if (h < G) {
-          const float lg = lg_s[h * CT + uc];
+        if (h < G && ftile) {
+          const float lg = lg_s[h * CTP + uc];
+          const float pv = valid ? __expf(lg - mh[hh]) : 0.f;
+          psum[hh] += pv;
+          unsigned long long* wrow = w_s + h * ls;
+          // a reference position adds p to its own slot and 0 to its row's
+          const bool isref = slot >= 0;
+          const unsigned long long pw = to_fixed32(isref ? 0.f : pv * (1.0f / KM));
+#pragma unroll
+          for (int j = 0; j < KM; ++j)
+            atomicAdd(wrow + ((r.iw[b][j >> 1] >> (16 * (j & 1))) & 0xFFFFu), pw);
+          if (isref) atomicAdd(wrow + slot, to_fixed32(pv));
+          pst[h * kDecTile + pos] = (_Float16)(isref ? 0.f : pv);
+        } else if (h < G) {
+          const float lg = lg_s[h * CTP + uc];
           const float pv = (valid && lg > -INFINITY) ? __expf(lg - mh[hh]) : 0.f;
           psum[hh] += pv;
           unsigned long long* wrow = w_s + h * ls;
@@ -464,20 +533,24 @@ __global__ __launch_bounds__(256, 2) void k_decode(
     __builtin_amdgcn_wave_barrier();
   };
 
-  for (int64_t c0 = t0; c0 < t1; c0 += kChunkTiles) {
-    const int64_t c1 = (c0 + kChunkTiles < t1) ? c0 + kChunkTiles : t1;
+  for (int32_t c0 = t0; c0 < t1; c0 += kChunkTiles) {
+    const int32_t c1 = (c0 + kChunkTiles < t1) ? c0 + kChunkTiles : t1;
     // ================= phase A: logits of the chunk into LDS (next tile prefetched)
     float wmax[HPL];
 #pragma unroll
     for (int hh = 0; hh < HPL; ++hh) wmax[hh] = -INFINITY;
     {
-      ARegs cur, nxt;
-      int64_t t = c0 + w;
-      if (t < c1) loadA(t, nxt);
+      // two register sets alternate (unrolled by 2): no copies of loads in flight
+      ARegs ra, rb;
+      int32_t t = c0 + w;
+      if (t < c1) loadA(t, ra);
       while (t < c1) {
-        cur = nxt;
-        if (t + 4 < c1) loadA(t + 4, nxt);
-        computeA(t, c0, cur, wmax);
+        if (t + 4 < c1) loadA(t + 4, rb);
+        computeA(t, c0, ra, wmax);
+        t += 4;
+        if (t >= c1) break;
+        if (t + 4 < c1) loadA(t + 4, ra);
+        computeA(t, c0, rb, wmax);
         t += 4;
       }
     }
@@ -526,13 +599,16 @@ __global__ __launch_bounds__(256, 2) void k_decode(
 #pragma unroll
     for (int hh = 0; hh < HPL; ++hh) mh[hh] = (h0 + hh < G) ? m_s[h0 + hh] : 0.f;
     {
-      BRegs cur, nxt;
-      int64_t t = c0 + w;
-      if (t < c1) loadB(t, nxt);
+      BRegs ra, rb;
+      int32_t t = c0 + w;
+      if (t < c1) loadB(t, ra);
       while (t < c1) {
-        cur = nxt;
-        if (t + 4 < c1) loadB(t + 4, nxt);
-        computeB(t, c0, cur, mh);
+        if (t + 4 < c1) loadB(t + 4, rb);
+        computeB(t, c0, ra, mh);
+        t += 4;
+        if (t >= c1) break;
+        if (t + 4 < c1) loadB(t + 4, ra);
+        computeB(t, c0, rb, mh);
         t += 4;
       }
     }
@@ -686,7 +762,7 @@ size_t decode_ws_bytes(int64_t n_inst, int H, int n_q_heads, int n_split, int64_
 
 size_t decode_lds_bytes(int G, int NG, int64_t n_refs) {
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
-  return (size_t)(3 * G * (nrp + 8) + G * kChunkTiles * kDecTile + G * 128 + 96) * 4 +
+  return (size_t)(3 * G * (nrp + 8) + G * (kChunkTiles * kDecTile + kLgPad) + G * 128 + 96) * 4 +
          (size_t)(4 * 16 + 4 * NG) * kDecTile * 2;
 }
 
@@ -702,7 +778,7 @@ bool decode_fits(int G, int group, int64_t n_refs, int n_split) {
          combine_lds_bytes(G, n_refs, n_split) <= 160 * 1024;
 }
 
-template <typename T, int BITS, int NG, int KM>
+template <typename T, int BITS, int NG, int KM, bool EX>
 hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
                            const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
                            const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
@@ -717,7 +793,7 @@ hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = decode_lds_bytes(G, NG, n_refs);
-  auto kern = k_decode<T, BITS, NG, KM>;
+  auto kern = k_decode<T, BITS, NG, KM, EX>;
   if (lds > 64 * 1024) {
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -744,11 +820,12 @@ hipError_t launch_decode_k(int k, const void* q, int n_q_heads, const uint16_t* 
                            const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
                            int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
                            hipStream_t st) {
-  if (k <= 4)
-    return launch_decode_t<T, BITS, NG, 4>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
-  if (k <= 8)
-    return launch_decode_t<T, BITS, NG, 8>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
-  return launch_decode_t<T, BITS, NG, 16>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
+  if (k == 4) return launch_decode_t<T, BITS, NG, 4, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
+  if (k == 8) return launch_decode_t<T, BITS, NG, 8, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
+  if (k == 16) return launch_decode_t<T, BITS, NG, 16, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
+  if (k < 4) return launch_decode_t<T, BITS, NG, 4, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
+  if (k < 8) return launch_decode_t<T, BITS, NG, 8, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
+  return launch_decode_t<T, BITS, NG, 16, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
 }
 
 template <typename T, int BITS>
