@@ -246,6 +246,7 @@ def main():
     alg = algorithmic(cfg, bits, n_refs, count_le)
 
     dec = None
+    dec_sparse = None
     if cfg.decode:
         layer0 = cache.slice(0, cfg.batch)
         q0 = q[: cfg.batch].contiguous()
@@ -258,6 +259,27 @@ def main():
                                                         ws=ws_l),
                             max(a.kernel_reps, 10), flush_between=True)
         gbps = alg["decode_layer_bytes"] / dmean / 1e9
+        # block-sparse selective decode of the same layer: 30 % of each KV
+        # head's 32-position tiles (seeded random choice)
+        n_tiles = (N + 31) // 32
+        n_sel = max(1, round(0.3 * n_tiles))
+        g = torch.Generator(device="cpu")
+        g.manual_seed(30)
+        sel = torch.stack([torch.randperm(n_tiles, generator=g)[:n_sel]
+                           for _ in range(cfg.batch * H)]).to(torch.int32)
+        tiles = sel.view(cfg.batch, H, n_sel).contiguous().to(dev)
+        smed, smean = timed(lambda: rkv.rkv_decode_attn_tiles(q0, cfg.n_q_heads, layer0, scale,
+                                                              tiles, out=out_l, n_split=ns_layer,
+                                                              ws=ws_l),
+                            max(a.kernel_reps, 10), flush_between=True)
+        rec_b = _record_bytes(cfg, bits)
+        sp_bytes = (cfg.batch * H * (n_sel * 32 * rec_b + n_refs * 2 * D * (2 if cfg.dtype == "bf16" else 4))
+                    + cfg.batch * cfg.n_q_heads * D * 6)
+        dec_sparse = {"us_per_layer": smean * 1e6, "GBps": sp_bytes / smean / 1e9,
+                      "frac_peak": sp_bytes / smean / 1e9 / HBM_PEAK_GBPS, "tiles_selected": n_sel,
+                      "tiles_total": n_tiles, "bytes_per_layer": sp_bytes,
+                      "speedup_vs_dense": dmean / smean,
+                      "note": "rkv_decode_attn_tiles: 30 % of the 32-position tiles per KV head"}
         dec = {"us_per_layer": dmean * 1e6, "GBps": gbps, "frac_peak": gbps / HBM_PEAK_GBPS,
                "bytes_per_layer": alg["decode_layer_bytes"], "n_split": ns_layer,
                "traffic_k_decode": measured_traffic("k_decode", cfg.name),
@@ -325,6 +347,7 @@ def main():
         },
         "positions_per_s": value / (cfg.n_layers * H),
         "decode_attn": dec,
+        "decode_attn_sparse": dec_sparse,
         "kernels": kernels,
         "roofline": roof,
     }

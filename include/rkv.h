@@ -175,6 +175,24 @@ rkv_status rkv_decode_attn(const void *q, int32_t n_q_heads,
                            float *out, int32_t n_split, void *ws,
                            size_t ws_bytes, void *stream);
 
+/* Selective decompression under a block-sparse attention mask (paper page,
+ * section "Training and Inference Integration": only the KV pairs that the
+ * sparse attention mask needs are rebuilt; news page, section "Performance
+ * Results": about 30% of the attention computation).  Same as
+ * rkv_decode_attn, but each (instance, KV head) attends only to the
+ * positions of its selected 32-position tiles:
+ *   tiles  int32 device [inst][H][n_tiles], tile indices t (positions
+ *          32t .. 32t+31, those >= seq_len excluded), distinct; an entry
+ *          outside [0, ceil(seq_len/32)) selects nothing.  The order is
+ *          free.  Every query head of a KV head uses its KV head's list.
+ * The reference rows (QK table, W . Vref) are read as in rkv_decode_attn;
+ * only the selected tiles' records are streamed.  Workspace as for
+ * rkv_decode_attn.  RKV_ERR_INVALID_ARG if n_tiles < 1 or tiles is NULL. */
+rkv_status rkv_decode_attn_tiles(const void *q, int32_t n_q_heads, const rkv_cache *c,
+                                 float softmax_scale, const int32_t *tiles, int32_t n_tiles,
+                                 float *out, int32_t n_split, void *ws, size_t ws_bytes,
+                                 void *stream);
+
 const char *rkv_status_string(rkv_status s);
 int32_t rkv_last_hip_error(void);
 int32_t rkv_version(void);

@@ -217,3 +217,27 @@ def rkv_decode_attn(q, n_q_heads: int, cache: Cache, softmax_scale: float, out=N
                                   _ptr(out), int(n_split), _ptr(ws), ws.numel(),
                                   _stream(stream)), "rkv_decode_attn")
     return out
+
+
+def rkv_decode_attn_tiles(q, n_q_heads: int, cache: Cache, softmax_scale: float, tiles,
+                          out=None, n_split: int = 1, ws=None, stream=None):
+    """Decode attention over the selected 32-position tiles only; `tiles` is an
+    int32 device tensor [n_inst, n_kv_heads, n_tiles]."""
+    c = cache.c
+    if q.dtype != cache.torch_dtype or not q.is_cuda or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous {cache.torch_dtype} device tensor")
+    if q.numel() != c.n_inst * n_q_heads * c.head_dim:
+        raise ValueError("q must hold n_inst * n_q_heads * head_dim elements")
+    if (tiles.dtype != torch.int32 or not tiles.is_cuda or not tiles.is_contiguous()
+            or tiles.dim() != 3 or tiles.shape[0] != c.n_inst or tiles.shape[1] != c.n_kv_heads):
+        raise ValueError("tiles must be a contiguous int32 device tensor [n_inst, n_kv_heads, n]")
+    if out is None:
+        out = torch.empty((c.n_inst, n_q_heads, c.head_dim), dtype=torch.float32,
+                          device=q.device)
+    nb = rkv_decode_workspace(cache, n_q_heads, n_split)
+    ws = _ws(nb, q.device, ws)
+    _check(_load().rkv_decode_attn_tiles(_ptr(q), int(n_q_heads), C.byref(c),
+                                        float(softmax_scale), _ptr(tiles), int(tiles.shape[2]),
+                                        _ptr(out), int(n_split), _ptr(ws), ws.numel(),
+                                        _stream(stream)), "rkv_decode_attn_tiles")
+    return out

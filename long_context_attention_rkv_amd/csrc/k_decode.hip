@@ -206,7 +206,8 @@ __global__ __launch_bounds__(256, 2) void k_decode(
     const T* __restrict__ q, const T* __restrict__ ref_kv, const uint16_t* __restrict__ idx,
     const uint8_t* __restrict__ codes_k, const uint8_t* __restrict__ codes_v,
     const uint16_t* __restrict__ scales, const float* __restrict__ qk, float* __restrict__ part,
-    float alpha, int64_t N, int64_t n_refs, Sched sc, int k, int G, int H, int n_split) {
+    float alpha, int64_t N, int64_t n_refs, Sched sc, int k, int G, int H, int n_split,
+    const int32_t* __restrict__ tile_list, int32_t n_list) {
   constexpr int HPL = 4 / NG;  // query heads per lane in the score layout
   constexpr int GS = 128 / NG;  // dims per scale group
   constexpr int CT = kChunkTiles * kDecTile;  // tokens per chunk
@@ -240,9 +241,20 @@ __global__ __launch_bounds__(256, 2) void k_decode(
   const int64_t ih = inst * H + kvh;
   const int Hq = H * G;
   const int32_t tiles = (int32_t)((N + kDecTile - 1) / kDecTile);
-  const int32_t tps = (tiles + n_split - 1) / n_split;
+  // The splits walk entries [0, n_ent) of the tile list (all tiles when there
+  // is no list); entry e names tile tile_of(e).
+  const int32_t* tl = tile_list ? tile_list + ih * n_list : nullptr;
+  const int32_t n_ent = tl ? n_list : tiles;
+  // an entry outside [0, tiles) reads as the empty tile `tiles` (all of its
+  // positions are >= N: masked, nothing loaded)
+  auto tile_of = [&](int32_t e) -> int32_t {
+    if (!tl) return e;
+    const int32_t x = tl[e];
+    return (x >= 0 && x < tiles) ? x : tiles;
+  };
+  const int32_t tps = (n_ent + n_split - 1) / n_split;
   const int32_t t0 = split * tps;
-  const int32_t t1 = (t0 + tps < tiles) ? t0 + tps : tiles;
+  const int32_t t1 = (t0 + tps < n_ent) ? t0 + tps : n_ent;
   const int32_t N32 = (int32_t)N;
   const T* qh = q + (inst * Hq + kvh * G) * 128;
 
@@ -317,7 +329,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(
     uint32_t iw[2][KM / 2];
   };
   auto loadA = [&](int32_t t, ARegs& r) {
-    const int32_t tb = t * kDecTile;
+    const int32_t tb = tile_of(t) * kDecTile;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int32_t tok = tb + 16 * b + n;
@@ -336,7 +348,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(
     }
   };
   auto computeA = [&](int32_t t, int32_t c0, const ARegs& r, float (&wmax)[HPL]) {
-    const int32_t tb = t * kDecTile;
+    const int32_t tb = tile_of(t) * kDecTile;
     const TileRefs tr = tile_refs(tb, N32, sc);
     const bool ftile = EX && tr.cb >= KM;  // wave-uniform
 #pragma unroll
@@ -361,7 +373,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(
       pos_info(tok, tr, sc, k, slot, keff);
       if (!valid) { slot = -1; keff = 0; }
       const float inv_keff = keff > 0 ? 1.0f / (float)keff : 0.f;
-      const int u = tok - c0 * kDecTile;
+      const int u = (t - c0) * kDecTile + 16 * b + n;
 #pragma unroll
       for (int hh = 0; hh < HPL; ++hh) {
         const int h = h0 + hh;
@@ -412,12 +424,16 @@ __global__ __launch_bounds__(256, 2) void k_decode(
     }
   };
   auto loadB = [&](int32_t t, BRegs& r) {
-    const int32_t tb = t * kDecTile;
-    const uint8_t* cvt = cv + (uint32_t)t * (128 * 4 * BITS);
+    const int32_t tb = tile_of(t) * kDecTile;
+    const bool tvalid = tb < N32;
+    const uint8_t* cvt = cv + (uint32_t)(tvalid ? tile_of(t) : 0) * (128 * 4 * BITS);
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
       const uint8_t* pp = cvt + 16 * blk * (4 * BITS);
-      if constexpr (BITS == 8) {
+      if (!tvalid) {
+        r.vw[blk][0] = 0;
+        if constexpr (BITS == 8) r.vw[blk][1] = 0;
+      } else if constexpr (BITS == 8) {
         const uint2 v = *reinterpret_cast<const uint2*>(pp);
         r.vw[blk][0] = v.x;
         r.vw[blk][1] = v.y;
@@ -442,7 +458,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(
     }
   };
   auto computeB = [&](int32_t t, int32_t c0, const BRegs& r, const float (&mh)[HPL]) {
-    const int32_t tb = t * kDecTile;
+    const int32_t tb = tile_of(t) * kDecTile;
     const TileRefs tr = tile_refs(tb, N32, sc);
     const bool ftile = EX && tr.cb >= KM;  // wave-uniform
     float psum[HPL];
@@ -458,7 +474,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(
       if (!valid) { slot = -1; keff = 0; }
       const int u = 16 * b + n;
       const int pos = 8 * (u >> 3) + invperm_of<BITS>(u & 7);
-      const int uc = tok - c0 * kDecTile;
+      const int uc = (t - c0) * kDecTile + u;
 #pragma unroll
       for (int hh = 0; hh < HPL; ++hh) {
         const int h = h0 + hh;
@@ -783,7 +799,7 @@ hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
                            const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
                            const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
                            int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc, int k,
-                           hipStream_t st) {
+                           const int32_t* tile_list, int32_t n_list, hipStream_t st) {
   const int G = n_q_heads / H;
   float* qk = (float*)ws;
   float* part = (float*)((char*)ws + qk_bytes(n_inst, n_q_heads, n_refs));
@@ -800,7 +816,7 @@ hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
   }
   hipLaunchKernelGGL(kern, dim3(n_split, H, (unsigned)n_inst), dim3(256), lds, st, (const T*)q,
                      (const T*)ref_kv, idx, ck, cv, sc16, qk, part, alpha, N, n_refs, sc, k, G, H,
-                     n_split);
+                     n_split, tile_list, n_list);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t clds = combine_lds_bytes(G, n_refs, n_split);
@@ -818,27 +834,27 @@ template <typename T, int BITS, int NG>
 hipError_t launch_decode_k(int k, const void* q, int n_q_heads, const uint16_t* idx,
                            const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
                            const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
-                           int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
-                           hipStream_t st) {
-  if (k == 4) return launch_decode_t<T, BITS, NG, 4, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
-  if (k == 8) return launch_decode_t<T, BITS, NG, 8, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
-  if (k == 16) return launch_decode_t<T, BITS, NG, 16, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
-  if (k < 4) return launch_decode_t<T, BITS, NG, 4, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
-  if (k < 8) return launch_decode_t<T, BITS, NG, 8, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
-  return launch_decode_t<T, BITS, NG, 16, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, st);
+                           int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc, const int32_t* tile_list,
+                           int32_t n_list, hipStream_t st) {
+  if (k == 4) return launch_decode_t<T, BITS, NG, 4, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, tile_list, n_list, st);
+  if (k == 8) return launch_decode_t<T, BITS, NG, 8, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, tile_list, n_list, st);
+  if (k == 16) return launch_decode_t<T, BITS, NG, 16, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, tile_list, n_list, st);
+  if (k < 4) return launch_decode_t<T, BITS, NG, 4, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, tile_list, n_list, st);
+  if (k < 8) return launch_decode_t<T, BITS, NG, 8, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, tile_list, n_list, st);
+  return launch_decode_t<T, BITS, NG, 16, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, tile_list, n_list, st);
 }
 
 template <typename T, int BITS>
 hipError_t launch_decode_g(int group, int k, const void* q, int n_q_heads, const uint16_t* idx,
                            const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
                            const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
-                           int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
-                           hipStream_t st) {
+                           int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc, const int32_t* tile_list,
+                           int32_t n_list, hipStream_t st) {
   if (group == 32)
-    return launch_decode_k<T, BITS, 4>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, st);
+    return launch_decode_k<T, BITS, 4>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, tile_list, n_list, st);
   if (group == 64)
-    return launch_decode_k<T, BITS, 2>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, st);
-  return launch_decode_k<T, BITS, 1>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, st);
+    return launch_decode_k<T, BITS, 2>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, tile_list, n_list, st);
+  return launch_decode_k<T, BITS, 1>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, tile_list, n_list, st);
 }
 
 template <typename T>
@@ -846,22 +862,24 @@ hipError_t launch_decode_b(int bits, int group, int k, const void* q, int n_q_he
                            const uint16_t* idx, const void* ref_kv, const uint8_t* ck,
                            const uint8_t* cv, const uint16_t* sc16, float alpha, float* out,
                            int n_split, void* ws, int64_t n_inst, int H, int64_t N,
-                           int64_t n_refs, Sched sc, hipStream_t st) {
+                           int64_t n_refs, Sched sc, const int32_t* tile_list,
+                           int32_t n_list, hipStream_t st) {
   if (bits == 2)
-    return launch_decode_g<T, 2>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, st);
+    return launch_decode_g<T, 2>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, tile_list, n_list, st);
   if (bits == 4)
-    return launch_decode_g<T, 4>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, st);
-  return launch_decode_g<T, 8>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, st);
+    return launch_decode_g<T, 4>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, tile_list, n_list, st);
+  return launch_decode_g<T, 8>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, tile_list, n_list, st);
 }
 
 hipError_t launch_decode(int dtype, int bits, const void* q, int n_q_heads, const uint16_t* idx,
                          const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
                          const uint16_t* sc16, float softmax_scale, float* out, int n_split,
                          void* ws, int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
-                         int k, int group, hipStream_t st) {
+                         int k, int group, const int32_t* tile_list, int32_t n_list,
+                         hipStream_t st) {
   if (dtype == 0)
-    return launch_decode_b<float>(bits, group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, n_refs, sc, st);
-  return launch_decode_b<__bf16>(bits, group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, n_refs, sc, st);
+    return launch_decode_b<float>(bits, group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, n_refs, sc, tile_list, n_list, st);
+  return launch_decode_b<__bf16>(bits, group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, n_refs, sc, tile_list, n_list, st);
 }
 
 }  // namespace rkv

@@ -26,7 +26,8 @@ hipError_t launch_decode(int dtype, int bits, const void* q, int n_q_heads, cons
                          const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
                          const uint16_t* sc16, float softmax_scale, float* out, int n_split,
                          void* ws, int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
-                         int k, int group, hipStream_t st);
+                         int k, int group, const int32_t* tile_list, int32_t n_list,
+                         hipStream_t st);
 size_t decode_ws_bytes(int64_t n_inst, int H, int n_q_heads, int n_split, int64_t n_refs);
 bool decode_fits(int G, int group, int64_t n_refs, int n_split);
 }  // namespace rkv
@@ -218,9 +219,10 @@ rkv_status rkv_decode_workspace(const rkv_cache* c, int32_t n_q_heads, int32_t n
   return RKV_OK;
 }
 
-rkv_status rkv_decode_attn(const void* q, int32_t n_q_heads, const rkv_cache* c,
-                           float softmax_scale, float* out, int32_t n_split, void* ws,
-                           size_t ws_bytes, void* stream) {
+static rkv_status decode_common(const void* q, int32_t n_q_heads, const rkv_cache* c,
+                                float softmax_scale, float* out, const int32_t* tiles,
+                                int32_t n_tiles, int32_t n_split, void* ws, size_t ws_bytes,
+                                void* stream) {
   rkv_status s = check_ready(c);
   if (s != RKV_OK) return s;
   if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0 || n_split < 1 || n_split > 4096)
@@ -237,9 +239,26 @@ rkv_status rkv_decode_attn(const void* q, int32_t n_q_heads, const rkv_cache* c,
   hipError_t e = rkv::launch_decode((int)c->dtype, c->bits, q, n_q_heads, c->ref_idx, c->ref_kv,
                                     c->codes_k, c->codes_v, c->scales, softmax_scale, out,
                                     n_split, ws, c->n_inst, c->n_kv_heads, c->seq_len,
-                                    c->n_refs, to_sched(c->stride), c->k, c->group,
-                                    (hipStream_t)stream);
+                                    c->n_refs, to_sched(c->stride), c->k, c->group, tiles,
+                                    n_tiles, (hipStream_t)stream);
   return hip_status(e);
+}
+
+rkv_status rkv_decode_attn(const void* q, int32_t n_q_heads, const rkv_cache* c,
+                           float softmax_scale, float* out, int32_t n_split, void* ws,
+                           size_t ws_bytes, void* stream) {
+  return decode_common(q, n_q_heads, c, softmax_scale, out, nullptr, 0, n_split, ws, ws_bytes,
+                       stream);
+}
+
+rkv_status rkv_decode_attn_tiles(const void* q, int32_t n_q_heads, const rkv_cache* c,
+                                 float softmax_scale, const int32_t* tiles, int32_t n_tiles,
+                                 float* out, int32_t n_split, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  if (n_tiles < 0 || (n_tiles > 0 && !tiles)) return RKV_ERR_INVALID_ARG;
+  if (n_tiles == 0) return RKV_ERR_INVALID_ARG;  // attention over no position is undefined
+  return decode_common(q, n_q_heads, c, softmax_scale, out, tiles, n_tiles, n_split, ws,
+                       ws_bytes, stream);
 }
 
 const char* rkv_status_string(rkv_status s) {

@@ -299,3 +299,21 @@ def decode_attn(q, k_hat, v_hat, scale):
         p = w / w.sum()
         out[h] = p @ v_hat[h // grp]
     return out
+
+
+# ---------------------------------------------------------------------------
+# Selective decompression ([P1] "Training and Inference Integration": only
+# the KV pairs the sparse attention mask needs are rebuilt)
+# ---------------------------------------------------------------------------
+
+def tile_positions(tiles, n: int, tile: int = 32) -> np.ndarray:
+    """Sorted positions covered by a block-sparse selection: tile t covers
+    positions [t*tile, (t+1)*tile) below n; entries outside
+    [0, ceil(n/tile)) select nothing.  Attention under the selection is
+    decode_attn over k_hat[:, positions], v_hat[:, positions]."""
+    n_tiles = -(-n // tile)
+    pos = []
+    for t in sorted(set(int(x) for x in tiles)):
+        if 0 <= t < n_tiles:
+            pos.extend(range(t * tile, min((t + 1) * tile, n)))
+    return np.array(pos, dtype=np.int64)

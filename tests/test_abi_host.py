@@ -144,6 +144,15 @@ def test_entry_points_validate_before_touching_the_device(lib):
     out = C.c_void_p(0x5000)
     assert lib.rkv_decode_attn(C.c_void_p(0x6000), 32, C.byref(c), 0.1, out, 4,
                                C.c_void_p(0x7000), ws.value - 1, null) == L.RKV_ERR_WORKSPACE
+    # block-sparse decode: a tile list is required, and must not be empty
+    assert lib.rkv_decode_attn_tiles(C.c_void_p(0x6000), 32, C.byref(c), 0.1, null, 4, out, 4,
+                                     C.c_void_p(0x7000), ws.value, null) == L.RKV_ERR_INVALID_ARG
+    assert lib.rkv_decode_attn_tiles(C.c_void_p(0x6000), 32, C.byref(c), 0.1,
+                                     C.c_void_p(0x8000), 0, out, 4, C.c_void_p(0x7000),
+                                     ws.value, null) == L.RKV_ERR_INVALID_ARG
+    assert lib.rkv_decode_attn_tiles(C.c_void_p(0x6000), 32, C.byref(c), 0.1,
+                                     C.c_void_p(0x8000), 4, out, 4, C.c_void_p(0x7000),
+                                     ws.value - 1, null) == L.RKV_ERR_WORKSPACE
     c.bits = 0
     assert lib.rkv_decode_attn(C.c_void_p(0x6000), 32, C.byref(c), 0.1, out, 4,
                                C.c_void_p(0x7000), ws.value, null) == L.RKV_ERR_UNSUPPORTED

@@ -227,6 +227,82 @@ def test_decode_split_invariance():
         assert rel_l2(o, outs[0]) <= 2 * 2.0 ** -11
 
 
+# ------------------------------------------------------------------ selective decode
+
+TILE_CASES = [
+    ("tiny_30pct", get_config(0), 8, 1, 1024, 0.3),
+    ("llama_ragged_30pct", _cfg(1, n_kv_heads=2, n_q_heads=8), 4, 2, 1000, 0.3),
+    ("gqa7_int2_half", _cfg(4, n_kv_heads=2, n_q_heads=14, batch=1), 2, 1, 500, 0.5),
+    ("llama_one_tile", _cfg(1, n_kv_heads=2, n_q_heads=8), 4, 1, 640, 0.0),
+]
+
+
+def _tile_lists(n_inst, H, N, frac, seed):
+    """Random distinct tiles per (instance, KV head) in shuffled order, the
+    ragged last tile forced into one list, plus two entries that select
+    nothing (-1 and one past the end)."""
+    rng = np.random.default_rng(seed)
+    n_tiles = -(-N // 32)
+    n_sel = max(1, int(round(frac * n_tiles)))
+    lists = np.empty((n_inst, H, n_sel + 2), dtype=np.int32)
+    for i in range(n_inst):
+        for h in range(H):
+            sel = rng.choice(n_tiles, n_sel, replace=False)
+            if i == 0 and h == 0:
+                sel[0] = n_tiles - 1 if (n_tiles - 1) not in sel[1:] else sel[0]
+            row = np.concatenate([sel, [-1, n_tiles + 3]])
+            rng.shuffle(row)
+            lists[i, h] = row
+    return lists
+
+
+@pytest.mark.parametrize("case", TILE_CASES, ids=[c[0] for c in TILE_CASES])
+def test_decode_tiles_parity(case):
+    _need_gpu()
+    name, cfg, bits, n_inst, N, frac = case
+    say(f"[decode tiles] {name}: N={N} frac={frac}")
+    K, V = make_kv(cfg, n_inst, N)
+    q = make_q(cfg, n_inst)
+    cache = encode(cfg, K, V, bits, n_inst, N)
+    lists = _tile_lists(n_inst, cfg.n_kv_heads, N, frac, seed=11)
+    tiles = torch.from_numpy(lists).cuda()
+    Kn, Vn, qn = to_np_f32(K), to_np_f32(V), to_np_f32(q)
+    G = cfg.n_q_heads // cfg.n_kv_heads
+    for scale in (1.0 / math.sqrt(cfg.head_dim), 1.0):
+        got = rkv.rkv_decode_attn_tiles(q, cfg.n_q_heads, cache, scale, tiles, n_split=3)
+        torch.cuda.synchronize()
+        got = got.cpu().numpy()
+        want = np.zeros_like(got, dtype=np.float64)
+        for i in range(n_inst):
+            for h in range(cfg.n_kv_heads):
+                enc = oracle.encode(Kn[i, h], Vn[i, h], cfg.stride_base, cfg.double_after,
+                                    cfg.k, bits, cfg.group)
+                kv = oracle.reconstruct(enc, Kn[i, h], Vn[i, h], bits)
+                pos = oracle.tile_positions(lists[i, h], N)
+                want[i, h * G:(h + 1) * G] = oracle.decode_attn(
+                    qn[i, h * G:(h + 1) * G], kv[None, pos, 0], kv[None, pos, 1], scale)
+        err = rel_l2(got, want)
+        say(f"  scale={scale:.4f} rel L2 = {err:.2e}")
+        assert err <= 2e-3
+
+
+def test_decode_all_tiles_equals_dense():
+    _need_gpu()
+    cfg = _cfg(1, n_kv_heads=2, n_q_heads=8)
+    say("[decode tiles] all tiles == dense")
+    N = 1500
+    K, V = make_kv(cfg, 2, N)
+    q = make_q(cfg, 2)
+    cache = encode(cfg, K, V, 4, 2, N)
+    n_tiles = -(-N // 32)
+    tiles = torch.arange(n_tiles, dtype=torch.int32, device="cuda").expand(2, 2, n_tiles).contiguous()
+    dense = rkv.rkv_decode_attn(q, 8, cache, 1.0, n_split=5).cpu().numpy()
+    sparse = rkv.rkv_decode_attn_tiles(q, 8, cache, 1.0, tiles, n_split=5).cpu().numpy()
+    # identical streams; only the float-atomic merge of the four waves may
+    # add in another order
+    assert rel_l2(sparse, dense) <= 1e-6
+
+
 # ------------------------------------------------------------------ full sizes
 # The workloads at their real per-instance shapes, in the launch
 # configuration the benchmark times; the oracle checks sampled tokens.

@@ -362,3 +362,11 @@ def test_decode_dominant_key_selects_its_value():
     vh = np.arange(40, dtype=np.float64).reshape(1, 10, 4)
     out = oracle.decode_attn(np.array([[1.0, 0, 0, 0]]), kh, vh, 1.0)
     np.testing.assert_allclose(out[0], vh[0, 6], atol=1e-15)
+
+
+def test_tile_positions_golden():
+    # n = 70: three tiles, the last one ragged (64..69); -1 and 9 select nothing
+    got = oracle.tile_positions([2, -1, 0, 9], 70)
+    assert got.tolist() == list(range(0, 32)) + list(range(64, 70))
+    assert oracle.tile_positions([1], 32).tolist() == []
+    assert oracle.tile_positions(range(3), 70).tolist() == list(range(70))
