@@ -240,6 +240,17 @@ def main():
     sel_med, sel_mean = timed(lambda: rkv.rkv_select_refs(K, V, cache, ws=ws_enc), a.kernel_reps)
     qz_med, qz_mean = timed(lambda: rkv.rkv_quantize(K, V, cache), a.kernel_reps)
 
+    # streaming encode: one new position for every (layer, sequence, KV head),
+    # appended at the last position of the (already encoded) cache
+    K_last = K[:, :, N - 1:N].contiguous()
+    V_last = V[:, :, N - 1:N].contiguous()
+    ap_med, ap_mean = timed(lambda: rkv.rkv_append(K_last, V_last, cache, N - 1, ws_enc),
+                            max(a.kernel_reps, 10))
+    stream_append = {"us_per_call": ap_mean * 1e6, "head_tokens_per_call": n_inst * H,
+                     "head_tokens_per_s": n_inst * H / ap_mean,
+                     "note": "rkv_append of one position for all layers x sequences x KV heads "
+                             "(distance/top-k against the 512 references + quantise)"}
+
     T = np.array([rkv.rkv_ref_position(s, cfg.stride_base, cfg.double_after)
                   for s in range(n_refs)], dtype=np.int64)
     count_le = np.searchsorted(T, np.arange(N), side="right")
@@ -348,6 +359,7 @@ def main():
         "positions_per_s": value / (cfg.n_layers * H),
         "decode_attn": dec,
         "decode_attn_sparse": dec_sparse,
+        "stream_append": stream_append,
         "kernels": kernels,
         "roofline": roof,
     }

@@ -131,6 +131,22 @@ rkv_status rkv_encode_workspace(const rkv_cache *c, size_t *bytes);
 rkv_status rkv_encode(const void *K, const void *V, const rkv_cache *c,
                       void *ws, size_t ws_bytes, void *stream);
 
+/* Streaming encode (decode-time append; the references are historical
+ * tokens, paper page section "DeltaKV Framework Architecture"): encodes the
+ * n_new positions pos0 .. pos0+n_new-1 from their rows only,
+ *   K_new, V_new  dtype [inst][H][n_new][D]  (device),
+ * writing their ref_idx rows, codes, scales and, for reference positions,
+ * their ref_kv rows.  The result is bit-identical to rkv_encode over the
+ * whole sequence: a position's candidates are the references at or before
+ * it, so positions before pos0 must already be encoded -- by rkv_encode or
+ * earlier rkv_append calls -- with this same workspace `ws`, which carries
+ * the reference keys and norms from call to call (rkv_encode_workspace
+ * bytes).  Positions from pos0 + n_new on are not touched; codes of other
+ * positions sharing a 32-position V tile keep their bits.
+ * RKV_ERR_INVALID_ARG unless 0 <= pos0 and pos0 + n_new <= seq_len, n_new >= 1. */
+rkv_status rkv_append(const void *K_new, const void *V_new, int64_t n_new, const rkv_cache *c,
+                      int64_t pos0, void *ws, size_t ws_bytes, void *stream);
+
 /* Reference selection ("Batch L2 distance" search of the paper page):
  * writes ref_kv, and ref_idx as the k_eff references with the smallest
  * squared L2 distance between bf16-rounded keys (ties: lower slot), found
@@ -174,6 +190,13 @@ rkv_status rkv_decode_attn(const void *q, int32_t n_q_heads,
                            const rkv_cache *c, float softmax_scale,
                            float *out, int32_t n_split, void *ws,
                            size_t ws_bytes, void *stream);
+
+/* rkv_decode_attn over the first `length` positions only (1 <= length <=
+ * seq_len), for a cache filled up to there by rkv_append: positions and
+ * references beyond are never read.  RKV_ERR_INVALID_ARG for another length. */
+rkv_status rkv_decode_attn_len(const void *q, int32_t n_q_heads, const rkv_cache *c,
+                               int64_t length, float softmax_scale, float *out, int32_t n_split,
+                               void *ws, size_t ws_bytes, void *stream);
 
 /* Selective decompression under a block-sparse attention mask (paper page,
  * section "Training and Inference Integration": only the KV pairs that the

@@ -95,7 +95,9 @@ class Cache:
         self.buffers = {}
         if allocate:
             for name in self.BUFFERS:
-                t = torch.empty(max(1, self.sizes[name]), dtype=torch.uint8, device=device)
+                # cleared once: positions a streaming cache has not reached
+                # (and the V-tile bits past seq_len) read as zero
+                t = torch.zeros(max(1, self.sizes[name]), dtype=torch.uint8, device=device)
                 self.buffers[name] = t
                 setattr(s, name, t.data_ptr() if self.sizes[name] else None)
 
@@ -171,6 +173,25 @@ def rkv_encode(K, V, cache: Cache, ws=None, stream=None):
     return ws
 
 
+def rkv_append(K_new, V_new, cache: Cache, pos0: int, ws, stream=None):
+    """Encode positions pos0 .. pos0 + n_new - 1 from K_new/V_new
+    [n_inst, n_kv_heads, n_new, head_dim]; `ws` is the encode workspace that
+    earlier rkv_encode/rkv_append calls on this cache used (it carries the
+    reference keys)."""
+    c = cache.c
+    for name, t in (("K_new", K_new), ("V_new", V_new)):
+        if t.dtype != cache.torch_dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {cache.torch_dtype} device tensor")
+        if t.dim() != 4 or tuple(t.shape[:2]) != (c.n_inst, c.n_kv_heads) or t.shape[3] != c.head_dim:
+            raise ValueError(f"{name} must be [n_inst, n_kv_heads, n_new, head_dim]")
+    if K_new.shape != V_new.shape:
+        raise ValueError("K_new and V_new differ in shape")
+    if ws is None or ws.numel() < rkv_encode_workspace(cache):
+        raise ValueError("rkv_append needs the encode workspace of the earlier calls")
+    _check(_load().rkv_append(_ptr(K_new), _ptr(V_new), int(K_new.shape[2]), C.byref(c),
+                             int(pos0), _ptr(ws), ws.numel(), _stream(stream)), "rkv_append")
+
+
 def rkv_select_refs(K, V, cache: Cache, ws=None, stream=None):
     _check_kv(K, V, cache)
     nb = rkv_encode_workspace(cache)
@@ -216,6 +237,25 @@ def rkv_decode_attn(q, n_q_heads: int, cache: Cache, softmax_scale: float, out=N
     _check(_load().rkv_decode_attn(_ptr(q), int(n_q_heads), C.byref(c), float(softmax_scale),
                                   _ptr(out), int(n_split), _ptr(ws), ws.numel(),
                                   _stream(stream)), "rkv_decode_attn")
+    return out
+
+
+def rkv_decode_attn_len(q, n_q_heads: int, cache: Cache, length: int, softmax_scale: float,
+                        out=None, n_split: int = 1, ws=None, stream=None):
+    """Decode attention over positions 0 .. length - 1."""
+    c = cache.c
+    if q.dtype != cache.torch_dtype or not q.is_cuda or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous {cache.torch_dtype} device tensor")
+    if q.numel() != c.n_inst * n_q_heads * c.head_dim:
+        raise ValueError("q must hold n_inst * n_q_heads * head_dim elements")
+    if out is None:
+        out = torch.empty((c.n_inst, n_q_heads, c.head_dim), dtype=torch.float32,
+                          device=q.device)
+    nb = rkv_decode_workspace(cache, n_q_heads, n_split)
+    ws = _ws(nb, q.device, ws)
+    _check(_load().rkv_decode_attn_len(_ptr(q), int(n_q_heads), C.byref(c), int(length),
+                                      float(softmax_scale), _ptr(out), int(n_split), _ptr(ws),
+                                      ws.numel(), _stream(stream)), "rkv_decode_attn_len")
     return out
 
 

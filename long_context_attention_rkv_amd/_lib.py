@@ -62,6 +62,11 @@ SIGNATURES = {
     "rkv_decode_attn_tiles": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(RkvCache), C.c_float,
                                         C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
                                         C.c_void_p, C.c_size_t, C.c_void_p]),
+    "rkv_append": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.POINTER(RkvCache), C.c_int64,
+                             C.c_void_p, C.c_size_t, C.c_void_p]),
+    "rkv_decode_attn_len": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(RkvCache), C.c_int64,
+                                      C.c_float, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
+                                      C.c_void_p]),
     "rkv_status_string": (C.c_char_p, [C.c_int]),
     "rkv_last_hip_error": (C.c_int32, []),
     "rkv_version": (C.c_int32, []),

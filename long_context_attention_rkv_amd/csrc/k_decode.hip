@@ -137,11 +137,12 @@ __host__ __device__ inline int64_t part_rec_floats(int64_t n_refs) {
 // QK[inst][hq][slot] = q_hq . Kref_slot in fp32; one thread per reference,
 // whole row loaded before the dot products.  Rows of the table are padded to
 // a multiple of 4 (nrp) with zeros.
+// Rows from n_valid on (references not written yet) are zero.
 template <typename T>
 __global__ __launch_bounds__(256) void k_qk_table(const T* __restrict__ q,
                                                   const T* __restrict__ ref_kv,
                                                   float* __restrict__ qk, int G, int H,
-                                                  int64_t n_refs) {
+                                                  int64_t n_refs, int64_t n_valid) {
   __shared__ float qs[16 * 128];
   const int kvh = blockIdx.y;
   const int64_t inst = blockIdx.z;
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(256) void k_qk_table(const T* __restrict__ q,
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (j >= nrp) return;
   float* out = qk + (inst * Hq + kvh * G) * nrp + j;
-  if (j >= n_refs) {
+  if (j >= n_valid) {
     for (int h = 0; h < G; ++h) out[h * nrp] = 0.f;
     return;
   }
@@ -206,8 +207,9 @@ __global__ __launch_bounds__(256, 2) void k_decode(
     const T* __restrict__ q, const T* __restrict__ ref_kv, const uint16_t* __restrict__ idx,
     const uint8_t* __restrict__ codes_k, const uint8_t* __restrict__ codes_v,
     const uint16_t* __restrict__ scales, const float* __restrict__ qk, float* __restrict__ part,
-    float alpha, int64_t N, int64_t n_refs, Sched sc, int k, int G, int H, int n_split,
-    const int32_t* __restrict__ tile_list, int32_t n_list) {
+    float alpha, int64_t N, int64_t Nlen, int64_t n_refs, Sched sc, int k, int G, int H,
+    int n_split, const int32_t* __restrict__ tile_list, int32_t n_list) {
+  // N: positions the cache holds (layout); Nlen <= N: positions attended
   constexpr int HPL = 4 / NG;  // query heads per lane in the score layout
   constexpr int GS = 128 / NG;  // dims per scale group
   constexpr int CT = kChunkTiles * kDecTile;  // tokens per chunk
@@ -240,22 +242,23 @@ __global__ __launch_bounds__(256, 2) void k_decode(
   const int64_t inst = blockIdx.z;
   const int64_t ih = inst * H + kvh;
   const int Hq = H * G;
-  const int32_t tiles = (int32_t)((N + kDecTile - 1) / kDecTile);
-  // The splits walk entries [0, n_ent) of the tile list (all tiles when there
-  // is no list); entry e names tile tile_of(e).
+  const int32_t tiles = (int32_t)((N + kDecTile - 1) / kDecTile);       // layout
+  const int32_t tiles_len = (int32_t)((Nlen + kDecTile - 1) / kDecTile);
+  // The splits walk entries [0, n_ent) of the tile list (all tiles below
+  // Nlen when there is no list); entry e names tile tile_of(e).
   const int32_t* tl = tile_list ? tile_list + ih * n_list : nullptr;
-  const int32_t n_ent = tl ? n_list : tiles;
-  // an entry outside [0, tiles) reads as the empty tile `tiles` (all of its
-  // positions are >= N: masked, nothing loaded)
+  const int32_t n_ent = tl ? n_list : tiles_len;
+  // an entry outside [0, tiles_len) reads as the empty tile `tiles_len` (all
+  // of its positions are >= Nlen: masked, nothing loaded)
   auto tile_of = [&](int32_t e) -> int32_t {
     if (!tl) return e;
     const int32_t x = tl[e];
-    return (x >= 0 && x < tiles) ? x : tiles;
+    return (x >= 0 && x < tiles_len) ? x : tiles_len;
   };
   const int32_t tps = (n_ent + n_split - 1) / n_split;
   const int32_t t0 = split * tps;
   const int32_t t1 = (t0 + tps < n_ent) ? t0 + tps : n_ent;
-  const int32_t N32 = (int32_t)N;
+  const int32_t N32 = (int32_t)Nlen;  // masking bound
   const T* qh = q + (inst * Hq + kvh * G) * 128;
 
   // ---- prologue: QK table into LDS, clears
@@ -666,11 +669,12 @@ __global__ __launch_bounds__(256, 2) void k_decode(
 // G query heads, then add W . Vref for the chunk's dims.
 constexpr int kCombChunks = 4;
 
+// W . Vref runs over the n_valid written references only.
 template <typename T>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
                                                  const T* __restrict__ ref_kv,
                                                  float* __restrict__ out, int G, int H,
-                                                 int64_t n_refs, int n_split) {
+                                                 int64_t n_refs, int64_t n_valid, int n_split) {
   extern __shared__ float cs[];
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
   float* wt = cs;                   // [G][nrp]
@@ -732,7 +736,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
 #pragma unroll
   for (int h = 0; h < 16; ++h) a[h] = 0.f;
   int64_t j = g;
-  for (; j + 8 * 7 < n_refs; j += 8 * 8) {
+  for (; j + 8 * 7 < n_valid; j += 8 * 8) {
     float v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = (float)vref[(j + 8 * u) * 128];
@@ -743,7 +747,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
         if (h < G) a[h] = __builtin_fmaf(wt[h * nrp + j + 8 * u], v[u], a[h]);
     }
   }
-  for (; j < n_refs; j += 8) {
+  for (; j < n_valid; j += 8) {
     const float v = (float)vref[j * 128];
 #pragma unroll
     for (int h = 0; h < 16; ++h)
@@ -798,14 +802,15 @@ template <typename T, int BITS, int NG, int KM, bool EX>
 hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
                            const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
                            const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
-                           int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc, int k,
+                           int64_t n_inst, int H, int64_t N, int64_t len, int64_t n_refs, Sched sc, int k,
                            const int32_t* tile_list, int32_t n_list, hipStream_t st) {
   const int G = n_q_heads / H;
   float* qk = (float*)ws;
   float* part = (float*)((char*)ws + qk_bytes(n_inst, n_q_heads, n_refs));
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
+  const int64_t n_valid = sched_count((int32_t)len, sc);
   hipLaunchKernelGGL(k_qk_table<T>, dim3((unsigned)((nrp + 255) / 256), H, (unsigned)n_inst),
-                     dim3(256), 0, st, (const T*)q, (const T*)ref_kv, qk, G, H, n_refs);
+                     dim3(256), 0, st, (const T*)q, (const T*)ref_kv, qk, G, H, n_refs, n_valid);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = decode_lds_bytes(G, NG, n_refs);
@@ -815,7 +820,7 @@ hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, dim3(n_split, H, (unsigned)n_inst), dim3(256), lds, st, (const T*)q,
-                     (const T*)ref_kv, idx, ck, cv, sc16, qk, part, alpha, N, n_refs, sc, k, G, H,
+                     (const T*)ref_kv, idx, ck, cv, sc16, qk, part, alpha, N, len, n_refs, sc, k, G, H,
                      n_split, tile_list, n_list);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -826,7 +831,7 @@ hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_combine<T>, dim3(H, (unsigned)n_inst, kCombChunks), dim3(256), clds, st,
-                     part, (const T*)ref_kv, out, G, H, n_refs, n_split);
+                     part, (const T*)ref_kv, out, G, H, n_refs, n_valid, n_split);
   return hipGetLastError();
 }
 
@@ -834,52 +839,51 @@ template <typename T, int BITS, int NG>
 hipError_t launch_decode_k(int k, const void* q, int n_q_heads, const uint16_t* idx,
                            const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
                            const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
-                           int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc, const int32_t* tile_list,
+                           int64_t n_inst, int H, int64_t N, int64_t len, int64_t n_refs, Sched sc, const int32_t* tile_list,
                            int32_t n_list, hipStream_t st) {
-  if (k == 4) return launch_decode_t<T, BITS, NG, 4, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, tile_list, n_list, st);
-  if (k == 8) return launch_decode_t<T, BITS, NG, 8, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, tile_list, n_list, st);
-  if (k == 16) return launch_decode_t<T, BITS, NG, 16, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, tile_list, n_list, st);
-  if (k < 4) return launch_decode_t<T, BITS, NG, 4, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, tile_list, n_list, st);
-  if (k < 8) return launch_decode_t<T, BITS, NG, 8, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, tile_list, n_list, st);
-  return launch_decode_t<T, BITS, NG, 16, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, k, tile_list, n_list, st);
+  if (k == 4) return launch_decode_t<T, BITS, NG, 4, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
+  if (k == 8) return launch_decode_t<T, BITS, NG, 8, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
+  if (k == 16) return launch_decode_t<T, BITS, NG, 16, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
+  if (k < 4) return launch_decode_t<T, BITS, NG, 4, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
+  if (k < 8) return launch_decode_t<T, BITS, NG, 8, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
+  return launch_decode_t<T, BITS, NG, 16, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
 }
 
 template <typename T, int BITS>
 hipError_t launch_decode_g(int group, int k, const void* q, int n_q_heads, const uint16_t* idx,
                            const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
                            const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
-                           int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc, const int32_t* tile_list,
+                           int64_t n_inst, int H, int64_t N, int64_t len, int64_t n_refs, Sched sc, const int32_t* tile_list,
                            int32_t n_list, hipStream_t st) {
   if (group == 32)
-    return launch_decode_k<T, BITS, 4>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, tile_list, n_list, st);
+    return launch_decode_k<T, BITS, 4>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
   if (group == 64)
-    return launch_decode_k<T, BITS, 2>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, tile_list, n_list, st);
-  return launch_decode_k<T, BITS, 1>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, tile_list, n_list, st);
+    return launch_decode_k<T, BITS, 2>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
+  return launch_decode_k<T, BITS, 1>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
 }
 
 template <typename T>
 hipError_t launch_decode_b(int bits, int group, int k, const void* q, int n_q_heads,
                            const uint16_t* idx, const void* ref_kv, const uint8_t* ck,
                            const uint8_t* cv, const uint16_t* sc16, float alpha, float* out,
-                           int n_split, void* ws, int64_t n_inst, int H, int64_t N,
-                           int64_t n_refs, Sched sc, const int32_t* tile_list,
+                           int n_split, void* ws, int64_t n_inst, int H, int64_t N, int64_t len, int64_t n_refs, Sched sc, const int32_t* tile_list,
                            int32_t n_list, hipStream_t st) {
   if (bits == 2)
-    return launch_decode_g<T, 2>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, tile_list, n_list, st);
+    return launch_decode_g<T, 2>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
   if (bits == 4)
-    return launch_decode_g<T, 4>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, tile_list, n_list, st);
-  return launch_decode_g<T, 8>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, n_refs, sc, tile_list, n_list, st);
+    return launch_decode_g<T, 4>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
+  return launch_decode_g<T, 8>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
 }
 
 hipError_t launch_decode(int dtype, int bits, const void* q, int n_q_heads, const uint16_t* idx,
                          const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
                          const uint16_t* sc16, float softmax_scale, float* out, int n_split,
-                         void* ws, int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
+                         void* ws, int64_t n_inst, int H, int64_t N, int64_t len, int64_t n_refs, Sched sc,
                          int k, int group, const int32_t* tile_list, int32_t n_list,
                          hipStream_t st) {
   if (dtype == 0)
-    return launch_decode_b<float>(bits, group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, n_refs, sc, tile_list, n_list, st);
-  return launch_decode_b<__bf16>(bits, group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, n_refs, sc, tile_list, n_list, st);
+    return launch_decode_b<float>(bits, group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
+  return launch_decode_b<__bf16>(bits, group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
 }
 
 }  // namespace rkv

@@ -125,6 +125,42 @@ __device__ inline void store_codes(uint8_t* p, const uint32_t (&c)[8]) {
   }
 }
 
+// The codes of 8 consecutive positions of one transposed V row as one word
+// (BITS bytes), and stores of it: whole, or only the fields of positions
+// lo .. hi-1 (the others keep their bits).
+template <int BITS>
+__device__ inline uint64_t pack_codes8(const int (&c)[8]) {
+  uint64_t w = 0;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) w |= (uint64_t)(c[t] & ((1 << BITS) - 1)) << (BITS * t);
+  return w;
+}
+
+template <int BITS>
+__device__ inline void store_word(uint8_t* p, uint64_t w) {
+  if constexpr (BITS == 8) *reinterpret_cast<uint64_t*>(p) = w;
+  else if constexpr (BITS == 4) *reinterpret_cast<uint32_t*>(p) = (uint32_t)w;
+  else *reinterpret_cast<uint16_t*>(p) = (uint16_t)w;
+}
+
+template <int BITS>
+__device__ inline void store_word_range(uint8_t* p, uint64_t w, int lo, int hi) {
+  const uint64_t full = BITS == 8 ? ~0ull : ((1ull << (8 * BITS)) - 1);
+  const uint64_t below_hi = hi >= 8 ? full : ((1ull << (BITS * hi)) - 1);
+  const uint64_t below_lo = (1ull << (BITS * lo)) - 1;  // lo <= 7 here
+  const uint64_t m = below_hi & ~below_lo;
+  if constexpr (BITS == 8) {
+    uint64_t* q = reinterpret_cast<uint64_t*>(p);
+    *q = (*q & ~m) | (w & m);
+  } else if constexpr (BITS == 4) {
+    uint32_t* q = reinterpret_cast<uint32_t*>(p);
+    *q = (uint32_t)((*q & ~m) | (w & m));
+  } else {
+    uint16_t* q = reinterpret_cast<uint16_t*>(p);
+    *q = (uint16_t)((*q & ~m) | (w & m));
+  }
+}
+
 template <int BITS>
 __device__ inline void store_codes(uint8_t* p, const int (&c)[8]) {
   if constexpr (BITS == 4) {
@@ -287,8 +323,8 @@ struct PosLoads {
 
 template <typename T, int KM>
 __device__ inline void issue_pos_loads(const T* __restrict__ src, const uint16_t* __restrict__ idx_h,
-                                       int tok, PosLoads<T, KM>& p) {
-  load_raw8(src + (uint32_t)tok * 128u, p.x);
+                                       int tok, int row, PosLoads<T, KM>& p) {
+  load_raw8(src + (uint32_t)row * 128u, p.x);
   const uint16_t* irow = idx_h + (uint32_t)tok * KM;
   if constexpr (KM == 4) {
     const uint2 v = *reinterpret_cast<const uint2*>(irow);
@@ -319,23 +355,31 @@ __device__ inline void unpack_slots(const PosLoads<T, KM>& p, uint32_t (&sl)[KM]
 // step ahead and its mean is the unpredicated fast form; otherwise k_eff is
 // taken per position.
 template <typename T, int BITS, int KM>
-__global__ __launch_bounds__(512) void k_quantize(
+__global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
     const T* __restrict__ K, const T* __restrict__ V, const uint16_t* __restrict__ idx,
     const T* __restrict__ ref_kv, uint8_t* __restrict__ codes_k,
     uint8_t* __restrict__ codes_v, uint16_t* __restrict__ scales, int64_t N,
-    int64_t n_refs, Sched sc, int k, int group, int chunk, int H) {
+    int64_t n_refs, Sched sc, int k, int group, int chunk, int H, int p0, int n_in) {
   __shared__ int8_t vt[128][kVTile + 1];  // odd pitch: the 16 writing lanes hit 16 banks
   const int tid = threadIdx.x;
   const int tok_l = tid >> 5;          // position within the step
   const int plane = (tid >> 4) & 1;    // 0 = K, 1 = V
   const int dl = tid & 15;             // dims [8*dl, 8*dl+8)
   const int64_t ih = (int64_t)blockIdx.z * H + blockIdx.y;
-  const int c0 = (int)blockIdx.x * chunk;
-  const int c1 = (int)((c0 + chunk < N) ? c0 + chunk : N);
+  // positions [p0, p1) from input rows [ih][n_in][128]; chunks start on
+  // tile boundaries (no two blocks share a transposed V tile); positions of
+  // a chunk outside [p0, p1) are skipped and keep their codes
+  const int p1 = p0 + n_in;
+  const int c0 = (p0 & ~(kVTile - 1)) + (int)blockIdx.x * chunk;
+  const int c1 = c0 + chunk < p1 ? c0 + chunk : p1;
+  const int v0 = c0 > p0 ? c0 : p0;
   const int n_groups = 128 / group;
   const int lanes_per_group = group >> 3;
   // per-(instance, head) bases; positions below index them with 32-bit offsets
-  const T* src = (plane ? V : K) + ih * N * 128 + 8 * dl;
+  // row of position t: src + t * 128 (the base is offset by -p0 rows; only
+  // positions >= p0 are read)
+  const T* src = (plane ? V : K) + (ih * n_in - p0) * 128 + 8 * dl;
+  const uint32_t vspan = (uint32_t)(c1 - v0);  // t is ours iff (uint32_t)(t - v0) < vspan
   const T* refs = ref_kv + (ih * 2 + plane) * n_refs * 128 + 8 * dl;
   const uint16_t* idx_h = idx + ih * N * k;
   uint8_t* ck_h = codes_k + ih * N * (128 * BITS / 8) + dl * BITS;
@@ -372,8 +416,9 @@ __global__ __launch_bounds__(512) void k_quantize(
   // One step of the fast path: use the loads in `cur`, request the next
   // step's into `nxt`.
   auto fast_step = [&](int tok, PosLoads<T, KM>& cur, PosLoads<T, KM>& nxt, uint32_t (&u)[8]) {
-    if (tok + kQTokens < c1) issue_pos_loads<T, KM>(src, idx_h, tok + kQTokens, nxt);
-    if (tok < c1) {
+    const int tn = tok + kQTokens;
+    if ((uint32_t)(tn - v0) < vspan) issue_pos_loads<T, KM>(src, idx_h, tn, tn, nxt);
+    if ((uint32_t)(tok - v0) < vspan) {
       uint32_t sl[KM];
       unpack_slots<T, KM>(cur, sl);
       float x[8], m[8];
@@ -383,7 +428,7 @@ __global__ __launch_bounds__(512) void k_quantize(
     }
   };
   auto slow_step = [&](int tok, uint32_t (&u)[8]) {
-    if (tok < c1) {
+    if ((uint32_t)(tok - v0) < vspan) {
       float x[8], m[8];
       load8(src + (uint32_t)tok * 128u, x);
       const int keff = min(k, sched_count_le(tok, sc));
@@ -409,16 +454,26 @@ __global__ __launch_bounds__(512) void k_quantize(
 #pragma unroll
       for (int e = 0; e < 8; ++e) cc[e] = vt[dim][8 * uu + e];
       const int64_t tile = tb / kVTile;
-      store_codes<BITS>(codes_v + ((ih * ((N + kVTile - 1) / kVTile) + tile) * 128 + dim) *
-                                      (kVTile * BITS / 8) + uu * BITS,
-                        cc);
+      uint8_t* dst = codes_v + ((ih * ((N + kVTile - 1) / kVTile) + tile) * 128 + dim) *
+                                   (kVTile * BITS / 8) + uu * BITS;
+      const int g0 = tb + 8 * uu;  // positions g0 .. g0+7
+      const uint64_t wv = pack_codes8<BITS>(cc);
+      if (g0 >= v0 && g0 + 8 <= c1) {
+        store_word<BITS>(dst, wv);
+      } else {
+        // a tile cut by the range: only positions v0 .. c1-1 are ours
+        const int lo = v0 - g0 < 0 ? 0 : v0 - g0;
+        const int hi = c1 - g0 > 8 ? 8 : c1 - g0;
+        if (lo < hi) store_word_range<BITS>(dst, wv, lo, hi);
+      }
       __syncthreads();
     }
   };
 
   if (fast) {
     PosLoads<T, KM> pa, pb;
-    if (c0 + tok_l < c1) issue_pos_loads<T, KM>(src, idx_h, c0 + tok_l, pa);
+    if ((uint32_t)(c0 + tok_l - v0) < vspan)
+      issue_pos_loads<T, KM>(src, idx_h, c0 + tok_l, c0 + tok_l, pa);
     for (int tb = c0; tb < c1; tb += kVTile) {
       uint32_t u0[8] = {0, 0, 0, 0, 0, 0, 0, 0}, u1[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       fast_step(tb + tok_l, pa, pb, u0);
@@ -504,14 +559,15 @@ template <typename T, int BITS>
 hipError_t launch_quantize_t(const void* K, const void* V, const uint16_t* idx,
                              const void* ref_kv, uint8_t* ck, uint8_t* cv, uint16_t* sc16,
                              int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
-                             int k, int group, hipStream_t st) {
+                             int k, int group, int64_t p0, int64_t n_in, hipStream_t st) {
   const int chunk = 256;
-  const int64_t nchunks = (N + chunk - 1) / chunk;
+  const int64_t start = p0 & ~(int64_t)(kVTile - 1);
+  const int64_t nchunks = (p0 + n_in - start + chunk - 1) / chunk;
   auto kern = k <= 4 ? k_quantize<T, BITS, 4> : (k <= 8 ? k_quantize<T, BITS, 8>
                                                        : k_quantize<T, BITS, 16>);
   hipLaunchKernelGGL(kern, dim3((unsigned)nchunks, H, (unsigned)n_inst),
                      dim3(512), 0, st, (const T*)K, (const T*)V, idx, (const T*)ref_kv, ck,
-                     cv, sc16, N, n_refs, sc, k, group, chunk, H);
+                     cv, sc16, N, n_refs, sc, k, group, chunk, H, (int)p0, (int)n_in);
   return hipGetLastError();
 }
 
@@ -519,23 +575,24 @@ template <typename T>
 hipError_t launch_quantize_d(int bits, const void* K, const void* V, const uint16_t* idx,
                              const void* ref_kv, uint8_t* ck, uint8_t* cv, uint16_t* sc16,
                              int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
-                             int k, int group, hipStream_t st) {
+                             int k, int group, int64_t p0, int64_t n_in, hipStream_t st) {
   switch (bits) {
-    case 0: return launch_quantize_t<T, 0>(K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, st);
-    case 2: return launch_quantize_t<T, 2>(K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, st);
-    case 4: return launch_quantize_t<T, 4>(K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, st);
-    default: return launch_quantize_t<T, 8>(K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, st);
+    case 0: return launch_quantize_t<T, 0>(K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
+    case 2: return launch_quantize_t<T, 2>(K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
+    case 4: return launch_quantize_t<T, 4>(K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
+    default: return launch_quantize_t<T, 8>(K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
   }
 }
 
 hipError_t launch_quantize(int dtype, int bits, const void* K, const void* V,
                            const uint16_t* idx, const void* ref_kv, uint8_t* ck, uint8_t* cv,
                            uint16_t* sc16, int64_t n_inst, int H, int64_t N, int64_t n_refs,
-                           Sched sc, int k, int group, hipStream_t st) {
-  if (N == 0 || n_inst == 0) return hipSuccess;
+                           Sched sc, int k, int group, int64_t p0, int64_t n_in,
+                           hipStream_t st) {
+  if (n_in == 0 || n_inst == 0) return hipSuccess;
   if (dtype == 0)
-    return launch_quantize_d<float>(bits, K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, st);
-  return launch_quantize_d<__bf16>(bits, K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, st);
+    return launch_quantize_d<float>(bits, K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
+  return launch_quantize_d<__bf16>(bits, K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
 }
 
 template <typename T, int BITS>

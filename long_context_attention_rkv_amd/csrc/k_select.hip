@@ -28,21 +28,23 @@
 namespace rkv {
 
 // ------------------------------------------------------------------ refstore
-// One wave per reference: copies its K and V rows into the cache's reference
-// store, writes the bf16-rounded key and its squared norm to the workspace.
+// One wave per new reference (slots s0 .. s0+ns-1 of every (instance,
+// head), at positions inside the input range that starts at p0): copies its
+// K and V rows into the cache's reference store, writes the bf16-rounded key
+// and its squared norm to the workspace.  Input rows are [ih][n_in][128].
 template <typename T>
 __global__ __launch_bounds__(256) void k_refstore(
     const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ ref_kv,
-    __bf16* __restrict__ refkey, float* __restrict__ refnorm, int64_t N,
-    int64_t n_refs, Sched sc, int64_t total_refs) {
+    __bf16* __restrict__ refkey, float* __restrict__ refnorm, int64_t n_in, int64_t p0,
+    int64_t n_refs, int64_t s0, int64_t ns, Sched sc, int64_t total_refs) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= total_refs) return;
-  const int64_t ih = r / n_refs;
-  const int64_t slot = r - ih * n_refs;
+  const int64_t ih = r / ns;
+  const int64_t slot = s0 + (r - ih * ns);
   const int64_t pos = sched_pos((int32_t)slot, sc);
-  const T* kr = K + (ih * N + pos) * 128;
-  const T* vr = V + (ih * N + pos) * 128;
+  const T* kr = K + (ih * n_in + (pos - p0)) * 128;
+  const T* vr = V + (ih * n_in + (pos - p0)) * 128;
   T* dk = ref_kv + ((ih * 2 + 0) * n_refs + slot) * 128;
   T* dv = ref_kv + ((ih * 2 + 1) * n_refs + slot) * 128;
   const int t = lane * 2;
@@ -52,12 +54,13 @@ __global__ __launch_bounds__(256) void k_refstore(
   dv[t + 1] = vr[t + 1];
   const __bf16 b0 = (__bf16)(float)kr[t];
   const __bf16 b1 = (__bf16)(float)kr[t + 1];
-  refkey[r * 128 + t] = b0;
-  refkey[r * 128 + t + 1] = b1;
+  const int64_t wr = ih * n_refs + slot;
+  refkey[wr * 128 + t] = b0;
+  refkey[wr * 128 + t + 1] = b1;
   double s = (double)(float)b0 * (double)(float)b0 + (double)(float)b1 * (double)(float)b1;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (lane == 0) refnorm[r] = (float)s;
+  if (lane == 0) refnorm[wr] = (float)s;
 }
 
 // ------------------------------------------------------------------ top-k
@@ -222,7 +225,9 @@ template <typename T, int KM>
 __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
     const T* __restrict__ K, const __bf16* __restrict__ refkey,
     const float* __restrict__ refnorm, uint16_t* __restrict__ idx_out, int64_t N,
-    int64_t n_refs, Sched sc, int k, int H, int n_blocks) {
+    int64_t n_refs, Sched sc, int k, int H, int n_blocks, int64_t p0, int64_t n_in) {
+  // positions [p0, p1) from input rows [ih][n_in][128]; idx rows at ih * N + position
+  const int64_t p1 = p0 + n_in;
   constexpr int CAP = surv_cap<KM>();
   __shared__ float sb_e[4][kSets][CAP][64];
   __shared__ uint16_t sb_j[4][kSets][CAP][64];
@@ -233,14 +238,14 @@ __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
   const int w = tid >> 6;
   const int blk = n_blocks - 1 - (int)blockIdx.x;
   const int64_t ih = (int64_t)blockIdx.z * H + blockIdx.y;
-  const int64_t blk0 = (int64_t)blk * kBlockRows;
+  const int64_t blk0 = p0 + (int64_t)blk * kBlockRows;
   const int64_t row0 = blk0 + w * 32 * kSets;
-  const bool active = row0 < N;
+  const bool active = row0 < p1;
   const int n = lane & 31;
   const int half = lane >> 5;
-  const int64_t blk_last = (blk0 + kBlockRows - 1 < N) ? blk0 + kBlockRows - 1 : N - 1;
+  const int64_t blk_last = (blk0 + kBlockRows - 1 < p1) ? blk0 + kBlockRows - 1 : p1 - 1;
   const int ntile_blk = (int)((sched_count_le((int32_t)blk_last, sc) + 31) / 32);
-  const int64_t last_row = (row0 + 32 * kSets - 1 < N) ? row0 + 32 * kSets - 1 : N - 1;
+  const int64_t last_row = (row0 + 32 * kSets - 1 < p1) ? row0 + 32 * kSets - 1 : p1 - 1;
   const int ntile = active ? (int)((sched_count_le((int32_t)last_row, sc) + 31) / 32) : 0;
   const int full_tiles = active ? (int)(sched_count_le((int32_t)row0, sc) / 32) : 0;
   bool valid_row[kSets];
@@ -250,9 +255,9 @@ __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
 #pragma unroll
   for (int c = 0; c < kSets; ++c) {
     const int64_t i = row0 + 32 * c + n;
-    valid_row[c] = i < N;
+    valid_row[c] = i < p1;
     my_last[c] = valid_row[c] ? sched_count_le((int32_t)i, sc) - 1 : -1;
-    const T* krow = K + (ih * N + (valid_row[c] ? i : 0)) * 128 + 8 * half;
+    const T* krow = K + (ih * n_in + (valid_row[c] ? i - p0 : 0)) * 128 + 8 * half;
 #pragma unroll
     for (int s = 0; s < 8; ++s) bfrag[c][s] = load_key_frag(krow + 16 * s, valid_row[c]);
   }
@@ -423,48 +428,51 @@ __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
 
 template <typename T>
 hipError_t launch_refstore_t(const void* K, const void* V, void* ref_kv, void* refkey,
-                             float* refnorm, int64_t n_inst, int H, int64_t N,
+                             float* refnorm, int64_t n_inst, int H, int64_t p0, int64_t n_in,
                              int64_t n_refs, Sched sc, hipStream_t st) {
-  const int64_t total = n_inst * H * n_refs;
+  const int64_t s0 = sched_count((int32_t)p0, sc);
+  const int64_t ns = sched_count((int32_t)(p0 + n_in), sc) - s0;
+  const int64_t total = n_inst * H * ns;
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + 3) / 4;
   hipLaunchKernelGGL(k_refstore<T>, dim3((unsigned)blocks), dim3(256), 0, st,
-                     (const T*)K, (const T*)V, (T*)ref_kv, (__bf16*)refkey, refnorm, N,
-                     n_refs, sc, total);
+                     (const T*)K, (const T*)V, (T*)ref_kv, (__bf16*)refkey, refnorm, n_in, p0,
+                     n_refs, s0, ns, sc, total);
   return hipGetLastError();
 }
 
 hipError_t launch_refstore(int dtype, const void* K, const void* V, void* ref_kv,
                            void* refkey, float* refnorm, int64_t n_inst, int H,
-                           int64_t N, int64_t n_refs, Sched sc, hipStream_t st) {
+                           int64_t p0, int64_t n_in, int64_t n_refs, Sched sc, hipStream_t st) {
   if (dtype == 0)
-    return launch_refstore_t<float>(K, V, ref_kv, refkey, refnorm, n_inst, H, N, n_refs, sc, st);
-  return launch_refstore_t<__bf16>(K, V, ref_kv, refkey, refnorm, n_inst, H, N, n_refs, sc, st);
+    return launch_refstore_t<float>(K, V, ref_kv, refkey, refnorm, n_inst, H, p0, n_in, n_refs, sc, st);
+  return launch_refstore_t<__bf16>(K, V, ref_kv, refkey, refnorm, n_inst, H, p0, n_in, n_refs, sc, st);
 }
 
 template <typename T, int KM>
 hipError_t launch_topk_t(const void* K, const void* refkey, const float* refnorm,
                          uint16_t* idx, int64_t n_inst, int H, int64_t N, int64_t n_refs,
-                         Sched sc, int k, hipStream_t st) {
-  const int n_blocks = (int)((N + kBlockRows - 1) / kBlockRows);
+                         Sched sc, int k, int64_t p0, int64_t n_in, hipStream_t st) {
+  const int n_blocks = (int)((n_in + kBlockRows - 1) / kBlockRows);
   hipLaunchKernelGGL((k_dist_topk<T, KM>), dim3(n_blocks, H, (unsigned)n_inst), dim3(256), 0,
                      st, (const T*)K, (const __bf16*)refkey, refnorm, idx, N, n_refs, sc, k,
-                     H, n_blocks);
+                     H, n_blocks, p0, n_in);
   return hipGetLastError();
 }
 
 hipError_t launch_dist_topk(int dtype, const void* K, const void* refkey,
                             const float* refnorm, uint16_t* idx, int64_t n_inst, int H,
-                            int64_t N, int64_t n_refs, Sched sc, int k, hipStream_t st) {
-  if (N == 0 || n_inst == 0) return hipSuccess;
+                            int64_t N, int64_t n_refs, Sched sc, int k, int64_t p0,
+                            int64_t n_in, hipStream_t st) {
+  if (n_in == 0 || n_inst == 0) return hipSuccess;
   if (dtype == 0) {
-    if (k <= 4) return launch_topk_t<float, 4>(K, refkey, refnorm, idx, n_inst, H, N, n_refs, sc, k, st);
-    if (k <= 8) return launch_topk_t<float, 8>(K, refkey, refnorm, idx, n_inst, H, N, n_refs, sc, k, st);
-    return launch_topk_t<float, 16>(K, refkey, refnorm, idx, n_inst, H, N, n_refs, sc, k, st);
+    if (k <= 4) return launch_topk_t<float, 4>(K, refkey, refnorm, idx, n_inst, H, N, n_refs, sc, k, p0, n_in, st);
+    if (k <= 8) return launch_topk_t<float, 8>(K, refkey, refnorm, idx, n_inst, H, N, n_refs, sc, k, p0, n_in, st);
+    return launch_topk_t<float, 16>(K, refkey, refnorm, idx, n_inst, H, N, n_refs, sc, k, p0, n_in, st);
   }
-  if (k <= 4) return launch_topk_t<__bf16, 4>(K, refkey, refnorm, idx, n_inst, H, N, n_refs, sc, k, st);
-  if (k <= 8) return launch_topk_t<__bf16, 8>(K, refkey, refnorm, idx, n_inst, H, N, n_refs, sc, k, st);
-  return launch_topk_t<__bf16, 16>(K, refkey, refnorm, idx, n_inst, H, N, n_refs, sc, k, st);
+  if (k <= 4) return launch_topk_t<__bf16, 4>(K, refkey, refnorm, idx, n_inst, H, N, n_refs, sc, k, p0, n_in, st);
+  if (k <= 8) return launch_topk_t<__bf16, 8>(K, refkey, refnorm, idx, n_inst, H, N, n_refs, sc, k, p0, n_in, st);
+  return launch_topk_t<__bf16, 16>(K, refkey, refnorm, idx, n_inst, H, N, n_refs, sc, k, p0, n_in, st);
 }
 
 }  // namespace rkv

@@ -8,16 +8,19 @@
 #include "rkv_common.h"
 
 namespace rkv {
+// Encode kernels work on positions [p0, p0 + n_in) whose K/V rows are the
+// input [inst][H][n_in][128]; the cache keeps its full [.][.][N] layout.
 hipError_t launch_refstore(int dtype, const void* K, const void* V, void* ref_kv, void* refkey,
-                           float* refnorm, int64_t n_inst, int H, int64_t N, int64_t n_refs,
-                           Sched sc, hipStream_t st);
+                           float* refnorm, int64_t n_inst, int H, int64_t p0, int64_t n_in,
+                           int64_t n_refs, Sched sc, hipStream_t st);
 hipError_t launch_dist_topk(int dtype, const void* K, const void* refkey, const float* refnorm,
                             uint16_t* idx, int64_t n_inst, int H, int64_t N, int64_t n_refs,
-                            Sched sc, int k, hipStream_t st);
+                            Sched sc, int k, int64_t p0, int64_t n_in, hipStream_t st);
 hipError_t launch_quantize(int dtype, int bits, const void* K, const void* V,
                            const uint16_t* idx, const void* ref_kv, uint8_t* ck, uint8_t* cv,
                            uint16_t* sc16, int64_t n_inst, int H, int64_t N, int64_t n_refs,
-                           Sched sc, int k, int group, hipStream_t st);
+                           Sched sc, int k, int group, int64_t p0, int64_t n_in,
+                           hipStream_t st);
 hipError_t launch_reconstruct(int dtype, int bits, const uint16_t* idx, const void* ref_kv,
                               const uint8_t* ck, const uint8_t* cv, const uint16_t* sc16,
                               float* Kh, float* Vh, int64_t n_inst, int H, int64_t N,
@@ -25,9 +28,9 @@ hipError_t launch_reconstruct(int dtype, int bits, const uint16_t* idx, const vo
 hipError_t launch_decode(int dtype, int bits, const void* q, int n_q_heads, const uint16_t* idx,
                          const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
                          const uint16_t* sc16, float softmax_scale, float* out, int n_split,
-                         void* ws, int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
-                         int k, int group, const int32_t* tile_list, int32_t n_list,
-                         hipStream_t st);
+                         void* ws, int64_t n_inst, int H, int64_t N, int64_t len,
+                         int64_t n_refs, Sched sc, int k, int group, const int32_t* tile_list,
+                         int32_t n_list, hipStream_t st);
 size_t decode_ws_bytes(int64_t n_inst, int H, int n_q_heads, int n_split, int64_t n_refs);
 bool decode_fits(int G, int group, int64_t n_refs, int n_split);
 }  // namespace rkv
@@ -151,25 +154,39 @@ rkv_status rkv_encode_workspace(const rkv_cache* c, size_t* bytes) {
   return RKV_OK;
 }
 
+// Reference store + selection for positions [p0, p0 + n_in).
+static rkv_status select_range(const void* K, const void* V, const rkv_cache* c, int64_t p0,
+                               int64_t n_in, void* ws, size_t ws_bytes, hipStream_t st) {
+  const size_t need = encode_ws(c);
+  if (!ws || ws_bytes < need) return RKV_ERR_WORKSPACE;
+  const size_t nr = (size_t)c->n_inst * c->n_kv_heads * c->n_refs;
+  char* refkey = (char*)ws;
+  float* refnorm = (float*)((char*)ws + align_up(nr * 128 * 2));
+  const Sched sc = to_sched(c->stride);
+  hipError_t e = rkv::launch_refstore((int)c->dtype, K, V, c->ref_kv, refkey, refnorm, c->n_inst,
+                                      c->n_kv_heads, p0, n_in, c->n_refs, sc, st);
+  if (e != hipSuccess) return hip_status(e);
+  e = rkv::launch_dist_topk((int)c->dtype, K, refkey, refnorm, c->ref_idx, c->n_inst,
+                            c->n_kv_heads, c->seq_len, c->n_refs, sc, c->k, p0, n_in, st);
+  return hip_status(e);
+}
+
+static rkv_status quantize_range(const void* K, const void* V, const rkv_cache* c, int64_t p0,
+                                 int64_t n_in, hipStream_t st) {
+  hipError_t e = rkv::launch_quantize((int)c->dtype, c->bits, K, V, c->ref_idx, c->ref_kv,
+                                      c->codes_k, c->codes_v, c->scales, c->n_inst,
+                                      c->n_kv_heads, c->seq_len, c->n_refs,
+                                      to_sched(c->stride), c->k, c->group, p0, n_in, st);
+  return hip_status(e);
+}
+
 rkv_status rkv_select_refs(const void* K, const void* V, const rkv_cache* c, void* ws,
                            size_t ws_bytes, void* stream) {
   rkv_status s = check_ready(c);
   if (s != RKV_OK) return s;
   if (c->n_inst == 0 || c->seq_len == 0) return RKV_OK;
   if (!K || !V) return RKV_ERR_INVALID_ARG;
-  const size_t need = encode_ws(c);
-  if (!ws || ws_bytes < need) return RKV_ERR_WORKSPACE;
-  const size_t nr = (size_t)c->n_inst * c->n_kv_heads * c->n_refs;
-  char* refkey = (char*)ws;
-  float* refnorm = (float*)((char*)ws + align_up(nr * 128 * 2));
-  hipStream_t st = (hipStream_t)stream;
-  const Sched sc = to_sched(c->stride);
-  hipError_t e = rkv::launch_refstore((int)c->dtype, K, V, c->ref_kv, refkey, refnorm, c->n_inst,
-                                      c->n_kv_heads, c->seq_len, c->n_refs, sc, st);
-  if (e != hipSuccess) return hip_status(e);
-  e = rkv::launch_dist_topk((int)c->dtype, K, refkey, refnorm, c->ref_idx, c->n_inst,
-                            c->n_kv_heads, c->seq_len, c->n_refs, sc, c->k, st);
-  return hip_status(e);
+  return select_range(K, V, c, 0, c->seq_len, ws, ws_bytes, (hipStream_t)stream);
 }
 
 rkv_status rkv_quantize(const void* K, const void* V, const rkv_cache* c, void* ws,
@@ -180,11 +197,7 @@ rkv_status rkv_quantize(const void* K, const void* V, const rkv_cache* c, void* 
   if (s != RKV_OK) return s;
   if (c->n_inst == 0 || c->seq_len == 0) return RKV_OK;
   if (!K || !V) return RKV_ERR_INVALID_ARG;
-  hipError_t e = rkv::launch_quantize((int)c->dtype, c->bits, K, V, c->ref_idx, c->ref_kv,
-                                      c->codes_k, c->codes_v, c->scales, c->n_inst,
-                                      c->n_kv_heads, c->seq_len, c->n_refs,
-                                      to_sched(c->stride), c->k, c->group, (hipStream_t)stream);
-  return hip_status(e);
+  return quantize_range(K, V, c, 0, c->seq_len, (hipStream_t)stream);
 }
 
 rkv_status rkv_encode(const void* K, const void* V, const rkv_cache* c, void* ws,
@@ -192,6 +205,19 @@ rkv_status rkv_encode(const void* K, const void* V, const rkv_cache* c, void* ws
   rkv_status s = rkv_select_refs(K, V, c, ws, ws_bytes, stream);
   if (s != RKV_OK) return s;
   return rkv_quantize(K, V, c, ws, ws_bytes, stream);
+}
+
+rkv_status rkv_append(const void* K_new, const void* V_new, int64_t n_new, const rkv_cache* c,
+                      int64_t pos0, void* ws, size_t ws_bytes, void* stream) {
+  rkv_status s = check_ready(c);
+  if (s != RKV_OK) return s;
+  if (n_new < 1 || pos0 < 0 || pos0 + n_new > c->seq_len) return RKV_ERR_INVALID_ARG;
+  if (c->n_inst == 0) return RKV_OK;
+  if (!K_new || !V_new) return RKV_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  s = select_range(K_new, V_new, c, pos0, n_new, ws, ws_bytes, st);
+  if (s != RKV_OK) return s;
+  return quantize_range(K_new, V_new, c, pos0, n_new, st);
 }
 
 rkv_status rkv_reconstruct(const rkv_cache* c, float* K_hat, float* V_hat, void* stream) {
@@ -220,9 +246,10 @@ rkv_status rkv_decode_workspace(const rkv_cache* c, int32_t n_q_heads, int32_t n
 }
 
 static rkv_status decode_common(const void* q, int32_t n_q_heads, const rkv_cache* c,
-                                float softmax_scale, float* out, const int32_t* tiles,
-                                int32_t n_tiles, int32_t n_split, void* ws, size_t ws_bytes,
-                                void* stream) {
+                                int64_t length, float softmax_scale, float* out,
+                                const int32_t* tiles, int32_t n_tiles, int32_t n_split, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (length < 1 || length > c->seq_len) return RKV_ERR_INVALID_ARG;
   rkv_status s = check_ready(c);
   if (s != RKV_OK) return s;
   if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0 || n_split < 1 || n_split > 4096)
@@ -238,7 +265,7 @@ static rkv_status decode_common(const void* q, int32_t n_q_heads, const rkv_cach
   if (!ws || ws_bytes < need) return RKV_ERR_WORKSPACE;
   hipError_t e = rkv::launch_decode((int)c->dtype, c->bits, q, n_q_heads, c->ref_idx, c->ref_kv,
                                     c->codes_k, c->codes_v, c->scales, softmax_scale, out,
-                                    n_split, ws, c->n_inst, c->n_kv_heads, c->seq_len,
+                                    n_split, ws, c->n_inst, c->n_kv_heads, c->seq_len, length,
                                     c->n_refs, to_sched(c->stride), c->k, c->group, tiles,
                                     n_tiles, (hipStream_t)stream);
   return hip_status(e);
@@ -247,8 +274,17 @@ static rkv_status decode_common(const void* q, int32_t n_q_heads, const rkv_cach
 rkv_status rkv_decode_attn(const void* q, int32_t n_q_heads, const rkv_cache* c,
                            float softmax_scale, float* out, int32_t n_split, void* ws,
                            size_t ws_bytes, void* stream) {
-  return decode_common(q, n_q_heads, c, softmax_scale, out, nullptr, 0, n_split, ws, ws_bytes,
-                       stream);
+  if (!c) return RKV_ERR_INVALID_ARG;
+  return decode_common(q, n_q_heads, c, c->seq_len, softmax_scale, out, nullptr, 0, n_split, ws,
+                       ws_bytes, stream);
+}
+
+rkv_status rkv_decode_attn_len(const void* q, int32_t n_q_heads, const rkv_cache* c,
+                               int64_t length, float softmax_scale, float* out, int32_t n_split,
+                               void* ws, size_t ws_bytes, void* stream) {
+  if (!c) return RKV_ERR_INVALID_ARG;
+  return decode_common(q, n_q_heads, c, length, softmax_scale, out, nullptr, 0, n_split, ws,
+                       ws_bytes, stream);
 }
 
 rkv_status rkv_decode_attn_tiles(const void* q, int32_t n_q_heads, const rkv_cache* c,
@@ -257,8 +293,9 @@ rkv_status rkv_decode_attn_tiles(const void* q, int32_t n_q_heads, const rkv_cac
                                  void* stream) {
   if (n_tiles < 0 || (n_tiles > 0 && !tiles)) return RKV_ERR_INVALID_ARG;
   if (n_tiles == 0) return RKV_ERR_INVALID_ARG;  // attention over no position is undefined
-  return decode_common(q, n_q_heads, c, softmax_scale, out, tiles, n_tiles, n_split, ws,
-                       ws_bytes, stream);
+  if (!c) return RKV_ERR_INVALID_ARG;
+  return decode_common(q, n_q_heads, c, c->seq_len, softmax_scale, out, tiles, n_tiles, n_split,
+                       ws, ws_bytes, stream);
 }
 
 const char* rkv_status_string(rkv_status s) {

@@ -144,6 +144,16 @@ def test_entry_points_validate_before_touching_the_device(lib):
     out = C.c_void_p(0x5000)
     assert lib.rkv_decode_attn(C.c_void_p(0x6000), 32, C.byref(c), 0.1, out, 4,
                                C.c_void_p(0x7000), ws.value - 1, null) == L.RKV_ERR_WORKSPACE
+    # streaming encode: the range must lie inside the cache
+    for pos0, n_new in ((-1, 1), (0, 0), (8190, 3), (8192, 1)):
+        assert lib.rkv_append(C.c_void_p(0x2000), C.c_void_p(0x3000), n_new, C.byref(c), pos0,
+                              C.c_void_p(0x4000), 1 << 40, null) == L.RKV_ERR_INVALID_ARG
+    assert lib.rkv_append(C.c_void_p(0x2000), C.c_void_p(0x3000), 1, C.byref(c), 100,
+                          C.c_void_p(0x4000), 16, null) == L.RKV_ERR_WORKSPACE
+    # decode over a prefix: 1 <= length <= seq_len
+    for length in (0, 8193):
+        assert lib.rkv_decode_attn_len(C.c_void_p(0x6000), 32, C.byref(c), length, 0.1, out, 4,
+                                       C.c_void_p(0x7000), ws.value, null) == L.RKV_ERR_INVALID_ARG
     # block-sparse decode: a tile list is required, and must not be empty
     assert lib.rkv_decode_attn_tiles(C.c_void_p(0x6000), 32, C.byref(c), 0.1, null, 4, out, 4,
                                      C.c_void_p(0x7000), ws.value, null) == L.RKV_ERR_INVALID_ARG

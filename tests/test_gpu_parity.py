@@ -303,6 +303,80 @@ def test_decode_all_tiles_equals_dense():
     assert rel_l2(sparse, dense) <= 1e-6
 
 
+# ------------------------------------------------------------------ streaming encode
+
+APPEND_CASES = [
+    # (id, config, bits, n_inst, N, prefill, chunk sizes cycled after it)
+    ("tiny_int8_f32", get_config(0), 8, 1, 1024, 200, (1,)),
+    ("llama_int4_from_zero", _cfg(1, n_kv_heads=2), 4, 1, 700, 0, (1, 7, 33)),
+    ("stress_int2_k16", _cfg(4, n_kv_heads=2, batch=2), 2, 2, 777, 100, (1, 5, 64)),
+    ("dynamic_int4", _cfg(3, n_kv_heads=2, double_after=512, drift_block=128), 4, 1, 1500, 450,
+     (3, 1, 40)),
+    ("bf16_nobits", _cfg(1, n_kv_heads=1), 0, 1, 300, 37, (1, 2)),
+]
+
+
+def _stream_encode(cfg, K, V, bits, n_inst, N, prefill, chunks):
+    cache = rkv.Cache(n_inst, cfg.n_kv_heads, N, cfg.dtype, cfg.stride_base, cfg.k, bits,
+                      cfg.group, double_after=cfg.double_after)
+    ws = torch.empty(rkv.rkv_encode_workspace(cache), dtype=torch.uint8, device="cuda")
+    pos = 0
+    if prefill:
+        rkv.rkv_append(K[:, :, :prefill].contiguous(), V[:, :, :prefill].contiguous(), cache, 0, ws)
+        pos = prefill
+    i = 0
+    while pos < N:
+        n = min(chunks[i % len(chunks)], N - pos)
+        rkv.rkv_append(K[:, :, pos:pos + n].contiguous(), V[:, :, pos:pos + n].contiguous(),
+                       cache, pos, ws)
+        pos += n
+        i += 1
+    torch.cuda.synchronize()
+    return cache
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
+def test_append_equals_batch_encode(case):
+    """Appending positions (prefill, then chunks of a few positions) gives the
+    batch encode byte for byte: same arithmetic, causal candidate sets."""
+    _need_gpu()
+    name, cfg, bits, n_inst, N, prefill, chunks = case
+    say(f"[append] {name}: N={N} prefill={prefill} chunks={chunks}")
+    K, V = make_kv(cfg, n_inst, N)
+    whole = encode(cfg, K, V, bits, n_inst, N)
+    streamed = _stream_encode(cfg, K, V, bits, n_inst, N, prefill, chunks)
+    for buf in rkv.Cache.BUFFERS:
+        if bits == 0 and buf == "scales":
+            continue
+        assert torch.equal(whole.buffers[buf], streamed.buffers[buf]), buf
+
+
+def test_decode_len_reads_only_the_prefix():
+    """A cache of capacity N filled to L by appends, every other byte garbage
+    (NaN patterns included): decode over length L matches the oracle on the
+    first L positions."""
+    _need_gpu()
+    cfg = _cfg(1, n_kv_heads=2, n_q_heads=8)
+    N, L = 1000, 643
+    say(f"[decode len] N={N} L={L}")
+    K, V = make_kv(cfg, 1, N)
+    q = make_q(cfg, 1)
+    cache = rkv.Cache(1, 2, N, cfg.dtype, cfg.stride_base, cfg.k, 4, cfg.group)
+    for buf in rkv.Cache.BUFFERS:
+        cache.buffers[buf].fill_(0xFF)   # fp16/bf16 NaN, slot 65535, code -1
+    ws = torch.empty(rkv.rkv_encode_workspace(cache), dtype=torch.uint8, device="cuda")
+    rkv.rkv_append(K[:, :, :400].contiguous(), V[:, :, :400].contiguous(), cache, 0, ws)
+    rkv.rkv_append(K[:, :, 400:L].contiguous(), V[:, :, 400:L].contiguous(), cache, 400, ws)
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    got = rkv.rkv_decode_attn_len(q, 8, cache, L, scale, n_split=4).cpu().numpy()
+    Kn, Vn, qn = to_np_f32(K[:, :, :L]), to_np_f32(V[:, :, :L]), to_np_f32(q)
+    want = _oracle_decode(cfg, Kn, Vn, qn, 4, scale)
+    err = rel_l2(got, want)
+    say(f"  rel L2 = {err:.2e}")
+    assert np.isfinite(got).all()
+    assert err <= 2e-3
+
+
 # ------------------------------------------------------------------ full sizes
 # The workloads at their real per-instance shapes, in the launch
 # configuration the benchmark times; the oracle checks sampled tokens.
