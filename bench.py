@@ -251,6 +251,32 @@ def main():
                      "note": "rkv_append of one position for all layers x sequences x KV heads "
                              "(distance/top-k against the 512 references + quantise)"}
 
+    # full-pipeline quantisation: the same layer with the reference store in
+    # int4 (storage per head-token, and the layer's encode + decode)
+    fpq = None
+    if cfg.decode:
+        cq = rkv.Cache(cfg.batch, H, N, cfg.dtype, cfg.stride_base, cfg.k, bits, cfg.group,
+                       double_after=cfg.double_after, device=dev, ref_bits=4)
+        Kl, Vl = K[: cfg.batch].contiguous(), V[: cfg.batch].contiguous()
+        ws_q = torch.empty(rkv.rkv_encode_workspace(cq), dtype=torch.uint8, device=dev)
+        em, emean = timed(lambda: rkv.rkv_encode(Kl, Vl, cq, ws=ws_q), a.kernel_reps)
+        ns_q = max(1, min((N + 31) // 32, 512 // (cfg.batch * H)))
+        ws_qd = torch.empty(rkv.rkv_decode_workspace(cq, cfg.n_q_heads, ns_q), dtype=torch.uint8,
+                            device=dev)
+        out_q = torch.empty(cfg.batch, cfg.n_q_heads, D, dtype=torch.float32, device=dev)
+        q0q = q[: cfg.batch].contiguous()
+        dm, dmean_q = timed(lambda: rkv.rkv_decode_attn(q0q, cfg.n_q_heads, cq, scale, out=out_q,
+                                                        n_split=ns_q, ws=ws_qd),
+                            max(a.kernel_reps, 10), flush_between=True)
+        raw = cfg.batch * H * N * 2 * D * (2 if cfg.dtype == "bf16" else 4)
+        lay = cache.slice(0, cfg.batch)
+        fpq = {"bytes_per_head_token": cq.nbytes() / (cfg.batch * H * N),
+               "bytes_per_head_token_raw_refs": lay.nbytes() / (cfg.batch * H * N),
+               "fraction_of_raw": cq.nbytes() / raw,
+               "fraction_of_raw_raw_refs": lay.nbytes() / raw,
+               "encode_layer_ms": emean * 1e3, "decode_layer_us": dmean_q * 1e6,
+               "note": "reference store in int4 + fp16 scales (ref_bits=4); one layer of the workload"}
+
     T = np.array([rkv.rkv_ref_position(s, cfg.stride_base, cfg.double_after)
                   for s in range(n_refs)], dtype=np.int64)
     count_le = np.searchsorted(T, np.arange(N), side="right")
@@ -360,6 +386,7 @@ def main():
         "decode_attn": dec,
         "decode_attn_sparse": dec_sparse,
         "stream_append": stream_append,
+        "full_pipeline_quant": fpq,
         "kernels": kernels,
         "roofline": roof,
     }

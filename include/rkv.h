@@ -106,6 +106,22 @@ typedef struct {
   uint8_t *codes_v;
   uint16_t *scales;
   void *ref_kv;
+  /* Full-pipeline quantisation (paper page, sections "Impact and Future
+   * Directions" and "Improvements for AI systems": 4-bit quantisation applied
+   * to the uncompressed reference tokens too).  ref_bits = 0: ref_kv holds the
+   * raw rows (layout above), ref_scales unused.  ref_bits = 4 (needs
+   * bits > 0): every reference row is quantised like a residual -- per group
+   * of `group` dims an fp16 scale nearest to max|x|/7 and codes nearest to
+   * x/scale, clamped to +-7 -- and
+   *   ref_kv      uint8  [inst][H][2][n_refs][D/2]  two's-complement nibbles,
+   *                                                  dim t in bits [4t, 4t+4)
+   *   ref_scales  uint16 [inst][H][2][n_refs][D/group]  fp16 bit patterns.
+   * Everything downstream then uses the dequantised references: the means
+   * the residuals are taken against, reference positions in reconstruction
+   * and decode, the QK table and W . Vref.  Selection still compares the
+   * original keys. */
+  int32_t ref_bits;
+  uint16_t *ref_scales;
 } rkv_cache;
 
 /* Number of references below seq_len; -1 if the schedule is invalid. */
@@ -120,8 +136,8 @@ int64_t rkv_ref_position(int64_t slot, rkv_stride stride);
 rkv_status rkv_cache_init(rkv_cache *c);
 
 /* Bytes of each cache buffer for the shape in *c (after rkv_cache_init):
- * sizes[0..4] = ref_idx, codes_k, codes_v, scales, ref_kv. */
-rkv_status rkv_cache_sizes(const rkv_cache *c, size_t sizes[5]);
+ * sizes[0..5] = ref_idx, codes_k, codes_v, scales, ref_kv, ref_scales. */
+rkv_status rkv_cache_sizes(const rkv_cache *c, size_t sizes[6]);
 
 /* Workspace bytes for rkv_encode / rkv_select_refs / rkv_quantize. */
 rkv_status rkv_encode_workspace(const rkv_cache *c, size_t *bytes);

@@ -71,10 +71,10 @@ class Cache:
     """A compressed cache: the rkv_cache shape plus torch-owned device
     buffers (ref_idx, codes_k, codes_v, scales, ref_kv) as raw bytes."""
 
-    BUFFERS = ("ref_idx", "codes_k", "codes_v", "scales", "ref_kv")
+    BUFFERS = ("ref_idx", "codes_k", "codes_v", "scales", "ref_kv", "ref_scales")
 
     def __init__(self, n_inst, n_kv_heads, seq_len, dtype, stride_base, k, bits, group,
-                 double_after=0, head_dim=128, device="cuda", allocate=True):
+                 double_after=0, head_dim=128, device="cuda", allocate=True, ref_bits=0):
         self.dtype = dtype
         self.torch_dtype = _DT[dtype][1]
         s = L.RkvCache()
@@ -87,9 +87,10 @@ class Cache:
         s.k = int(k)
         s.bits = int(bits)
         s.group = int(group)
+        s.ref_bits = int(ref_bits)
         _check(_load().rkv_cache_init(C.byref(s)), "rkv_cache_init")
         self.c = s
-        sizes = (C.c_size_t * 5)()
+        sizes = (C.c_size_t * 6)()
         _check(_load().rkv_cache_sizes(C.byref(s), sizes), "rkv_cache_sizes")
         self.sizes = dict(zip(self.BUFFERS, [int(x) for x in sizes]))
         self.buffers = {}

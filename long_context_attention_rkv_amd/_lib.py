@@ -38,6 +38,8 @@ class RkvCache(C.Structure):
         ("codes_v", C.c_void_p),
         ("scales", C.c_void_p),
         ("ref_kv", C.c_void_p),
+        ("ref_bits", C.c_int32),
+        ("ref_scales", C.c_void_p),
     ]
 
 

@@ -141,6 +141,8 @@ __host__ __device__ inline int64_t part_rec_floats(int64_t n_refs) {
 template <typename T>
 __global__ __launch_bounds__(256) void k_qk_table(const T* __restrict__ q,
                                                   const T* __restrict__ ref_kv,
+                                                  const uint16_t* __restrict__ ref_scales,
+                                                  int ref_bits, int group,
                                                   float* __restrict__ qk, int G, int H,
                                                   int64_t n_refs, int64_t n_valid) {
   __shared__ float qs[16 * 128];
@@ -158,14 +160,36 @@ __global__ __launch_bounds__(256) void k_qk_table(const T* __restrict__ q,
     for (int h = 0; h < G; ++h) out[h * nrp] = 0.f;
     return;
   }
-  const T* row = ref_kv + ((inst * H + kvh) * 2 + 0) * n_refs * 128 + j * 128;
   float x[128];
+  if (ref_bits == 4) {
+    // quantised reference: nibbles times the fp16 scale of their group (exact)
+    const int ng = 128 / group;
+    const int64_t r = ((inst * H + kvh) * 2 + 0) * n_refs + j;
+    const uint4* cw = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(ref_kv) + r * 64);
+    const uint16_t* sr = ref_scales + r * ng;
 #pragma unroll
-  for (int t = 0; t < 128; t += 8) {
-    float v[8];
-    load8(row + t, v);
+    for (int c = 0; c < 4; ++c) {
+      const uint4 v = cw[c];
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[t + e] = v[e];
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = 32 * c + 8 * u + e;
+          const float s = half_bits_to_f32(sr[t / group]);
+          x[t] = (float)((int32_t)(w4[u] << (28 - 4 * e)) >> 28) * s;
+        }
+      }
+    }
+  } else {
+    const T* row = ref_kv + ((inst * H + kvh) * 2 + 0) * n_refs * 128 + j * 128;
+#pragma unroll
+    for (int t = 0; t < 128; t += 8) {
+      float v[8];
+      load8(row + t, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[t + e] = v[e];
+    }
   }
   for (int h = 0; h < G; ++h) {
     float acc = 0.f;
@@ -673,6 +697,8 @@ constexpr int kCombChunks = 4;
 template <typename T>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
                                                  const T* __restrict__ ref_kv,
+                                                 const uint16_t* __restrict__ ref_scales,
+                                                 int ref_bits, int group,
                                                  float* __restrict__ out, int G, int H,
                                                  int64_t n_refs, int64_t n_valid, int n_split) {
   extern __shared__ float cs[];
@@ -732,6 +758,18 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
   const int g = tid >> 5;
   const int dim = chunk * 32 + t;
   const T* vref = ref_kv + ((inst * H + kvh) * 2 + 1) * n_refs * 128 + dim;
+  // quantised references: nibble of `dim` in row j, times its group's scale
+  const uint8_t* vq = reinterpret_cast<const uint8_t*>(ref_kv) +
+                      ((inst * H + kvh) * 2 + 1) * n_refs * 64 + (dim >> 1);
+  const int ngq = ref_bits == 4 ? 128 / group : 1;
+  const uint16_t* vs = ref_scales + ((inst * H + kvh) * 2 + 1) * n_refs * ngq + dim / (ref_bits == 4 ? group : 128);
+  auto vref_at = [&](int64_t jj) -> float {
+    if (ref_bits == 4) {
+      const int c = ((int)vq[jj * 64] >> (4 * (dim & 1))) & 0xF;
+      return (float)(c >= 8 ? c - 16 : c) * half_bits_to_f32(vs[jj * ngq]);
+    }
+    return (float)vref[jj * 128];
+  };
   float a[16];
 #pragma unroll
   for (int h = 0; h < 16; ++h) a[h] = 0.f;
@@ -739,7 +777,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
   for (; j + 8 * 7 < n_valid; j += 8 * 8) {
     float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = (float)vref[(j + 8 * u) * 128];
+    for (int u = 0; u < 8; ++u) v[u] = vref_at(j + 8 * u);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
 #pragma unroll
@@ -748,7 +786,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
     }
   }
   for (; j < n_valid; j += 8) {
-    const float v = (float)vref[j * 128];
+    const float v = vref_at(j);
 #pragma unroll
     for (int h = 0; h < 16; ++h)
       if (h < G) a[h] = __builtin_fmaf(wt[h * nrp + j], v, a[h]);
@@ -800,7 +838,8 @@ bool decode_fits(int G, int group, int64_t n_refs, int n_split) {
 
 template <typename T, int BITS, int NG, int KM, bool EX>
 hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
-                           const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
+                           const void* ref_kv, const uint16_t* ref_scales, int ref_bits, int group_r,
+                           const uint8_t* ck, const uint8_t* cv,
                            const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
                            int64_t n_inst, int H, int64_t N, int64_t len, int64_t n_refs, Sched sc, int k,
                            const int32_t* tile_list, int32_t n_list, hipStream_t st) {
@@ -810,7 +849,8 @@ hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
   const int64_t n_valid = sched_count((int32_t)len, sc);
   hipLaunchKernelGGL(k_qk_table<T>, dim3((unsigned)((nrp + 255) / 256), H, (unsigned)n_inst),
-                     dim3(256), 0, st, (const T*)q, (const T*)ref_kv, qk, G, H, n_refs, n_valid);
+                     dim3(256), 0, st, (const T*)q, (const T*)ref_kv, ref_scales, ref_bits,
+                     group_r, qk, G, H, n_refs, n_valid);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = decode_lds_bytes(G, NG, n_refs);
@@ -831,59 +871,64 @@ hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_combine<T>, dim3(H, (unsigned)n_inst, kCombChunks), dim3(256), clds, st,
-                     part, (const T*)ref_kv, out, G, H, n_refs, n_valid, n_split);
+                     part, (const T*)ref_kv, ref_scales, ref_bits, group_r, out, G, H, n_refs,
+                     n_valid, n_split);
   return hipGetLastError();
 }
 
 template <typename T, int BITS, int NG>
 hipError_t launch_decode_k(int k, const void* q, int n_q_heads, const uint16_t* idx,
-                           const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
+                           const void* ref_kv, const uint16_t* ref_scales, int ref_bits, int group_r,
+                           const uint8_t* ck, const uint8_t* cv,
                            const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
                            int64_t n_inst, int H, int64_t N, int64_t len, int64_t n_refs, Sched sc, const int32_t* tile_list,
                            int32_t n_list, hipStream_t st) {
-  if (k == 4) return launch_decode_t<T, BITS, NG, 4, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
-  if (k == 8) return launch_decode_t<T, BITS, NG, 8, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
-  if (k == 16) return launch_decode_t<T, BITS, NG, 16, true>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
-  if (k < 4) return launch_decode_t<T, BITS, NG, 4, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
-  if (k < 8) return launch_decode_t<T, BITS, NG, 8, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
-  return launch_decode_t<T, BITS, NG, 16, false>(q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
+  if (k == 4) return launch_decode_t<T, BITS, NG, 4, true>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
+  if (k == 8) return launch_decode_t<T, BITS, NG, 8, true>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
+  if (k == 16) return launch_decode_t<T, BITS, NG, 16, true>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
+  if (k < 4) return launch_decode_t<T, BITS, NG, 4, false>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
+  if (k < 8) return launch_decode_t<T, BITS, NG, 8, false>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
+  return launch_decode_t<T, BITS, NG, 16, false>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
 }
 
 template <typename T, int BITS>
 hipError_t launch_decode_g(int group, int k, const void* q, int n_q_heads, const uint16_t* idx,
-                           const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
+                           const void* ref_kv, const uint16_t* ref_scales, int ref_bits, int group_r,
+                           const uint8_t* ck, const uint8_t* cv,
                            const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
                            int64_t n_inst, int H, int64_t N, int64_t len, int64_t n_refs, Sched sc, const int32_t* tile_list,
                            int32_t n_list, hipStream_t st) {
   if (group == 32)
-    return launch_decode_k<T, BITS, 4>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
+    return launch_decode_k<T, BITS, 4>(k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
   if (group == 64)
-    return launch_decode_k<T, BITS, 2>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
-  return launch_decode_k<T, BITS, 1>(k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
+    return launch_decode_k<T, BITS, 2>(k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
+  return launch_decode_k<T, BITS, 1>(k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
 }
 
 template <typename T>
 hipError_t launch_decode_b(int bits, int group, int k, const void* q, int n_q_heads,
-                           const uint16_t* idx, const void* ref_kv, const uint8_t* ck,
+                           const uint16_t* idx, const void* ref_kv, const uint16_t* ref_scales,
+                           int ref_bits, int group_r, const uint8_t* ck,
                            const uint8_t* cv, const uint16_t* sc16, float alpha, float* out,
                            int n_split, void* ws, int64_t n_inst, int H, int64_t N, int64_t len, int64_t n_refs, Sched sc, const int32_t* tile_list,
                            int32_t n_list, hipStream_t st) {
   if (bits == 2)
-    return launch_decode_g<T, 2>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
+    return launch_decode_g<T, 2>(group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
   if (bits == 4)
-    return launch_decode_g<T, 4>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
-  return launch_decode_g<T, 8>(group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
+    return launch_decode_g<T, 4>(group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
+  return launch_decode_g<T, 8>(group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
 }
 
 hipError_t launch_decode(int dtype, int bits, const void* q, int n_q_heads, const uint16_t* idx,
-                         const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
+                         const void* ref_kv, const uint16_t* ref_scales, int ref_bits,
+                         const uint8_t* ck, const uint8_t* cv,
                          const uint16_t* sc16, float softmax_scale, float* out, int n_split,
                          void* ws, int64_t n_inst, int H, int64_t N, int64_t len, int64_t n_refs, Sched sc,
                          int k, int group, const int32_t* tile_list, int32_t n_list,
                          hipStream_t st) {
   if (dtype == 0)
-    return launch_decode_b<float>(bits, group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
-  return launch_decode_b<__bf16>(bits, group, k, q, n_q_heads, idx, ref_kv, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
+    return launch_decode_b<float>(bits, group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
+  return launch_decode_b<__bf16>(bits, group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
 }
 
 }  // namespace rkv

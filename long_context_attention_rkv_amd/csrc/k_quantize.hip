@@ -20,87 +20,12 @@
 // are staged in LDS per tile of 32 tokens and stored transposed (for each
 // dim, the tile's 32 codes are one bit string) so decode can feed them to the
 // MFMA that contracts over tokens.
+#include <type_traits>
+
 #include "rkv_common.h"
+#include "rkv_quant.h"
 
 namespace rkv {
-
-// fp16 nearest to a/qmax, ties to even, saturating at 65504.  a >= 0 finite.
-__device__ __noinline__ uint16_t exact_scale_bits_slow(float a, float qmax, float inv_qmax) {
-  if (a == 0.f) return 0;
-  uint16_t b = f32_to_half_bits_rne(a * inv_qmax);
-  if (b >= 0x7C00) b = 0x7BFF;
-  float hv = half_bits_to_f32(b);
-  if (b < 0x7BFF) {
-    const float up = half_bits_to_f32((uint16_t)(b + 1));
-    const float lim = qmax * (0.5f * (hv + up));  // exact
-    if (a > lim || (a == lim && (b & 1))) {
-      ++b;
-      hv = up;
-    }
-  }
-  if (b > 0) {
-    const float dn = half_bits_to_f32((uint16_t)(b - 1));
-    const float lim = qmax * (0.5f * (hv + dn));  // exact
-    if (a < lim || (a == lim && (b & 1))) --b;
-  }
-  return b;
-}
-
-// Same result as exact_scale_bits_slow.  y = a * fl(1/qmax) is within 2 ulp
-// of a/qmax, so its fp16 rounding is the exact one unless the 13 bits below
-// fp16 precision sit within 3 of the half-way pattern 0x1000 (or y is
-// outside the normal fp16 range); only those cases take the exact path.
-__device__ inline uint16_t exact_scale_bits(float a, float qmax, float inv_qmax) {
-  const float y = a * inv_qmax;
-  const int low = (int)(__float_as_uint(y) & 0x1FFFu) - 0x1000;
-  if (y >= 0x1p-14f && y < 65504.f && (low > 3 || low < -3)) return f32_to_half_bits_rne(y);
-  return exact_scale_bits_slow(a, qmax, inv_qmax);
-}
-
-// Integer nearest to z/s (ties to even), clamped to [-qmax, qmax].  s > 0.
-__device__ inline int exact_code(float z, float s, float rs, float qmax, float tol) {
-  const float q = z * rs;
-  float n = __builtin_rintf(q);
-  if (fabsf(q - n) > 0.5f - tol) {
-    // q may sit on the wrong side of a half-integer: decide exactly.
-    const float n0 = n;
-    const float hi = __builtin_fmaf(-(n0 + 0.5f), s, z);
-    const float lo = __builtin_fmaf(-(n0 - 0.5f), s, z);
-    const bool odd = ((int)n0 & 1) != 0;
-    if (hi > 0.f || (hi == 0.f && odd)) n = n0 + 1.f;
-    else if (lo < 0.f || (lo == 0.f && odd)) n = n0 - 1.f;
-  }
-  n = __builtin_amdgcn_fmed3f(n, -qmax, qmax);
-  return (int)n;
-}
-
-// Codes of 8 residuals with scale s (rs ~ 1/s within 1 ulp; rs = 0 when
-// s = 0).  t = fl(z*rs + 1.5*2^23) holds the integer nearest to the exact
-// product z*rs (ties to even) in its low mantissa bits; fma(z, rs, M - t) is
-// that rounding's remainder.  When every remainder is clear of 1/2 by more
-// than the product's error, z*rs and z/s round alike; otherwise the lane
-// decides each code exactly.  Returned as M + code (so the low bits are the
-// two's complement code), clamped to [-qmax, qmax].
-constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
-
-__device__ inline void codes8(const float (&z)[8], float s, float rs, float qmax, float tol,
-                              uint32_t (&u)[8]) {
-  float t[8];
-  float emax = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    t[e] = __builtin_fmaf(z[e], rs, kMagic);
-    const float r = __builtin_fmaf(z[e], rs, kMagic - t[e]);
-    emax = fmaxf(emax, fabsf(r));
-  }
-  if (emax > 0.5f - tol) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = kMagic + (float)exact_code(z[e], s, rs, qmax, tol);
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    u[e] = __float_as_uint(__builtin_amdgcn_fmed3f(t[e], kMagic - qmax, kMagic + qmax));
-}
 
 template <int BITS>
 __device__ inline void store_codes(uint8_t* p, const uint32_t (&c)[8]) {
@@ -267,6 +192,76 @@ __device__ inline void ref_mean8(const T* __restrict__ refs, const uint16_t* __r
   }
 }
 
+// Reference rows of one (instance, head, plane), the 8 dims of this lane:
+// raw rows of T, or (RQ) int4 nibbles + one fp16 scale per group.
+template <typename T, bool RQ>
+struct RefSrc {
+  const T* raw;           // row slot at raw + slot * 128
+  const uint8_t* codes;   // row slot at codes + slot * 64 (4 bytes = 8 nibbles)
+  const uint16_t* sc;     // scale of this lane's group at sc + slot * ng
+  int ng;
+};
+
+// 8 nibbles of a quantised row times its scale: exact fp32 values.
+__device__ inline void dequant8(uint32_t w, uint16_t sb, float (&x)[8]) {
+  const float s = half_bits_to_f32(sb);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)((int32_t)(w << (28 - 4 * e)) >> 28) * s;
+}
+
+template <typename T, bool RQ>
+__device__ inline void ref_row8(const RefSrc<T, RQ>& r, uint32_t slot, float (&x)[8]) {
+  if constexpr (RQ) {
+    dequant8(*reinterpret_cast<const uint32_t*>(r.codes + slot * 64u), r.sc[slot * (uint32_t)r.ng], x);
+  } else {
+    load8(r.raw + slot * 128u, x);
+  }
+}
+
+// Mean of the k_eff selected rows: all loads first, then the fixed
+// ascending-slot fp32 sum and one multiply by 1/k_eff (power of two) or a
+// correctly rounded division.
+template <typename T, int KM, bool RQ>
+__device__ inline void ref_mean8_src(const RefSrc<T, RQ>& src, const uint16_t* __restrict__ irow,
+                                     int k, int keff, float (&m)[8]) {
+  if constexpr (!RQ) {
+    ref_mean8<T, KM>(src.raw, irow, k, keff, m);
+  } else {
+    uint32_t sl[KM];
+    load_slots<KM>(irow, k, sl);
+    uint32_t w[KM];
+    uint16_t sb[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (j < keff) {
+        w[j] = *reinterpret_cast<const uint32_t*>(src.codes + sl[j] * 64u);
+        sb[j] = src.sc[sl[j] * (uint32_t)src.ng];
+      }
+    }
+    float acc[8];
+    dequant8(w[0], sb[0], acc);
+#pragma unroll
+    for (int j = 1; j < KM; ++j) {
+      if (j < keff) {
+        float r[8];
+        dequant8(w[j], sb[j], r);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + r[e];
+      }
+    }
+    if (is_pow2(keff)) {
+      const float inv = __uint_as_float((uint32_t)(127 - __builtin_ctz(keff)) << 23);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m[e] = acc[e] * inv;
+    } else {
+      const float kf = (float)keff;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m[e] = acc[e] / kf;
+    }
+  }
+}
+
+
 constexpr int kQTokens = 16;   // tokens per step (512 threads)
 constexpr int kVTile = 32;     // tokens per transposed V tile
 
@@ -293,20 +288,38 @@ __device__ inline void load_slots_full(const uint16_t* __restrict__ irow, uint32
 
 // Mean of exactly KM selected rows (8 dims each): fixed ascending-slot fp32
 // sum, then one multiply by 1/KM (a power of two, exact) or a division.
-template <typename T, int KM>
-__device__ inline void ref_mean8_full(const T* __restrict__ refs, const uint32_t (&sl)[KM],
+template <typename T, int KM, bool RQ>
+__device__ inline void ref_mean8_full(const RefSrc<T, RQ>& src, const uint32_t (&sl)[KM],
                                       float (&m)[8]) {
-  Raw8<T> raw[KM];
-#pragma unroll
-  for (int j = 0; j < KM; ++j) load_raw8(refs + sl[j] * 128u, raw[j]);
   float acc[8];
-  widen8(raw[0], acc);
+  if constexpr (RQ) {
+    uint32_t w[KM];
+    uint16_t sb[KM];
 #pragma unroll
-  for (int j = 1; j < KM; ++j) {
-    float r[8];
-    widen8(raw[j], r);
+    for (int j = 0; j < KM; ++j) {
+      w[j] = *reinterpret_cast<const uint32_t*>(src.codes + sl[j] * 64u);
+      sb[j] = src.sc[sl[j] * (uint32_t)src.ng];
+    }
+    dequant8(w[0], sb[0], acc);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = acc[e] + r[e];
+    for (int j = 1; j < KM; ++j) {
+      float r[8];
+      dequant8(w[j], sb[j], r);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + r[e];
+    }
+  } else {
+    Raw8<T> raw[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) load_raw8(src.raw + sl[j] * 128u, raw[j]);
+    widen8(raw[0], acc);
+#pragma unroll
+    for (int j = 1; j < KM; ++j) {
+      float r[8];
+      widen8(raw[j], r);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + r[e];
+    }
   }
   constexpr float inv = 1.0f / KM;  // KM is 4, 8 or 16: exact
 #pragma unroll
@@ -354,10 +367,11 @@ __device__ inline void unpack_slots(const PosLoads<T, KM>& p, uint32_t (&sl)[KM]
 // the first chunks of a sequence) a position's row and slots are loaded one
 // step ahead and its mean is the unpredicated fast form; otherwise k_eff is
 // taken per position.
-template <typename T, int BITS, int KM>
+template <typename T, int BITS, int KM, bool RQ>
 __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
     const T* __restrict__ K, const T* __restrict__ V, const uint16_t* __restrict__ idx,
-    const T* __restrict__ ref_kv, uint8_t* __restrict__ codes_k,
+    const T* __restrict__ ref_kv, const uint16_t* __restrict__ ref_scales,
+    uint8_t* __restrict__ codes_k,
     uint8_t* __restrict__ codes_v, uint16_t* __restrict__ scales, int64_t N,
     int64_t n_refs, Sched sc, int k, int group, int chunk, int H, int p0, int n_in) {
   __shared__ int8_t vt[128][kVTile + 1];  // odd pitch: the 16 writing lanes hit 16 banks
@@ -380,7 +394,14 @@ __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
   // positions >= p0 are read)
   const T* src = (plane ? V : K) + (ih * n_in - p0) * 128 + 8 * dl;
   const uint32_t vspan = (uint32_t)(c1 - v0);  // t is ours iff (uint32_t)(t - v0) < vspan
-  const T* refs = ref_kv + (ih * 2 + plane) * n_refs * 128 + 8 * dl;
+  RefSrc<T, RQ> refs;
+  refs.ng = n_groups;
+  if constexpr (RQ) {
+    refs.codes = reinterpret_cast<const uint8_t*>(ref_kv) + (ih * 2 + plane) * n_refs * 64 + 4 * dl;
+    refs.sc = ref_scales + (ih * 2 + plane) * n_refs * n_groups + (8 * dl) / group;
+  } else {
+    refs.raw = ref_kv + (ih * 2 + plane) * n_refs * 128 + 8 * dl;
+  }
   const uint16_t* idx_h = idx + ih * N * k;
   uint8_t* ck_h = codes_k + ih * N * (128 * BITS / 8) + dl * BITS;
   uint16_t* sc_h = scales + ih * N * 2 * n_groups + plane * n_groups + dl / lanes_per_group;
@@ -422,7 +443,7 @@ __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
       uint32_t sl[KM];
       unpack_slots<T, KM>(cur, sl);
       float x[8], m[8];
-      ref_mean8_full<T, KM>(refs, sl, m);
+      ref_mean8_full<T, KM, RQ>(refs, sl, m);
       widen8(cur.x, x);
       finish(tok, x, m, u);
     }
@@ -432,7 +453,7 @@ __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
       float x[8], m[8];
       load8(src + (uint32_t)tok * 128u, x);
       const int keff = min(k, sched_count_le(tok, sc));
-      ref_mean8<T, KM>(refs, idx_h + (uint32_t)tok * k, k, keff, m);
+      ref_mean8_src<T, KM, RQ>(refs, idx_h + (uint32_t)tok * k, k, keff, m);
       finish(tok, x, m, u);
     }
   };
@@ -503,9 +524,10 @@ __device__ inline int code_at(const uint8_t* row, int t) {
   return v >= (1 << (BITS - 1)) ? v - (1 << BITS) : v;
 }
 
-template <typename T, int BITS, int KM>
+template <typename T, int BITS, int KM, bool RQ>
 __global__ __launch_bounds__(512) void k_reconstruct(
     const uint16_t* __restrict__ idx, const T* __restrict__ ref_kv,
+    const uint16_t* __restrict__ ref_scales,
     const uint8_t* __restrict__ codes_k, const uint8_t* __restrict__ codes_v,
     const uint16_t* __restrict__ scales, float* __restrict__ Kh, float* __restrict__ Vh,
     int64_t N, int64_t n_refs, Sched sc, int k, int group, int H) {
@@ -515,18 +537,25 @@ __global__ __launch_bounds__(512) void k_reconstruct(
   const int64_t ih = (int64_t)blockIdx.z * H + blockIdx.y;
   const int64_t tok = (int64_t)blockIdx.x * kQTokens + (tid >> 5);
   if (tok >= N) return;
-  const T* refs = ref_kv + (ih * 2 + plane) * n_refs * 128 + 8 * dl;
+  RefSrc<T, RQ> refs;
+  refs.ng = 128 / group;
+  if constexpr (RQ) {
+    refs.codes = reinterpret_cast<const uint8_t*>(ref_kv) + (ih * 2 + plane) * n_refs * 64 + 4 * dl;
+    refs.sc = ref_scales + (ih * 2 + plane) * n_refs * refs.ng + (8 * dl) / group;
+  } else {
+    refs.raw = ref_kv + (ih * 2 + plane) * n_refs * 128 + 8 * dl;
+  }
   float* dst = (plane ? Vh : Kh) + (ih * N + tok) * 128 + 8 * dl;
   float out[8];
   const int64_t slot = sched_slot((int32_t)tok, sc);
   if (slot >= 0) {
-    load8(refs + slot * 128, out);
+    ref_row8<T, RQ>(refs, (uint32_t)slot, out);
     store8(dst, out);
     return;
   }
   float m[8];
   const int keff = (int)min((int64_t)k, sched_count_le((int32_t)tok, sc));
-  ref_mean8<T, KM>(refs, idx + (ih * N + tok) * k, k, keff, m);
+  ref_mean8_src<T, KM, RQ>(refs, idx + (ih * N + tok) * k, k, keff, m);
   if constexpr (BITS == 0) {
     const double* r = reinterpret_cast<const double*>(plane ? codes_v : codes_k) +
                       (ih * N + tok) * 128 + 8 * dl;
@@ -557,79 +586,92 @@ __global__ __launch_bounds__(512) void k_reconstruct(
 // ------------------------------------------------------------ launchers
 template <typename T, int BITS>
 hipError_t launch_quantize_t(const void* K, const void* V, const uint16_t* idx,
-                             const void* ref_kv, uint8_t* ck, uint8_t* cv, uint16_t* sc16,
+                             const void* ref_kv, const uint16_t* ref_scales, int ref_bits,
+                             uint8_t* ck, uint8_t* cv, uint16_t* sc16,
                              int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
                              int k, int group, int64_t p0, int64_t n_in, hipStream_t st) {
   const int chunk = 256;
   const int64_t start = p0 & ~(int64_t)(kVTile - 1);
   const int64_t nchunks = (p0 + n_in - start + chunk - 1) / chunk;
-  auto kern = k <= 4 ? k_quantize<T, BITS, 4> : (k <= 8 ? k_quantize<T, BITS, 8>
-                                                       : k_quantize<T, BITS, 16>);
+  auto pick = [&](auto rq) {
+    constexpr bool R = decltype(rq)::value;
+    return k <= 4 ? k_quantize<T, BITS, 4, R>
+                  : (k <= 8 ? k_quantize<T, BITS, 8, R> : k_quantize<T, BITS, 16, R>);
+  };
+  auto kern = ref_bits == 4 ? pick(std::true_type{}) : pick(std::false_type{});
   hipLaunchKernelGGL(kern, dim3((unsigned)nchunks, H, (unsigned)n_inst),
-                     dim3(512), 0, st, (const T*)K, (const T*)V, idx, (const T*)ref_kv, ck,
+                     dim3(512), 0, st, (const T*)K, (const T*)V, idx, (const T*)ref_kv, ref_scales, ck,
                      cv, sc16, N, n_refs, sc, k, group, chunk, H, (int)p0, (int)n_in);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_quantize_d(int bits, const void* K, const void* V, const uint16_t* idx,
-                             const void* ref_kv, uint8_t* ck, uint8_t* cv, uint16_t* sc16,
+                             const void* ref_kv, const uint16_t* ref_scales, int ref_bits,
+                             uint8_t* ck, uint8_t* cv, uint16_t* sc16,
                              int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
                              int k, int group, int64_t p0, int64_t n_in, hipStream_t st) {
   switch (bits) {
-    case 0: return launch_quantize_t<T, 0>(K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
-    case 2: return launch_quantize_t<T, 2>(K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
-    case 4: return launch_quantize_t<T, 4>(K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
-    default: return launch_quantize_t<T, 8>(K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
+    case 0: return launch_quantize_t<T, 0>(K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
+    case 2: return launch_quantize_t<T, 2>(K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
+    case 4: return launch_quantize_t<T, 4>(K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
+    default: return launch_quantize_t<T, 8>(K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
   }
 }
 
 hipError_t launch_quantize(int dtype, int bits, const void* K, const void* V,
-                           const uint16_t* idx, const void* ref_kv, uint8_t* ck, uint8_t* cv,
+                           const uint16_t* idx, const void* ref_kv, const uint16_t* ref_scales,
+                           int ref_bits, uint8_t* ck, uint8_t* cv,
                            uint16_t* sc16, int64_t n_inst, int H, int64_t N, int64_t n_refs,
                            Sched sc, int k, int group, int64_t p0, int64_t n_in,
                            hipStream_t st) {
   if (n_in == 0 || n_inst == 0) return hipSuccess;
   if (dtype == 0)
-    return launch_quantize_d<float>(bits, K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
-  return launch_quantize_d<__bf16>(bits, K, V, idx, ref_kv, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
+    return launch_quantize_d<float>(bits, K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
+  return launch_quantize_d<__bf16>(bits, K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
 }
 
 template <typename T, int BITS>
-hipError_t launch_recon_t(const uint16_t* idx, const void* ref_kv, const uint8_t* ck,
+hipError_t launch_recon_t(const uint16_t* idx, const void* ref_kv, const uint16_t* ref_scales,
+                          int ref_bits, const uint8_t* ck,
                           const uint8_t* cv, const uint16_t* sc16, float* Kh, float* Vh,
                           int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc, int k,
                           int group, hipStream_t st) {
   const int64_t blocks = (N + kQTokens - 1) / kQTokens;
-  auto kern = k <= 4 ? k_reconstruct<T, BITS, 4>
-                     : (k <= 8 ? k_reconstruct<T, BITS, 8> : k_reconstruct<T, BITS, 16>);
+  auto pick = [&](auto rq) {
+    constexpr bool R = decltype(rq)::value;
+    return k <= 4 ? k_reconstruct<T, BITS, 4, R>
+                  : (k <= 8 ? k_reconstruct<T, BITS, 8, R> : k_reconstruct<T, BITS, 16, R>);
+  };
+  auto kern = ref_bits == 4 ? pick(std::true_type{}) : pick(std::false_type{});
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks, H, (unsigned)n_inst),
-                     dim3(512), 0, st, idx, (const T*)ref_kv, ck, cv, sc16, Kh, Vh, N, n_refs,
+                     dim3(512), 0, st, idx, (const T*)ref_kv, ref_scales, ck, cv, sc16, Kh, Vh, N, n_refs,
                      sc, k, group, H);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_recon_d(int bits, const uint16_t* idx, const void* ref_kv, const uint8_t* ck,
+hipError_t launch_recon_d(int bits, const uint16_t* idx, const void* ref_kv,
+                          const uint16_t* ref_scales, int ref_bits, const uint8_t* ck,
                           const uint8_t* cv, const uint16_t* sc16, float* Kh, float* Vh,
                           int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc, int k,
                           int group, hipStream_t st) {
   switch (bits) {
-    case 0: return launch_recon_t<T, 0>(idx, ref_kv, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
-    case 2: return launch_recon_t<T, 2>(idx, ref_kv, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
-    case 4: return launch_recon_t<T, 4>(idx, ref_kv, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
-    default: return launch_recon_t<T, 8>(idx, ref_kv, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
+    case 0: return launch_recon_t<T, 0>(idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
+    case 2: return launch_recon_t<T, 2>(idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
+    case 4: return launch_recon_t<T, 4>(idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
+    default: return launch_recon_t<T, 8>(idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
   }
 }
 
 hipError_t launch_reconstruct(int dtype, int bits, const uint16_t* idx, const void* ref_kv,
-                              const uint8_t* ck, const uint8_t* cv, const uint16_t* sc16,
+                              const uint16_t* ref_scales, int ref_bits, const uint8_t* ck, const uint8_t* cv, const uint16_t* sc16,
                               float* Kh, float* Vh, int64_t n_inst, int H, int64_t N,
                               int64_t n_refs, Sched sc, int k, int group, hipStream_t st) {
   if (N == 0 || n_inst == 0) return hipSuccess;
   if (dtype == 0)
-    return launch_recon_d<float>(bits, idx, ref_kv, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
-  return launch_recon_d<__bf16>(bits, idx, ref_kv, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
+    return launch_recon_d<float>(bits, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
+  return launch_recon_d<__bf16>(bits, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
 }
 
 }  // namespace rkv

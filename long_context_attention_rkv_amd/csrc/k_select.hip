@@ -24,6 +24,7 @@
 #include <float.h>
 
 #include "rkv_common.h"
+#include "rkv_quant.h"
 
 namespace rkv {
 
@@ -32,9 +33,13 @@ namespace rkv {
 // head), at positions inside the input range that starts at p0): copies its
 // K and V rows into the cache's reference store, writes the bf16-rounded key
 // and its squared norm to the workspace.  Input rows are [ih][n_in][128].
+// With ref_bits = 4 the rows are stored quantised (int4 nibbles, fp16 scale
+// per group of `group` dims, the residual quantiser's exact rounding); the
+// workspace keys and norms still come from the original key.
 template <typename T>
 __global__ __launch_bounds__(256) void k_refstore(
-    const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ ref_kv,
+    const T* __restrict__ K, const T* __restrict__ V, void* __restrict__ ref_kv_v,
+    uint16_t* __restrict__ ref_scales, int ref_bits, int group,
     __bf16* __restrict__ refkey, float* __restrict__ refnorm, int64_t n_in, int64_t p0,
     int64_t n_refs, int64_t s0, int64_t ns, Sched sc, int64_t total_refs) {
   const int lane = threadIdx.x & 63;
@@ -45,13 +50,33 @@ __global__ __launch_bounds__(256) void k_refstore(
   const int64_t pos = sched_pos((int32_t)slot, sc);
   const T* kr = K + (ih * n_in + (pos - p0)) * 128;
   const T* vr = V + (ih * n_in + (pos - p0)) * 128;
-  T* dk = ref_kv + ((ih * 2 + 0) * n_refs + slot) * 128;
-  T* dv = ref_kv + ((ih * 2 + 1) * n_refs + slot) * 128;
   const int t = lane * 2;
-  dk[t] = kr[t];
-  dk[t + 1] = kr[t + 1];
-  dv[t] = vr[t];
-  dv[t + 1] = vr[t + 1];
+  if (ref_bits == 4) {
+    // lane t/2 holds dims t, t+1: one byte of nibbles per plane
+    uint8_t* rq = reinterpret_cast<uint8_t*>(ref_kv_v);
+    const int lanes_per_group = group >> 1;
+    const int ng = 128 / group;
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl) {
+      const T* xr = pl ? vr : kr;
+      const float x0 = (float)xr[t], x1 = (float)xr[t + 1];
+      float a = fmaxf(fabsf(x0), fabsf(x1));
+      for (int off = 1; off < lanes_per_group; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
+      const uint16_t sb = exact_scale_bits(a, 7.f, 1.0f / 7.f);
+      const int c0 = exact_code_of(x0, sb, 7.f), c1 = exact_code_of(x1, sb, 7.f);
+      const int64_t row = (ih * 2 + pl) * n_refs + slot;
+      rq[row * 64 + lane] = (uint8_t)((c0 & 0xF) | ((c1 & 0xF) << 4));
+      if (t % group == 0) ref_scales[row * ng + t / group] = sb;
+    }
+  } else {
+    T* ref_kv = reinterpret_cast<T*>(ref_kv_v);
+    T* dk = ref_kv + ((ih * 2 + 0) * n_refs + slot) * 128;
+    T* dv = ref_kv + ((ih * 2 + 1) * n_refs + slot) * 128;
+    dk[t] = kr[t];
+    dk[t + 1] = kr[t + 1];
+    dv[t] = vr[t];
+    dv[t + 1] = vr[t + 1];
+  }
   const __bf16 b0 = (__bf16)(float)kr[t];
   const __bf16 b1 = (__bf16)(float)kr[t + 1];
   const int64_t wr = ih * n_refs + slot;
@@ -427,7 +452,8 @@ __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
 // ------------------------------------------------------------------ launchers
 
 template <typename T>
-hipError_t launch_refstore_t(const void* K, const void* V, void* ref_kv, void* refkey,
+hipError_t launch_refstore_t(const void* K, const void* V, void* ref_kv, uint16_t* ref_scales,
+                             int ref_bits, int group, void* refkey,
                              float* refnorm, int64_t n_inst, int H, int64_t p0, int64_t n_in,
                              int64_t n_refs, Sched sc, hipStream_t st) {
   const int64_t s0 = sched_count((int32_t)p0, sc);
@@ -436,17 +462,20 @@ hipError_t launch_refstore_t(const void* K, const void* V, void* ref_kv, void* r
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + 3) / 4;
   hipLaunchKernelGGL(k_refstore<T>, dim3((unsigned)blocks), dim3(256), 0, st,
-                     (const T*)K, (const T*)V, (T*)ref_kv, (__bf16*)refkey, refnorm, n_in, p0,
-                     n_refs, s0, ns, sc, total);
+                     (const T*)K, (const T*)V, ref_kv, ref_scales, ref_bits, group,
+                     (__bf16*)refkey, refnorm, n_in, p0, n_refs, s0, ns, sc, total);
   return hipGetLastError();
 }
 
 hipError_t launch_refstore(int dtype, const void* K, const void* V, void* ref_kv,
+                           uint16_t* ref_scales, int ref_bits, int group,
                            void* refkey, float* refnorm, int64_t n_inst, int H,
                            int64_t p0, int64_t n_in, int64_t n_refs, Sched sc, hipStream_t st) {
   if (dtype == 0)
-    return launch_refstore_t<float>(K, V, ref_kv, refkey, refnorm, n_inst, H, p0, n_in, n_refs, sc, st);
-  return launch_refstore_t<__bf16>(K, V, ref_kv, refkey, refnorm, n_inst, H, p0, n_in, n_refs, sc, st);
+    return launch_refstore_t<float>(K, V, ref_kv, ref_scales, ref_bits, group, refkey, refnorm,
+                                    n_inst, H, p0, n_in, n_refs, sc, st);
+  return launch_refstore_t<__bf16>(K, V, ref_kv, ref_scales, ref_bits, group, refkey, refnorm,
+                                   n_inst, H, p0, n_in, n_refs, sc, st);
 }
 
 template <typename T, int KM>

@@ -10,23 +10,26 @@
 namespace rkv {
 // Encode kernels work on positions [p0, p0 + n_in) whose K/V rows are the
 // input [inst][H][n_in][128]; the cache keeps its full [.][.][N] layout.
-hipError_t launch_refstore(int dtype, const void* K, const void* V, void* ref_kv, void* refkey,
+hipError_t launch_refstore(int dtype, const void* K, const void* V, void* ref_kv,
+                           uint16_t* ref_scales, int ref_bits, int group, void* refkey,
                            float* refnorm, int64_t n_inst, int H, int64_t p0, int64_t n_in,
                            int64_t n_refs, Sched sc, hipStream_t st);
 hipError_t launch_dist_topk(int dtype, const void* K, const void* refkey, const float* refnorm,
                             uint16_t* idx, int64_t n_inst, int H, int64_t N, int64_t n_refs,
                             Sched sc, int k, int64_t p0, int64_t n_in, hipStream_t st);
 hipError_t launch_quantize(int dtype, int bits, const void* K, const void* V,
-                           const uint16_t* idx, const void* ref_kv, uint8_t* ck, uint8_t* cv,
+                           const uint16_t* idx, const void* ref_kv, const uint16_t* ref_scales,
+                           int ref_bits, uint8_t* ck, uint8_t* cv,
                            uint16_t* sc16, int64_t n_inst, int H, int64_t N, int64_t n_refs,
                            Sched sc, int k, int group, int64_t p0, int64_t n_in,
                            hipStream_t st);
 hipError_t launch_reconstruct(int dtype, int bits, const uint16_t* idx, const void* ref_kv,
-                              const uint8_t* ck, const uint8_t* cv, const uint16_t* sc16,
+                              const uint16_t* ref_scales, int ref_bits, const uint8_t* ck, const uint8_t* cv, const uint16_t* sc16,
                               float* Kh, float* Vh, int64_t n_inst, int H, int64_t N,
                               int64_t n_refs, Sched sc, int k, int group, hipStream_t st);
 hipError_t launch_decode(int dtype, int bits, const void* q, int n_q_heads, const uint16_t* idx,
-                         const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
+                         const void* ref_kv, const uint16_t* ref_scales, int ref_bits,
+                         const uint8_t* ck, const uint8_t* cv,
                          const uint16_t* sc16, float softmax_scale, float* out, int n_split,
                          void* ws, int64_t n_inst, int H, int64_t N, int64_t len,
                          int64_t n_refs, Sched sc, int k, int group, const int32_t* tile_list,
@@ -76,6 +79,8 @@ rkv_status check_shape(const rkv_cache* c) {
   if (c->bits != 0) {
     if (c->group != 32 && c->group != 64 && c->group != 128) return RKV_ERR_INVALID_ARG;
   }
+  if (c->ref_bits != 0 && c->ref_bits != 4) return RKV_ERR_INVALID_ARG;
+  if (c->ref_bits != 0 && c->bits == 0) return RKV_ERR_INVALID_ARG;
   const int64_t nr = rkv::sched_count((int32_t)c->seq_len, to_sched(c->stride));
   if (nr > 65535) return RKV_ERR_RANGE;
   return RKV_OK;
@@ -88,10 +93,11 @@ rkv_status check_ready(const rkv_cache* c) {
   if (c->n_inst == 0 || c->seq_len == 0) return RKV_OK;
   if (!c->ref_idx || !c->codes_k || !c->codes_v || !c->ref_kv) return RKV_ERR_INVALID_ARG;
   if (c->bits != 0 && !c->scales) return RKV_ERR_INVALID_ARG;
+  if (c->ref_bits != 0 && !c->ref_scales) return RKV_ERR_INVALID_ARG;
   return RKV_OK;
 }
 
-void sizes_of(const rkv_cache* c, size_t out[5]) {
+void sizes_of(const rkv_cache* c, size_t out[6]) {
   const size_t ih = (size_t)c->n_inst * c->n_kv_heads;
   const size_t N = (size_t)c->seq_len;
   const size_t D = (size_t)c->head_dim;
@@ -105,7 +111,13 @@ void sizes_of(const rkv_cache* c, size_t out[5]) {
     out[2] = ih * ((N + 31) / 32) * D * (32 * c->bits / 8);
     out[3] = ih * N * 2 * (D / c->group) * 2;
   }
-  out[4] = ih * 2 * (size_t)c->n_refs * D * elt_bytes(c->dtype);
+  if (c->ref_bits == 4) {
+    out[4] = ih * 2 * (size_t)c->n_refs * D / 2;
+    out[5] = ih * 2 * (size_t)c->n_refs * (D / c->group) * 2;
+  } else {
+    out[4] = ih * 2 * (size_t)c->n_refs * D * elt_bytes(c->dtype);
+    out[5] = 0;
+  }
 }
 
 size_t encode_ws(const rkv_cache* c) {
@@ -136,7 +148,7 @@ rkv_status rkv_cache_init(rkv_cache* c) {
   return RKV_OK;
 }
 
-rkv_status rkv_cache_sizes(const rkv_cache* c, size_t sizes[5]) {
+rkv_status rkv_cache_sizes(const rkv_cache* c, size_t sizes[6]) {
   if (!sizes) return RKV_ERR_INVALID_ARG;
   rkv_status s = check_shape(c);
   if (s != RKV_OK) return s;
@@ -163,7 +175,8 @@ static rkv_status select_range(const void* K, const void* V, const rkv_cache* c,
   char* refkey = (char*)ws;
   float* refnorm = (float*)((char*)ws + align_up(nr * 128 * 2));
   const Sched sc = to_sched(c->stride);
-  hipError_t e = rkv::launch_refstore((int)c->dtype, K, V, c->ref_kv, refkey, refnorm, c->n_inst,
+  hipError_t e = rkv::launch_refstore((int)c->dtype, K, V, c->ref_kv, c->ref_scales, c->ref_bits,
+                                      c->group, refkey, refnorm, c->n_inst,
                                       c->n_kv_heads, p0, n_in, c->n_refs, sc, st);
   if (e != hipSuccess) return hip_status(e);
   e = rkv::launch_dist_topk((int)c->dtype, K, refkey, refnorm, c->ref_idx, c->n_inst,
@@ -174,7 +187,7 @@ static rkv_status select_range(const void* K, const void* V, const rkv_cache* c,
 static rkv_status quantize_range(const void* K, const void* V, const rkv_cache* c, int64_t p0,
                                  int64_t n_in, hipStream_t st) {
   hipError_t e = rkv::launch_quantize((int)c->dtype, c->bits, K, V, c->ref_idx, c->ref_kv,
-                                      c->codes_k, c->codes_v, c->scales, c->n_inst,
+                                      c->ref_scales, c->ref_bits, c->codes_k, c->codes_v, c->scales, c->n_inst,
                                       c->n_kv_heads, c->seq_len, c->n_refs,
                                       to_sched(c->stride), c->k, c->group, p0, n_in, st);
   return hip_status(e);
@@ -226,6 +239,7 @@ rkv_status rkv_reconstruct(const rkv_cache* c, float* K_hat, float* V_hat, void*
   if (c->n_inst == 0 || c->seq_len == 0) return RKV_OK;
   if (!K_hat || !V_hat) return RKV_ERR_INVALID_ARG;
   hipError_t e = rkv::launch_reconstruct((int)c->dtype, c->bits, c->ref_idx, c->ref_kv,
+                                         c->ref_scales, c->ref_bits,
                                          c->codes_k, c->codes_v, c->scales, K_hat, V_hat,
                                          c->n_inst, c->n_kv_heads, c->seq_len, c->n_refs,
                                          to_sched(c->stride), c->k, c->group,
@@ -264,6 +278,7 @@ static rkv_status decode_common(const void* q, int32_t n_q_heads, const rkv_cach
   const size_t need = rkv::decode_ws_bytes(c->n_inst, c->n_kv_heads, n_q_heads, n_split, c->n_refs);
   if (!ws || ws_bytes < need) return RKV_ERR_WORKSPACE;
   hipError_t e = rkv::launch_decode((int)c->dtype, c->bits, q, n_q_heads, c->ref_idx, c->ref_kv,
+                                    c->ref_scales, c->ref_bits,
                                     c->codes_k, c->codes_v, c->scales, softmax_scale, out,
                                     n_split, ws, c->n_inst, c->n_kv_heads, c->seq_len, length,
                                     c->n_refs, to_sched(c->stride), c->k, c->group, tiles,

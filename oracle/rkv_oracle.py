@@ -163,7 +163,32 @@ def quantize_residual(delta32: np.ndarray, bits: int, group: int):
     return scale, codes.reshape(-1).astype(np.int64)
 
 
-def encode(K, V, base, double_after, k, bits, group, rows=None):
+def quantize_refs(K, V, T, group, bits=4):
+    """Full-pipeline quantisation of the reference store ([P1] "Impact and
+    Future Directions" and "Improvements for AI systems": 4-bit applied to
+    the uncompressed components as well).  Every reference row of K and V is
+    quantised like a residual row (quantize_residual).  Returns a dict:
+      scales  fp16 [2, |T|, d/group]
+      codes   int64 [2, |T|, d]
+      deq     fp32 [2, |T|, d]   code * scale (exact in fp32: a 4-bit
+                                 integer times an fp16 value)
+    """
+    out = {"scales": [], "codes": [], "deq": []}
+    for X in (K, V):
+        sc_p, c_p, d_p = [], [], []
+        for pos in T:
+            sc, c = quantize_residual(np.asarray(X[pos], dtype=np.float32), bits, group)
+            deq = c.astype(np.float64) * np.repeat(sc.astype(np.float64), group)
+            sc_p.append(sc)
+            c_p.append(c)
+            d_p.append(deq.astype(np.float32))
+        out["scales"].append(np.stack(sc_p))
+        out["codes"].append(np.stack(c_p))
+        out["deq"].append(np.stack(d_p))
+    return {key: np.stack(v) for key, v in out.items()}
+
+
+def encode(K, V, base, double_after, k, bits, group, rows=None, ref_bits=0):
     """Encode one (instance, KV head).
 
     K, V: [N, d] arrays holding the input values (bf16 inputs widened to
@@ -177,7 +202,9 @@ def encode(K, V, base, double_after, k, bits, group, rows=None):
       scales    fp16 [R, 2, d/group]        (bits > 0)
       codes     int64 [R, 2, d]             (bits > 0)
       resid64   fp64 [R, 2, d]  exact residual (bits == 0)
-    plus ``T`` (reference positions).
+    plus ``T`` (reference positions), and with ref_bits = 4 ``ref_q`` (the
+    quantised reference store of quantize_refs), whose dequantised rows
+    then stand in for the references in the means.
     """
     K = np.asarray(K, dtype=np.float32)
     V = np.asarray(V, dtype=np.float32)
@@ -185,6 +212,7 @@ def encode(K, V, base, double_after, k, bits, group, rows=None):
     T = ref_positions(n, base, double_after)
     rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
     keys = bf16_round(K)
+    ref_q = quantize_refs(K, V, T, group) if ref_bits == 4 else None
     R = rows.shape[0]
     out = {
         "T": T, "rows": rows,
@@ -193,6 +221,8 @@ def encode(K, V, base, double_after, k, bits, group, rows=None):
         "mean": np.zeros((R, 2, d), dtype=np.float32),
         "delta": np.zeros((R, 2, d), dtype=np.float32),
     }
+    if ref_q is not None:
+        out["ref_q"] = ref_q
     if bits > 0:
         out["scales"] = np.zeros((R, 2, d // group), dtype=np.float16)
         out["codes"] = np.zeros((R, 2, d), dtype=np.int64)
@@ -206,7 +236,7 @@ def encode(K, V, base, double_after, k, bits, group, rows=None):
         out["k_eff"][r] = sel.shape[0]
         pos = T[sel]
         for p, X in enumerate((K, V)):
-            m32 = ref_mean_f32(X[pos])
+            m32 = ref_mean_f32(ref_q["deq"][p][sel] if ref_q is not None else X[pos])
             z32 = residual_f32(X[i], m32)
             out["mean"][r, p] = m32
             out["delta"][r, p] = z32
@@ -259,8 +289,8 @@ def ref_store(K, V, T) -> np.ndarray:
 def reconstruct(enc, K, V, bits):
     """KV^_i for the encoded rows, fp64 [R, 2, d].
 
-    Reference positions are stored uncompressed and come back as they are.
-    Every other position is KV_R (the fp32 mean the residual was taken
+    Reference positions come back as stored: raw, or dequantised when the
+    reference store is quantised (enc has ``ref_q``).  Every other position is KV_R (the fp32 mean the residual was taken
     against) plus the dequantised residual scale * code (bits > 0) or the
     exact residual (bits == 0).
     """
@@ -273,8 +303,14 @@ def reconstruct(enc, K, V, bits):
         out += sc * enc["codes"].astype(np.float64)
     else:
         out += enc["resid64"]
-    raw = np.stack([np.asarray(K, np.float64)[enc["rows"]],
-                    np.asarray(V, np.float64)[enc["rows"]]], axis=1)
+    if "ref_q" in enc:
+        slot = np.searchsorted(T, enc["rows"])
+        deq = enc["ref_q"]["deq"].astype(np.float64)
+        raw = np.stack([deq[0][np.minimum(slot, T.shape[0] - 1)],
+                        deq[1][np.minimum(slot, T.shape[0] - 1)]], axis=1)
+    else:
+        raw = np.stack([np.asarray(K, np.float64)[enc["rows"]],
+                        np.asarray(V, np.float64)[enc["rows"]]], axis=1)
     out[is_ref] = raw[is_ref]
     return out
 

@@ -54,12 +54,22 @@ class GpuCache:
             cv = cache.codes_v.cpu().numpy()[: cache.sizes["codes_v"]].view(np.float64)
             self.resid = np.stack([ck.reshape(ih, self.N, self.D),
                                    cv.reshape(ih, self.N, self.D)], axis=2)
+        self.ref_bits = c.ref_bits
         rk = cache.ref_kv.cpu()
-        if self.dtype == "bf16":
+        if self.ref_bits == 4:
+            rb = rk[: cache.sizes["ref_kv"]].numpy().reshape(ih, 2, self.n_refs, self.D // 2)
+            self.ref_codes = unpack_rows(rb, 4)
+            ng = self.D // self.group
+            self.ref_scales = buf_u16(cache.ref_scales)[: cache.sizes["ref_scales"] // 2].reshape(
+                ih, 2, self.n_refs, ng).view(np.float16)
+            self.ref_kv = (self.ref_codes.astype(np.float64) *
+                           np.repeat(self.ref_scales.astype(np.float64), self.group, axis=-1))
+        elif self.dtype == "bf16":
             rk = rk[: cache.sizes["ref_kv"]].view(torch.bfloat16).float().numpy()
+            self.ref_kv = rk.reshape(ih, 2, self.n_refs, self.D)
         else:
             rk = rk[: cache.sizes["ref_kv"]].view(torch.float32).numpy()
-        self.ref_kv = rk.reshape(ih, 2, self.n_refs, self.D)
+            self.ref_kv = rk.reshape(ih, 2, self.n_refs, self.D)
 
     def codes(self, ih: int) -> np.ndarray:
         """int [N, 2, D] codes of one (instance, head)."""
@@ -92,12 +102,19 @@ def compare_encode(gc: GpuCache, ih: int, K: np.ndarray, V: np.ndarray, stride_b
     """Compare one (instance, head) of a GPU cache with the oracle on `rows`.
 
     Returns a dict of counts; raises AssertionError on any failure."""
-    enc = oracle.encode(K, V, stride_base, double_after, gc.k, gc.bits, gc.group, rows=rows)
+    enc = oracle.encode(K, V, stride_base, double_after, gc.k, gc.bits, gc.group, rows=rows,
+                        ref_bits=gc.ref_bits)
     T = enc["T"]
     assert T.shape[0] == gc.n_refs
-    # the reference store is an exact copy
-    np.testing.assert_array_equal(gc.ref_kv[ih, 0], K[T])
-    np.testing.assert_array_equal(gc.ref_kv[ih, 1], V[T])
+    if gc.ref_bits == 4:
+        # the quantised reference store: codes and scales bit-exact
+        np.testing.assert_array_equal(gc.ref_codes[ih], enc["ref_q"]["codes"])
+        np.testing.assert_array_equal(gc.ref_scales[ih].view(np.uint16),
+                                      enc["ref_q"]["scales"].view(np.uint16))
+    else:
+        # the reference store is an exact copy
+        np.testing.assert_array_equal(gc.ref_kv[ih, 0], K[T])
+        np.testing.assert_array_equal(gc.ref_kv[ih, 1], V[T])
     keys = oracle.bf16_round(K)
     rows_ = enc["rows"]
     gidx = gc.idx[ih][rows_]

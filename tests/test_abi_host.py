@@ -94,6 +94,7 @@ def _cache(**kw):
     c.k = kw.get("k", 8)
     c.bits = kw.get("bits", 4)
     c.group = kw.get("group", 32)
+    c.ref_bits = kw.get("ref_bits", 0)
     return c
 
 
@@ -101,13 +102,17 @@ def test_cache_init_and_sizes(lib):
     c = _cache()
     assert lib.rkv_cache_init(C.byref(c)) == L.RKV_OK
     assert c.n_refs == 256
-    sz = (C.c_size_t * 5)()
+    sz = (C.c_size_t * 6)()
     assert lib.rkv_cache_sizes(C.byref(c), sz) == L.RKV_OK
     ih, N = 16, 8192
     assert list(sz) == [ih * N * 8 * 2, ih * N * 64, ih * (N // 32) * 128 * 16,
-                        ih * N * 2 * 4 * 2, ih * 2 * 256 * 128 * 2]
+                        ih * N * 2 * 4 * 2, ih * 2 * 256 * 128 * 2, 0]
     # per head-token record: 64 + 64 code bytes, 16 scale bytes, 16 index bytes
     assert (sz[0] + sz[1] + sz[2] + sz[3]) // (ih * N) == 160
+    # full-pipeline quantisation: the reference rows as int4 + fp16 scales
+    c.ref_bits = 4
+    assert lib.rkv_cache_sizes(C.byref(c), sz) == L.RKV_OK
+    assert (sz[4], sz[5]) == (ih * 2 * 256 * 64, ih * 2 * 256 * 4 * 2)
 
 
 @pytest.mark.parametrize("bad,status", [
@@ -116,6 +121,7 @@ def test_cache_init_and_sizes(lib):
     (dict(D=64), L.RKV_ERR_UNSUPPORTED), (dict(base=0), L.RKV_ERR_INVALID_ARG),
     (dict(dtype=7), L.RKV_ERR_INVALID_ARG), (dict(H=0), L.RKV_ERR_INVALID_ARG),
     (dict(N=65536 * 2, base=2), L.RKV_ERR_RANGE), (dict(A=100, base=16), L.RKV_ERR_INVALID_ARG),
+    (dict(ref_bits=2), L.RKV_ERR_INVALID_ARG), (dict(ref_bits=4, bits=0), L.RKV_ERR_INVALID_ARG),
 ])
 def test_cache_init_rejects(lib, bad, status):
     c = _cache(**bad)

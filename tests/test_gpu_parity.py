@@ -57,9 +57,9 @@ def make_q(cfg, n_inst, device="cuda"):
                         for i in range(n_inst)])
 
 
-def encode(cfg, K, V, bits, n_inst, seq_len):
+def encode(cfg, K, V, bits, n_inst, seq_len, ref_bits=0):
     cache = rkv.Cache(n_inst, cfg.n_kv_heads, seq_len, cfg.dtype, cfg.stride_base, cfg.k,
-                      bits, cfg.group, double_after=cfg.double_after)
+                      bits, cfg.group, double_after=cfg.double_after, ref_bits=ref_bits)
     rkv.rkv_encode(K, V, cache)
     torch.cuda.synchronize()
     return cache
@@ -177,14 +177,14 @@ DECODE = [
 ]
 
 
-def _oracle_decode(cfg, K, V, q, bits, scale):
+def _oracle_decode(cfg, K, V, q, bits, scale, ref_bits=0):
     n_inst, H = K.shape[0], K.shape[1]
     out = np.zeros((n_inst, q.shape[1], q.shape[2]))
     for i in range(n_inst):
         kh, vh = [], []
         for h in range(H):
             enc = oracle.encode(K[i, h], V[i, h], cfg.stride_base, cfg.double_after, cfg.k,
-                                bits, cfg.group)
+                                bits, cfg.group, ref_bits=ref_bits)
             kv = oracle.reconstruct(enc, K[i, h], V[i, h], bits)
             kh.append(kv[:, 0])
             vh.append(kv[:, 1])
@@ -303,6 +303,49 @@ def test_decode_all_tiles_equals_dense():
     assert rel_l2(sparse, dense) <= 1e-6
 
 
+# ------------------------------------------------------------------ quantised reference store
+
+REFQ_CASES = [
+    ("tiny_f32_int8", get_config(0), 8, 1, 1024),
+    ("llama_bf16_int4_gqa4", _cfg(1, n_kv_heads=2, n_q_heads=8), 4, 1, 1000),
+    ("stress_int2_k16_g64", _cfg(4, n_kv_heads=2, n_q_heads=14, batch=2), 2, 2, 500),
+]
+
+
+@pytest.mark.parametrize("case", REFQ_CASES, ids=[c[0] for c in REFQ_CASES])
+def test_quantized_refs_parity(case):
+    """Full-pipeline quantisation: reference codes/scales bit-exact, residual
+    codes bit-exact against the dequantised references, reconstruction and
+    decode against the oracle."""
+    _need_gpu()
+    name, cfg, bits, n_inst, N = case
+    say(f"[quantised refs] {name}: N={N} bits={bits}")
+    K, V = make_kv(cfg, n_inst, N)
+    q = make_q(cfg, n_inst)
+    cache = encode(cfg, K, V, bits, n_inst, N, ref_bits=4)
+    gc = GpuCache(cache)
+    Kn, Vn, qn = to_np_f32(K), to_np_f32(V), to_np_f32(q)
+    Kh, Vh = rkv.rkv_reconstruct(cache)
+    Khn, Vhn = Kh.cpu().numpy(), Vh.cpu().numpy()
+    near = 0
+    for i in range(n_inst):
+        for h in range(cfg.n_kv_heads):
+            r = compare_encode(gc, i * cfg.n_kv_heads + h, Kn[i, h], Vn[i, h],
+                               cfg.stride_base, cfg.double_after)
+            near += r["near_ties"]
+            kv = oracle.reconstruct(r["enc"], Kn[i, h], Vn[i, h], bits)
+            m = r["matched"]
+            assert rel_l2(Khn[i, h][m], kv[m, 0]) <= 1e-5
+            assert rel_l2(Vhn[i, h][m], kv[m, 1]) <= 1e-5
+    say(f"  near-ties: {near}")
+    for scale in (1.0 / math.sqrt(cfg.head_dim), 1.0):
+        got = rkv.rkv_decode_attn(q, cfg.n_q_heads, cache, scale, n_split=3).cpu().numpy()
+        want = _oracle_decode(cfg, Kn, Vn, qn, bits, scale, ref_bits=4)
+        err = rel_l2(got, want)
+        say(f"  decode scale={scale:.4f} rel L2 = {err:.2e}")
+        assert err <= 2e-3
+
+
 # ------------------------------------------------------------------ streaming encode
 
 APPEND_CASES = [
@@ -313,12 +356,13 @@ APPEND_CASES = [
     ("dynamic_int4", _cfg(3, n_kv_heads=2, double_after=512, drift_block=128), 4, 1, 1500, 450,
      (3, 1, 40)),
     ("bf16_nobits", _cfg(1, n_kv_heads=1), 0, 1, 300, 37, (1, 2)),
+    ("llama_int4_quantised_refs", _cfg(1, n_kv_heads=2), 4, 1, 700, 100, (1, 9)),
 ]
 
 
-def _stream_encode(cfg, K, V, bits, n_inst, N, prefill, chunks):
+def _stream_encode(cfg, K, V, bits, n_inst, N, prefill, chunks, ref_bits=0):
     cache = rkv.Cache(n_inst, cfg.n_kv_heads, N, cfg.dtype, cfg.stride_base, cfg.k, bits,
-                      cfg.group, double_after=cfg.double_after)
+                      cfg.group, double_after=cfg.double_after, ref_bits=ref_bits)
     ws = torch.empty(rkv.rkv_encode_workspace(cache), dtype=torch.uint8, device="cuda")
     pos = 0
     if prefill:
@@ -343,10 +387,11 @@ def test_append_equals_batch_encode(case):
     name, cfg, bits, n_inst, N, prefill, chunks = case
     say(f"[append] {name}: N={N} prefill={prefill} chunks={chunks}")
     K, V = make_kv(cfg, n_inst, N)
-    whole = encode(cfg, K, V, bits, n_inst, N)
-    streamed = _stream_encode(cfg, K, V, bits, n_inst, N, prefill, chunks)
+    ref_bits = 4 if "quantised_refs" in name else 0
+    whole = encode(cfg, K, V, bits, n_inst, N, ref_bits=ref_bits)
+    streamed = _stream_encode(cfg, K, V, bits, n_inst, N, prefill, chunks, ref_bits=ref_bits)
     for buf in rkv.Cache.BUFFERS:
-        if bits == 0 and buf == "scales":
+        if (bits == 0 and buf == "scales") or (ref_bits == 0 and buf == "ref_scales"):
             continue
         assert torch.equal(whole.buffers[buf], streamed.buffers[buf]), buf
 

@@ -370,3 +370,35 @@ def test_tile_positions_golden():
     assert got.tolist() == list(range(0, 32)) + list(range(64, 70))
     assert oracle.tile_positions([1], 32).tolist() == []
     assert oracle.tile_positions(range(3), 70).tolist() == list(range(70))
+
+
+def test_quantized_refs_dequantise_exactly_and_within_half_scale():
+    rng = np.random.default_rng(5)
+    K = rng.standard_normal((300, 128)).astype(np.float32)
+    V = (3.0 * rng.standard_normal((300, 128))).astype(np.float32)
+    T = oracle.ref_positions(300, 16)
+    q = oracle.quantize_refs(K, V, T, 32)
+    assert q["codes"].shape == (2, T.shape[0], 128)
+    assert np.abs(q["codes"]).max() <= 7
+    for p, X in enumerate((K, V)):
+        sc = np.repeat(q["scales"][p].astype(np.float64), 32, axis=-1)
+        # dequantised value = code * scale exactly (checked in rationals)
+        for s_, t in ((0, 0), (3, 77), (T.shape[0] - 1, 127)):
+            want = Fraction(int(q["codes"][p][s_, t])) * Fraction(float(sc[s_, t]))
+            assert Fraction(float(q["deq"][p][s_, t])) == want
+        err = np.abs(X[T].astype(np.float64) - q["deq"][p].astype(np.float64))
+        assert np.all(err <= sc / 2 + 1e-12)
+
+
+def test_encode_with_quantized_refs_uses_the_dequantised_rows():
+    rng = np.random.default_rng(6)
+    K = rng.standard_normal((96, 16)).astype(np.float32)
+    V = rng.standard_normal((96, 16)).astype(np.float32)
+    enc = oracle.encode(K, V, 8, 0, 3, 4, 8, ref_bits=4)
+    deq = enc["ref_q"]["deq"]
+    for r in (5, 40, 95):
+        sel = enc["idx"][r][enc["idx"][r] != oracle.IDX_PAD].astype(np.int64)
+        np.testing.assert_array_equal(enc["mean"][r, 0], oracle.ref_mean_f32(deq[0][sel]))
+    kv = oracle.reconstruct(enc, K, V, 4)
+    T = enc["T"]
+    np.testing.assert_array_equal(kv[T, 0], deq[0].astype(np.float64))
