@@ -122,6 +122,21 @@ typedef struct {
    * original keys. */
   int32_t ref_bits;
   uint16_t *ref_scales;
+  /* Latent residuals (paper page, section "DeltaKV Framework Architecture":
+   * the residual is taken between compressor outputs f_c(KV) - f_c(KV_R) and
+   * rebuilt through a decompressor f_d).  The pages' pair is trained; a
+   * fixed orthogonal pair stands in for it here.  latent = 1 (needs bits > 0) stores the codes and scales
+   * of f_c(KV - KV_R) instead of KV - KV_R, with the fixed orthogonal pair
+   *   f_c(x) = H D x / 16,   f_d(y) = D H y / 8   (f_d(f_c(x)) = x),
+   * H the 128-point Walsh-Hadamard matrix (entry (i, t) = (-1)^popcount(i&t))
+   * and D = diag(+-1), dim t negated iff the top bit of the (t+1)-th output
+   * of SplitMix64 seeded with latent_seed is set.  f_c is linear, so this is
+   * the pages' difference of projections.  Reconstruction adds f_d of the
+   * dequantised codes to KV_R; decode scores the codes against H D q / 8 and
+   * applies f_d to the merged residual output.  latent = 0: plain residuals,
+   * latent_seed unused. */
+  int32_t latent;
+  uint64_t latent_seed;
 } rkv_cache;
 
 /* Number of references below seq_len; -1 if the schedule is invalid. */

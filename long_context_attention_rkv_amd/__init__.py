@@ -74,7 +74,8 @@ class Cache:
     BUFFERS = ("ref_idx", "codes_k", "codes_v", "scales", "ref_kv", "ref_scales")
 
     def __init__(self, n_inst, n_kv_heads, seq_len, dtype, stride_base, k, bits, group,
-                 double_after=0, head_dim=128, device="cuda", allocate=True, ref_bits=0):
+                 double_after=0, head_dim=128, device="cuda", allocate=True, ref_bits=0,
+                 latent=0, latent_seed=0):
         self.dtype = dtype
         self.torch_dtype = _DT[dtype][1]
         s = L.RkvCache()
@@ -88,6 +89,8 @@ class Cache:
         s.bits = int(bits)
         s.group = int(group)
         s.ref_bits = int(ref_bits)
+        s.latent = int(latent)
+        s.latent_seed = int(latent_seed) & ((1 << 64) - 1)
         _check(_load().rkv_cache_init(C.byref(s)), "rkv_cache_init")
         self.c = s
         sizes = (C.c_size_t * 6)()

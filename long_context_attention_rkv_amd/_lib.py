@@ -40,6 +40,8 @@ class RkvCache(C.Structure):
         ("ref_kv", C.c_void_p),
         ("ref_bits", C.c_int32),
         ("ref_scales", C.c_void_p),
+        ("latent", C.c_int32),
+        ("latent_seed", C.c_uint64),
     ]
 
 

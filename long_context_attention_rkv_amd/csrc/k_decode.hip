@@ -232,7 +232,8 @@ __global__ __launch_bounds__(256, 2) void k_decode(
     const uint8_t* __restrict__ codes_k, const uint8_t* __restrict__ codes_v,
     const uint16_t* __restrict__ scales, const float* __restrict__ qk, float* __restrict__ part,
     float alpha, int64_t N, int64_t Nlen, int64_t n_refs, Sched sc, int k, int G, int H,
-    int n_split, const int32_t* __restrict__ tile_list, int32_t n_list) {
+    int n_split, const int32_t* __restrict__ tile_list, int32_t n_list,
+    const float* __restrict__ qrot) {
   // N: positions the cache holds (layout); Nlen <= N: positions attended
   constexpr int HPL = 4 / NG;  // query heads per lane in the score layout
   constexpr int GS = 128 / NG;  // dims per scale group
@@ -299,17 +300,20 @@ __global__ __launch_bounds__(256, 2) void k_decode(
   }
 
   // ---- A operand of the score MFMA: rows (h, g); lane quad covers dims
-  //      32*quad .. +31, step s dims 32*quad + 8*s + perm(e).
+  //      32*quad .. +31, step s dims 32*quad + 8*s + perm(e).  Latent codes
+  //      are scored against the rotated query qrot = H D q / 8 instead
+  //      (q . f_d(y) = (H D q / 8) . y).
   f16x8 aq[4];
   {
     const int h = n / NG, g = n % NG;
+    const float* qr = qrot ? qrot + (inst * Hq + kvh * G) * 128 : nullptr;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int dim = 32 * quad + 8 * s + perm_of<BITS>(e);
         float v = 0.f;
-        if (h < G && dim / GS == g) v = (float)qh[h * 128 + dim];
+        if (h < G && dim / GS == g) v = qr ? qr[h * 128 + dim] : (float)qh[h * 128 + dim];
         aq[s][e] = (_Float16)v;
       }
     }
@@ -700,7 +704,8 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
                                                  const uint16_t* __restrict__ ref_scales,
                                                  int ref_bits, int group,
                                                  float* __restrict__ out, int G, int H,
-                                                 int64_t n_refs, int64_t n_valid, int n_split) {
+                                                 int64_t n_refs, int64_t n_valid, int n_split,
+                                                 float* __restrict__ ores) {
   extern __shared__ float cs[];
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
   float* wt = cs;                   // [G][nrp]
@@ -802,8 +807,66 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
     const float* b = base + h * n_split * rec + 4 + chunk * 32 + tt;
     float o = 0.f;
     for (int x = 0; x < n_split; ++x) o += fs[h * n_split + x] * b[x * rec];
-    out[(inst * Hq + kvh * G + h) * 128 + chunk * 32 + tt] = (o + s) / ls_[h];
+    const int64_t at = (inst * Hq + kvh * G + h) * 128 + chunk * 32 + tt;
+    if (ores) {
+      // latent codes: the residual part is still rotated; f_d is applied
+      // to the whole row afterwards
+      ores[at] = o / ls_[h];
+      out[at] = s / ls_[h];
+    } else {
+      out[at] = (o + s) / ls_[h];
+    }
   }
+}
+
+// ------------------------------------------------------ latent transforms
+// One wave per 128-dim row, lane l holding dims 2l and 2l+1: index bit 0
+// inside the lane, bits 1-6 across lanes (xor 1 .. 32).
+__device__ inline void fwht128_2(float& a, float& b, int l) {
+  const float x = a + b, y = a - b;
+  a = x;
+  b = y;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const bool hi = (l & m) != 0;
+    const float pa = __shfl_xor(a, m), pb = __shfl_xor(b, m);
+    a = hi ? pa - a : a + pa;
+    b = hi ? pb - b : b + pb;
+  }
+}
+
+__device__ inline void lat_signs2(float& a, float& b, const LatMask& lm, int l) {
+  const uint32_t word = l < 32 ? (l < 16 ? lm.w[0] : lm.w[1]) : (l < 48 ? lm.w[2] : lm.w[3]);
+  const uint32_t bb = (word >> (2 * (l & 15))) & 3u;
+  a = __uint_as_float(__float_as_uint(a) ^ ((bb & 1u) << 31));
+  b = __uint_as_float(__float_as_uint(b) ^ ((bb >> 1) << 31));
+}
+
+// qrot[r] = H D q[r] / 8 (fp32), r < rows.
+template <typename T>
+__global__ __launch_bounds__(256) void k_latent_q(const T* __restrict__ q, LatMask lm,
+                                                  float* __restrict__ qrot, int64_t rows) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;  // whole waves
+  const int l = threadIdx.x & 63;
+  float a = (float)q[r * 128 + 2 * l], b = (float)q[r * 128 + 2 * l + 1];
+  lat_signs2(a, b, lm, l);
+  fwht128_2(a, b, l);
+  qrot[r * 128 + 2 * l] = a * 0.125f;
+  qrot[r * 128 + 2 * l + 1] = b * 0.125f;
+}
+
+// out[r] += f_d(ores[r]) = D H ores[r] / 8, r < rows.
+__global__ __launch_bounds__(256) void k_latent_out(const float* __restrict__ ores, LatMask lm,
+                                                    float* __restrict__ out, int64_t rows) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int l = threadIdx.x & 63;
+  float a = ores[r * 128 + 2 * l], b = ores[r * 128 + 2 * l + 1];
+  fwht128_2(a, b, l);
+  lat_signs2(a, b, lm, l);
+  out[r * 128 + 2 * l] += a * 0.125f;
+  out[r * 128 + 2 * l + 1] += b * 0.125f;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -812,10 +875,22 @@ static size_t qk_bytes(int64_t n_inst, int n_q_heads, int64_t n_refs) {
   return (b + 255) / 256 * 256;
 }
 
-size_t decode_ws_bytes(int64_t n_inst, int H, int n_q_heads, int n_split, int64_t n_refs) {
+static size_t part_bytes(int64_t n_inst, int n_q_heads, int n_split, int64_t n_refs) {
+  const size_t b = (size_t)n_inst * n_q_heads * n_split * part_rec_floats(n_refs) * 4;
+  return (b + 255) / 256 * 256;
+}
+
+// latent mode: rotated queries, then the merged rotated residual outputs
+static size_t row_bytes(int64_t n_inst, int n_q_heads) {
+  const size_t b = (size_t)n_inst * n_q_heads * 128 * 4;
+  return (b + 255) / 256 * 256;
+}
+
+size_t decode_ws_bytes(int64_t n_inst, int H, int n_q_heads, int n_split, int64_t n_refs,
+                       bool latent) {
   (void)H;
-  return qk_bytes(n_inst, n_q_heads, n_refs) +
-         (size_t)n_inst * n_q_heads * n_split * part_rec_floats(n_refs) * 4;
+  return qk_bytes(n_inst, n_q_heads, n_refs) + part_bytes(n_inst, n_q_heads, n_split, n_refs) +
+         (latent ? 2 * row_bytes(n_inst, n_q_heads) : 0);
 }
 
 size_t decode_lds_bytes(int G, int NG, int64_t n_refs) {
@@ -842,10 +917,22 @@ hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
                            const uint8_t* ck, const uint8_t* cv,
                            const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
                            int64_t n_inst, int H, int64_t N, int64_t len, int64_t n_refs, Sched sc, int k,
-                           const int32_t* tile_list, int32_t n_list, hipStream_t st) {
+                           const int32_t* tile_list, int32_t n_list, const LatMask* lm,
+                           hipStream_t st) {
   const int G = n_q_heads / H;
   float* qk = (float*)ws;
   float* part = (float*)((char*)ws + qk_bytes(n_inst, n_q_heads, n_refs));
+  float* qrot = nullptr;
+  float* ores = nullptr;
+  const int64_t rows = n_inst * n_q_heads;
+  if (lm) {
+    qrot = (float*)((char*)part + part_bytes(n_inst, n_q_heads, n_split, n_refs));
+    ores = (float*)((char*)qrot + row_bytes(n_inst, n_q_heads));
+    hipLaunchKernelGGL(k_latent_q<T>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+                       (const T*)q, *lm, qrot, rows);
+    const hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
   const int64_t n_valid = sched_count((int32_t)len, sc);
   hipLaunchKernelGGL(k_qk_table<T>, dim3((unsigned)((nrp + 255) / 256), H, (unsigned)n_inst),
@@ -861,7 +948,7 @@ hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
   }
   hipLaunchKernelGGL(kern, dim3(n_split, H, (unsigned)n_inst), dim3(256), lds, st, (const T*)q,
                      (const T*)ref_kv, idx, ck, cv, sc16, qk, part, alpha, N, len, n_refs, sc, k, G, H,
-                     n_split, tile_list, n_list);
+                     n_split, tile_list, n_list, qrot);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t clds = combine_lds_bytes(G, n_refs, n_split);
@@ -872,7 +959,11 @@ hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
   }
   hipLaunchKernelGGL(k_combine<T>, dim3(H, (unsigned)n_inst, kCombChunks), dim3(256), clds, st,
                      part, (const T*)ref_kv, ref_scales, ref_bits, group_r, out, G, H, n_refs,
-                     n_valid, n_split);
+                     n_valid, n_split, ores);
+  e = hipGetLastError();
+  if (e != hipSuccess || !lm) return e;
+  hipLaunchKernelGGL(k_latent_out, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, ores, *lm,
+                     out, rows);
   return hipGetLastError();
 }
 
@@ -882,13 +973,13 @@ hipError_t launch_decode_k(int k, const void* q, int n_q_heads, const uint16_t* 
                            const uint8_t* ck, const uint8_t* cv,
                            const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
                            int64_t n_inst, int H, int64_t N, int64_t len, int64_t n_refs, Sched sc, const int32_t* tile_list,
-                           int32_t n_list, hipStream_t st) {
-  if (k == 4) return launch_decode_t<T, BITS, NG, 4, true>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
-  if (k == 8) return launch_decode_t<T, BITS, NG, 8, true>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
-  if (k == 16) return launch_decode_t<T, BITS, NG, 16, true>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
-  if (k < 4) return launch_decode_t<T, BITS, NG, 4, false>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
-  if (k < 8) return launch_decode_t<T, BITS, NG, 8, false>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
-  return launch_decode_t<T, BITS, NG, 16, false>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
+                           int32_t n_list, const LatMask* lm, hipStream_t st) {
+  if (k == 4) return launch_decode_t<T, BITS, NG, 4, true>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, lm, st);
+  if (k == 8) return launch_decode_t<T, BITS, NG, 8, true>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, lm, st);
+  if (k == 16) return launch_decode_t<T, BITS, NG, 16, true>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, lm, st);
+  if (k < 4) return launch_decode_t<T, BITS, NG, 4, false>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, lm, st);
+  if (k < 8) return launch_decode_t<T, BITS, NG, 8, false>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, lm, st);
+  return launch_decode_t<T, BITS, NG, 16, false>(q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, lm, st);
 }
 
 template <typename T, int BITS>
@@ -897,12 +988,12 @@ hipError_t launch_decode_g(int group, int k, const void* q, int n_q_heads, const
                            const uint8_t* ck, const uint8_t* cv,
                            const uint16_t* sc16, float alpha, float* out, int n_split, void* ws,
                            int64_t n_inst, int H, int64_t N, int64_t len, int64_t n_refs, Sched sc, const int32_t* tile_list,
-                           int32_t n_list, hipStream_t st) {
+                           int32_t n_list, const LatMask* lm, hipStream_t st) {
   if (group == 32)
-    return launch_decode_k<T, BITS, 4>(k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
+    return launch_decode_k<T, BITS, 4>(k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, lm, st);
   if (group == 64)
-    return launch_decode_k<T, BITS, 2>(k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
-  return launch_decode_k<T, BITS, 1>(k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
+    return launch_decode_k<T, BITS, 2>(k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, lm, st);
+  return launch_decode_k<T, BITS, 1>(k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, lm, st);
 }
 
 template <typename T>
@@ -911,12 +1002,12 @@ hipError_t launch_decode_b(int bits, int group, int k, const void* q, int n_q_he
                            int ref_bits, int group_r, const uint8_t* ck,
                            const uint8_t* cv, const uint16_t* sc16, float alpha, float* out,
                            int n_split, void* ws, int64_t n_inst, int H, int64_t N, int64_t len, int64_t n_refs, Sched sc, const int32_t* tile_list,
-                           int32_t n_list, hipStream_t st) {
+                           int32_t n_list, const LatMask* lm, hipStream_t st) {
   if (bits == 2)
-    return launch_decode_g<T, 2>(group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
+    return launch_decode_g<T, 2>(group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, lm, st);
   if (bits == 4)
-    return launch_decode_g<T, 4>(group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
-  return launch_decode_g<T, 8>(group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
+    return launch_decode_g<T, 4>(group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, lm, st);
+  return launch_decode_g<T, 8>(group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group_r, ck, cv, sc16, alpha, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, lm, st);
 }
 
 hipError_t launch_decode(int dtype, int bits, const void* q, int n_q_heads, const uint16_t* idx,
@@ -925,10 +1016,10 @@ hipError_t launch_decode(int dtype, int bits, const void* q, int n_q_heads, cons
                          const uint16_t* sc16, float softmax_scale, float* out, int n_split,
                          void* ws, int64_t n_inst, int H, int64_t N, int64_t len, int64_t n_refs, Sched sc,
                          int k, int group, const int32_t* tile_list, int32_t n_list,
-                         hipStream_t st) {
+                         const LatMask* lm, hipStream_t st) {
   if (dtype == 0)
-    return launch_decode_b<float>(bits, group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
-  return launch_decode_b<__bf16>(bits, group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, st);
+    return launch_decode_b<float>(bits, group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, lm, st);
+  return launch_decode_b<__bf16>(bits, group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, lm, st);
 }
 
 }  // namespace rkv

@@ -367,13 +367,14 @@ __device__ inline void unpack_slots(const PosLoads<T, KM>& p, uint32_t (&sl)[KM]
 // the first chunks of a sequence) a position's row and slots are loaded one
 // step ahead and its mean is the unpredicated fast form; otherwise k_eff is
 // taken per position.
-template <typename T, int BITS, int KM, bool RQ>
+template <typename T, int BITS, int KM, bool RQ, bool LAT>
 __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
     const T* __restrict__ K, const T* __restrict__ V, const uint16_t* __restrict__ idx,
     const T* __restrict__ ref_kv, const uint16_t* __restrict__ ref_scales,
     uint8_t* __restrict__ codes_k,
     uint8_t* __restrict__ codes_v, uint16_t* __restrict__ scales, int64_t N,
-    int64_t n_refs, Sched sc, int k, int group, int chunk, int H, int p0, int n_in) {
+    int64_t n_refs, Sched sc, int k, int group, int chunk, int H, int p0, int n_in,
+    LatMask lm) {
   __shared__ int8_t vt[128][kVTile + 1];  // odd pitch: the 16 writing lanes hit 16 banks
   const int tid = threadIdx.x;
   const int tok_l = tid >> 5;          // position within the step
@@ -422,6 +423,14 @@ __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
 #pragma unroll
       for (int e = 0; e < 8; ++e) dst[e] = (double)x[e] - (double)m[e];
     } else {
+      if constexpr (LAT) {
+        // latent residual f_c(z) = H D z / 16 (the 16 lanes of the row take
+        // the same branch: they share `tok`)
+        lat_signs8(z, lm, dl);
+        fwht128_8(z, dl);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] *= 0.0625f;
+      }
       float a = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(z[e]));
@@ -524,13 +533,13 @@ __device__ inline int code_at(const uint8_t* row, int t) {
   return v >= (1 << (BITS - 1)) ? v - (1 << BITS) : v;
 }
 
-template <typename T, int BITS, int KM, bool RQ>
+template <typename T, int BITS, int KM, bool RQ, bool LAT>
 __global__ __launch_bounds__(512) void k_reconstruct(
     const uint16_t* __restrict__ idx, const T* __restrict__ ref_kv,
     const uint16_t* __restrict__ ref_scales,
     const uint8_t* __restrict__ codes_k, const uint8_t* __restrict__ codes_v,
     const uint16_t* __restrict__ scales, float* __restrict__ Kh, float* __restrict__ Vh,
-    int64_t N, int64_t n_refs, Sched sc, int k, int group, int H) {
+    int64_t N, int64_t n_refs, Sched sc, int k, int group, int H, LatMask lm) {
   const int tid = threadIdx.x;
   const int plane = (tid >> 4) & 1;
   const int dl = tid & 15;
@@ -565,10 +574,11 @@ __global__ __launch_bounds__(512) void k_reconstruct(
     const int n_groups = 128 / group;
     const float s = half_bits_to_f32(
         scales[((ih * N + tok) * 2 + plane) * n_groups + (8 * dl) / group]);
+    float y[8];  // dequantised residual (exact: fp16 scale x small integer)
     if (plane == 0) {
       const uint8_t* row = codes_k + (ih * N + tok) * (128 * BITS / 8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = m[e] + s * (float)code_at<BITS>(row, 8 * dl + e);
+      for (int e = 0; e < 8; ++e) y[e] = s * (float)code_at<BITS>(row, 8 * dl + e);
     } else {
       const int64_t tile = tok / kVTile;
       const int u = (int)(tok % kVTile);
@@ -576,9 +586,18 @@ __global__ __launch_bounds__(512) void k_reconstruct(
       for (int e = 0; e < 8; ++e) {
         const uint8_t* row = codes_v + ((ih * ((N + kVTile - 1) / kVTile) + tile) * 128 +
                                         8 * dl + e) * (kVTile * BITS / 8);
-        out[e] = m[e] + s * (float)code_at<BITS>(row, u);
+        y[e] = s * (float)code_at<BITS>(row, u);
       }
     }
+    if constexpr (LAT) {
+      // f_d(y) = D H y / 8
+      fwht128_8(y, dl);
+      lat_signs8(y, lm, dl);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] *= 0.125f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = m[e] + y[e];
   }
   store8(dst, out);
 }
@@ -589,19 +608,26 @@ hipError_t launch_quantize_t(const void* K, const void* V, const uint16_t* idx,
                              const void* ref_kv, const uint16_t* ref_scales, int ref_bits,
                              uint8_t* ck, uint8_t* cv, uint16_t* sc16,
                              int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
-                             int k, int group, int64_t p0, int64_t n_in, hipStream_t st) {
+                             int k, int group, int64_t p0, int64_t n_in, const LatMask* lm,
+                             hipStream_t st) {
   const int chunk = 256;
   const int64_t start = p0 & ~(int64_t)(kVTile - 1);
   const int64_t nchunks = (p0 + n_in - start + chunk - 1) / chunk;
-  auto pick = [&](auto rq) {
+  // latent codes exist only with quantisation (BITS > 0)
+  auto pick = [&](auto rq, auto lat) {
     constexpr bool R = decltype(rq)::value;
-    return k <= 4 ? k_quantize<T, BITS, 4, R>
-                  : (k <= 8 ? k_quantize<T, BITS, 8, R> : k_quantize<T, BITS, 16, R>);
+    constexpr bool L = decltype(lat)::value && BITS != 0;
+    return k <= 4 ? k_quantize<T, BITS, 4, R, L>
+                  : (k <= 8 ? k_quantize<T, BITS, 8, R, L> : k_quantize<T, BITS, 16, R, L>);
   };
-  auto kern = ref_bits == 4 ? pick(std::true_type{}) : pick(std::false_type{});
+  auto pick_r = [&](auto lat) {
+    return ref_bits == 4 ? pick(std::true_type{}, lat) : pick(std::false_type{}, lat);
+  };
+  auto kern = lm ? pick_r(std::true_type{}) : pick_r(std::false_type{});
+  const LatMask m = lm ? *lm : LatMask{{0u, 0u, 0u, 0u}};
   hipLaunchKernelGGL(kern, dim3((unsigned)nchunks, H, (unsigned)n_inst),
                      dim3(512), 0, st, (const T*)K, (const T*)V, idx, (const T*)ref_kv, ref_scales, ck,
-                     cv, sc16, N, n_refs, sc, k, group, chunk, H, (int)p0, (int)n_in);
+                     cv, sc16, N, n_refs, sc, k, group, chunk, H, (int)p0, (int)n_in, m);
   return hipGetLastError();
 }
 
@@ -610,12 +636,13 @@ hipError_t launch_quantize_d(int bits, const void* K, const void* V, const uint1
                              const void* ref_kv, const uint16_t* ref_scales, int ref_bits,
                              uint8_t* ck, uint8_t* cv, uint16_t* sc16,
                              int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc,
-                             int k, int group, int64_t p0, int64_t n_in, hipStream_t st) {
+                             int k, int group, int64_t p0, int64_t n_in, const LatMask* lm,
+                             hipStream_t st) {
   switch (bits) {
-    case 0: return launch_quantize_t<T, 0>(K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
-    case 2: return launch_quantize_t<T, 2>(K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
-    case 4: return launch_quantize_t<T, 4>(K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
-    default: return launch_quantize_t<T, 8>(K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
+    case 0: return launch_quantize_t<T, 0>(K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, lm, st);
+    case 2: return launch_quantize_t<T, 2>(K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, lm, st);
+    case 4: return launch_quantize_t<T, 4>(K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, lm, st);
+    default: return launch_quantize_t<T, 8>(K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, lm, st);
   }
 }
 
@@ -624,11 +651,11 @@ hipError_t launch_quantize(int dtype, int bits, const void* K, const void* V,
                            int ref_bits, uint8_t* ck, uint8_t* cv,
                            uint16_t* sc16, int64_t n_inst, int H, int64_t N, int64_t n_refs,
                            Sched sc, int k, int group, int64_t p0, int64_t n_in,
-                           hipStream_t st) {
+                           const LatMask* lm, hipStream_t st) {
   if (n_in == 0 || n_inst == 0) return hipSuccess;
   if (dtype == 0)
-    return launch_quantize_d<float>(bits, K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
-  return launch_quantize_d<__bf16>(bits, K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, st);
+    return launch_quantize_d<float>(bits, K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, lm, st);
+  return launch_quantize_d<__bf16>(bits, K, V, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, n_inst, H, N, n_refs, sc, k, group, p0, n_in, lm, st);
 }
 
 template <typename T, int BITS>
@@ -636,17 +663,22 @@ hipError_t launch_recon_t(const uint16_t* idx, const void* ref_kv, const uint16_
                           int ref_bits, const uint8_t* ck,
                           const uint8_t* cv, const uint16_t* sc16, float* Kh, float* Vh,
                           int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc, int k,
-                          int group, hipStream_t st) {
+                          int group, const LatMask* lm, hipStream_t st) {
   const int64_t blocks = (N + kQTokens - 1) / kQTokens;
-  auto pick = [&](auto rq) {
+  auto pick = [&](auto rq, auto lat) {
     constexpr bool R = decltype(rq)::value;
-    return k <= 4 ? k_reconstruct<T, BITS, 4, R>
-                  : (k <= 8 ? k_reconstruct<T, BITS, 8, R> : k_reconstruct<T, BITS, 16, R>);
+    constexpr bool L = decltype(lat)::value && BITS != 0;
+    return k <= 4 ? k_reconstruct<T, BITS, 4, R, L>
+                  : (k <= 8 ? k_reconstruct<T, BITS, 8, R, L> : k_reconstruct<T, BITS, 16, R, L>);
   };
-  auto kern = ref_bits == 4 ? pick(std::true_type{}) : pick(std::false_type{});
+  auto pick_r = [&](auto lat) {
+    return ref_bits == 4 ? pick(std::true_type{}, lat) : pick(std::false_type{}, lat);
+  };
+  auto kern = lm ? pick_r(std::true_type{}) : pick_r(std::false_type{});
+  const LatMask m = lm ? *lm : LatMask{{0u, 0u, 0u, 0u}};
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks, H, (unsigned)n_inst),
                      dim3(512), 0, st, idx, (const T*)ref_kv, ref_scales, ck, cv, sc16, Kh, Vh, N, n_refs,
-                     sc, k, group, H);
+                     sc, k, group, H, m);
   return hipGetLastError();
 }
 
@@ -655,23 +687,24 @@ hipError_t launch_recon_d(int bits, const uint16_t* idx, const void* ref_kv,
                           const uint16_t* ref_scales, int ref_bits, const uint8_t* ck,
                           const uint8_t* cv, const uint16_t* sc16, float* Kh, float* Vh,
                           int64_t n_inst, int H, int64_t N, int64_t n_refs, Sched sc, int k,
-                          int group, hipStream_t st) {
+                          int group, const LatMask* lm, hipStream_t st) {
   switch (bits) {
-    case 0: return launch_recon_t<T, 0>(idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
-    case 2: return launch_recon_t<T, 2>(idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
-    case 4: return launch_recon_t<T, 4>(idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
-    default: return launch_recon_t<T, 8>(idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
+    case 0: return launch_recon_t<T, 0>(idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, lm, st);
+    case 2: return launch_recon_t<T, 2>(idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, lm, st);
+    case 4: return launch_recon_t<T, 4>(idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, lm, st);
+    default: return launch_recon_t<T, 8>(idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, lm, st);
   }
 }
 
 hipError_t launch_reconstruct(int dtype, int bits, const uint16_t* idx, const void* ref_kv,
                               const uint16_t* ref_scales, int ref_bits, const uint8_t* ck, const uint8_t* cv, const uint16_t* sc16,
                               float* Kh, float* Vh, int64_t n_inst, int H, int64_t N,
-                              int64_t n_refs, Sched sc, int k, int group, hipStream_t st) {
+                              int64_t n_refs, Sched sc, int k, int group, const LatMask* lm,
+                              hipStream_t st) {
   if (N == 0 || n_inst == 0) return hipSuccess;
   if (dtype == 0)
-    return launch_recon_d<float>(bits, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
-  return launch_recon_d<__bf16>(bits, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, st);
+    return launch_recon_d<float>(bits, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, lm, st);
+  return launch_recon_d<__bf16>(bits, idx, ref_kv, ref_scales, ref_bits, ck, cv, sc16, Kh, Vh, n_inst, H, N, n_refs, sc, k, group, lm, st);
 }
 
 }  // namespace rkv

@@ -22,19 +22,21 @@ hipError_t launch_quantize(int dtype, int bits, const void* K, const void* V,
                            int ref_bits, uint8_t* ck, uint8_t* cv,
                            uint16_t* sc16, int64_t n_inst, int H, int64_t N, int64_t n_refs,
                            Sched sc, int k, int group, int64_t p0, int64_t n_in,
-                           hipStream_t st);
+                           const LatMask* lm, hipStream_t st);
 hipError_t launch_reconstruct(int dtype, int bits, const uint16_t* idx, const void* ref_kv,
                               const uint16_t* ref_scales, int ref_bits, const uint8_t* ck, const uint8_t* cv, const uint16_t* sc16,
                               float* Kh, float* Vh, int64_t n_inst, int H, int64_t N,
-                              int64_t n_refs, Sched sc, int k, int group, hipStream_t st);
+                              int64_t n_refs, Sched sc, int k, int group, const LatMask* lm,
+                              hipStream_t st);
 hipError_t launch_decode(int dtype, int bits, const void* q, int n_q_heads, const uint16_t* idx,
                          const void* ref_kv, const uint16_t* ref_scales, int ref_bits,
                          const uint8_t* ck, const uint8_t* cv,
                          const uint16_t* sc16, float softmax_scale, float* out, int n_split,
                          void* ws, int64_t n_inst, int H, int64_t N, int64_t len,
                          int64_t n_refs, Sched sc, int k, int group, const int32_t* tile_list,
-                         int32_t n_list, hipStream_t st);
-size_t decode_ws_bytes(int64_t n_inst, int H, int n_q_heads, int n_split, int64_t n_refs);
+                         int32_t n_list, const LatMask* lm, hipStream_t st);
+size_t decode_ws_bytes(int64_t n_inst, int H, int n_q_heads, int n_split, int64_t n_refs,
+                       bool latent);
 bool decode_fits(int G, int group, int64_t n_refs, int n_split);
 }  // namespace rkv
 
@@ -81,6 +83,8 @@ rkv_status check_shape(const rkv_cache* c) {
   }
   if (c->ref_bits != 0 && c->ref_bits != 4) return RKV_ERR_INVALID_ARG;
   if (c->ref_bits != 0 && c->bits == 0) return RKV_ERR_INVALID_ARG;
+  if (c->latent != 0 && c->latent != 1) return RKV_ERR_INVALID_ARG;
+  if (c->latent != 0 && c->bits == 0) return RKV_ERR_INVALID_ARG;
   const int64_t nr = rkv::sched_count((int32_t)c->seq_len, to_sched(c->stride));
   if (nr > 65535) return RKV_ERR_RANGE;
   return RKV_OK;
@@ -119,6 +123,13 @@ void sizes_of(const rkv_cache* c, size_t out[6]) {
     out[5] = 0;
   }
 }
+
+// The latent sign mask of a cache, or NULL when latent codes are off.
+struct LatArg {
+  rkv::LatMask m;
+  const rkv::LatMask* p;
+  explicit LatArg(const rkv_cache* c) : m(rkv::make_latmask(c->latent_seed)), p(c->latent ? &m : nullptr) {}
+};
 
 size_t encode_ws(const rkv_cache* c) {
   const size_t nr = (size_t)c->n_inst * c->n_kv_heads * c->n_refs;
@@ -186,10 +197,12 @@ static rkv_status select_range(const void* K, const void* V, const rkv_cache* c,
 
 static rkv_status quantize_range(const void* K, const void* V, const rkv_cache* c, int64_t p0,
                                  int64_t n_in, hipStream_t st) {
+  const LatArg lat(c);
   hipError_t e = rkv::launch_quantize((int)c->dtype, c->bits, K, V, c->ref_idx, c->ref_kv,
                                       c->ref_scales, c->ref_bits, c->codes_k, c->codes_v, c->scales, c->n_inst,
                                       c->n_kv_heads, c->seq_len, c->n_refs,
-                                      to_sched(c->stride), c->k, c->group, p0, n_in, st);
+                                      to_sched(c->stride), c->k, c->group, p0, n_in,
+                                      lat.p, st);
   return hip_status(e);
 }
 
@@ -238,11 +251,12 @@ rkv_status rkv_reconstruct(const rkv_cache* c, float* K_hat, float* V_hat, void*
   if (s != RKV_OK) return s;
   if (c->n_inst == 0 || c->seq_len == 0) return RKV_OK;
   if (!K_hat || !V_hat) return RKV_ERR_INVALID_ARG;
+  const LatArg lat(c);
   hipError_t e = rkv::launch_reconstruct((int)c->dtype, c->bits, c->ref_idx, c->ref_kv,
                                          c->ref_scales, c->ref_bits,
                                          c->codes_k, c->codes_v, c->scales, K_hat, V_hat,
                                          c->n_inst, c->n_kv_heads, c->seq_len, c->n_refs,
-                                         to_sched(c->stride), c->k, c->group,
+                                         to_sched(c->stride), c->k, c->group, lat.p,
                                          (hipStream_t)stream);
   return hip_status(e);
 }
@@ -255,7 +269,8 @@ rkv_status rkv_decode_workspace(const rkv_cache* c, int32_t n_q_heads, int32_t n
   if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0 || n_split < 1 || n_split > 4096)
     return RKV_ERR_INVALID_ARG;
   *bytes = rkv::decode_ws_bytes(c->n_inst, c->n_kv_heads, n_q_heads, n_split,
-                                rkv::sched_count((int32_t)c->seq_len, to_sched(c->stride)));
+                                rkv::sched_count((int32_t)c->seq_len, to_sched(c->stride)),
+                                c->latent != 0);
   return RKV_OK;
 }
 
@@ -275,14 +290,16 @@ static rkv_status decode_common(const void* q, int32_t n_q_heads, const rkv_cach
   if (c->n_inst == 0) return RKV_OK;
   if (!q || !out) return RKV_ERR_INVALID_ARG;
   if (c->seq_len == 0) return RKV_ERR_INVALID_ARG;
-  const size_t need = rkv::decode_ws_bytes(c->n_inst, c->n_kv_heads, n_q_heads, n_split, c->n_refs);
+  const size_t need = rkv::decode_ws_bytes(c->n_inst, c->n_kv_heads, n_q_heads, n_split, c->n_refs,
+                                           c->latent != 0);
   if (!ws || ws_bytes < need) return RKV_ERR_WORKSPACE;
+  const LatArg lat(c);
   hipError_t e = rkv::launch_decode((int)c->dtype, c->bits, q, n_q_heads, c->ref_idx, c->ref_kv,
                                     c->ref_scales, c->ref_bits,
                                     c->codes_k, c->codes_v, c->scales, softmax_scale, out,
                                     n_split, ws, c->n_inst, c->n_kv_heads, c->seq_len, length,
                                     c->n_refs, to_sched(c->stride), c->k, c->group, tiles,
-                                    n_tiles, (hipStream_t)stream);
+                                    n_tiles, lat.p, (hipStream_t)stream);
   return hip_status(e);
 }
 

@@ -155,6 +155,70 @@ __device__ inline float group_max(float v, int lanes) {
   return v;
 }
 
+// ------------------------------------------------------- latent transform
+// Latent variant of the residual (paper page, "DeltaKV Framework
+// Architecture": residuals of compressed projections, rebuilt by a
+// decompressor).  Untrained stand-in: f_c(x) = H D x / 16, f_d(y) = D H y / 8
+// with H the 128-point Walsh-Hadamard matrix (entries (-1)^popcount(i & t))
+// and D = diag(+-1); f_d(f_c(x)) = x.
+//
+// Sign bits of D: dim t is negated iff bit t%32 of w[t/32] is set.  They are
+// the top bits of the first 128 outputs of SplitMix64 started at the seed.
+struct LatMask {
+  uint32_t w[4];
+};
+
+inline uint64_t splitmix64_next(uint64_t& state) {
+  state += 0x9E3779B97F4A7C15ull;
+  uint64_t z = state;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+inline LatMask make_latmask(uint64_t seed) {
+  LatMask m{{0u, 0u, 0u, 0u}};
+  uint64_t st = seed;
+  for (int t = 0; t < 128; ++t)
+    if (splitmix64_next(st) >> 63) m.w[t >> 5] |= 1u << (t & 31);
+  return m;
+}
+
+// Negate the dims of D among 8*dl .. 8*dl+7 (exact: a sign-bit flip).
+__device__ inline void lat_signs8(float (&z)[8], const LatMask& lm, int dl) {
+  const uint32_t word = dl < 8 ? (dl < 4 ? lm.w[0] : lm.w[1]) : (dl < 12 ? lm.w[2] : lm.w[3]);
+  const uint32_t b = (word >> (8 * (dl & 3))) & 0xFFu;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = __uint_as_float(__float_as_uint(z[e]) ^ (((b >> e) & 1u) << 31));
+}
+
+// Unnormalised 128-point Walsh-Hadamard transform of a row spread over 16
+// aligned lanes, lane dl holding dims 8*dl .. 8*dl+7.  Butterflies
+// (a, b) -> (a + b, a - b) over index bit 0, 1, ..., 6 in that order, each
+// rounded to fp32: bits 0-2 inside the lane, bits 3-6 across lanes (the lane
+// holding the upper element of a pair computes partner - own).
+__device__ inline void fwht128_8(float (&z)[8], int dl) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (e & h) continue;
+      const float a = z[e], b = z[e | h];
+      z[e] = a + b;
+      z[e | h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    const bool hi = (dl & m) != 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = __shfl_xor(z[e], m);
+      z[e] = hi ? p - z[e] : z[e] + p;
+    }
+  }
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));

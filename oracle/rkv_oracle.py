@@ -188,7 +188,78 @@ def quantize_refs(K, V, T, group, bits=4):
     return {key: np.stack(v) for key, v in out.items()}
 
 
-def encode(K, V, base, double_after, k, bits, group, rows=None, ref_bits=0):
+# ---------------------------------------------------------------------------
+# Latent variant ([P1] "DeltaKV Framework Architecture": the residual is taken
+# between compressed projections, z = f_c(KV) - f_c(KV_R), and decoded by f_d;
+# [P1] "Improvements for AI systems": f_c and f_d are a compressor /
+# decompressor pair).  Untrained stand-in: a fixed, seeded sign flip D
+# followed by the Walsh-Hadamard transform H (H[i][t] = (-1)^popcount(i&t)):
+#     f_c(x) = H D x / 16,     f_d(y) = D H y / 8,     f_d(f_c(x)) = x
+# (H H = 128 I, D D = I; both scalings are powers of two).  f_c is linear, so
+# z = f_c(KV - KV_R) is the rotated residual; it is quantised as usual.
+# ---------------------------------------------------------------------------
+
+_M64 = (1 << 64) - 1
+
+
+def splitmix64(seed: int, n: int):
+    """First n outputs of SplitMix64 (Steele, Lea and Flood; Vigna's public
+    reference): the state advances by 0x9E3779B97F4A7C15 and each output is
+    the state mixed by two xor-shift-multiply rounds and a final xor-shift."""
+    out, st = [], seed & _M64
+    for _ in range(n):
+        st = (st + 0x9E3779B97F4A7C15) & _M64
+        z = st
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+        out.append(z ^ (z >> 31))
+    return out
+
+
+def latent_signs(seed: int, d: int = 128) -> np.ndarray:
+    """D: sign of dim t is -1 when the top bit of the t-th SplitMix64 output
+    is set, else +1."""
+    return np.array([-1.0 if (x >> 63) else 1.0 for x in splitmix64(seed, d)], dtype=np.float32)
+
+
+def fwht_f32(x) -> np.ndarray:
+    """Unnormalised Walsh-Hadamard transform of a length-2^m vector in fp32:
+    butterflies (a, b) -> (a + b, a - b) on index bit 0, then bit 1, ..., each
+    result rounded to fp32."""
+    y = np.asarray(x, dtype=np.float32).copy()
+    n = y.shape[0]
+    h = 1
+    while h < n:
+        y = y.reshape(-1, 2, h)
+        a, b = y[:, 0, :].copy(), y[:, 1, :].copy()
+        y[:, 0, :] = (a + b).astype(np.float32)
+        y[:, 1, :] = (a - b).astype(np.float32)
+        y = y.reshape(n)
+        h *= 2
+    return y
+
+
+def latent_fc(z32, signs) -> np.ndarray:
+    """f_c of an fp32 row: sign flips (exact), the fp32 transform, / 16 (exact)."""
+    return (fwht_f32(np.asarray(z32, np.float32) * signs) * np.float32(1.0 / 16)).astype(np.float32)
+
+
+def latent_fd64(y, signs) -> np.ndarray:
+    """f_d in fp64: D H y / 8."""
+    y = np.asarray(y, dtype=np.float64)
+    n = y.shape[-1]
+    Hm = hadamard(n)
+    return (y @ Hm.T) * signs.astype(np.float64) / 8.0
+
+
+def hadamard(n: int) -> np.ndarray:
+    """Sylvester Hadamard matrix, entries (-1)^popcount(i & t), fp64."""
+    i = np.arange(n)
+    pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i[:, None] & i[None, :])
+    return np.where(pc % 2 == 0, 1.0, -1.0)
+
+
+def encode(K, V, base, double_after, k, bits, group, rows=None, ref_bits=0, latent_seed=None):
     """Encode one (instance, KV head).
 
     K, V: [N, d] arrays holding the input values (bf16 inputs widened to
@@ -204,7 +275,9 @@ def encode(K, V, base, double_after, k, bits, group, rows=None, ref_bits=0):
       resid64   fp64 [R, 2, d]  exact residual (bits == 0)
     plus ``T`` (reference positions), and with ref_bits = 4 ``ref_q`` (the
     quantised reference store of quantize_refs), whose dequantised rows
-    then stand in for the references in the means.
+    then stand in for the references in the means.  With latent_seed set
+    (bits > 0) the stored codes are those of f_c(residual), and ``signs``
+    holds D.
     """
     K = np.asarray(K, dtype=np.float32)
     V = np.asarray(V, dtype=np.float32)
@@ -223,6 +296,11 @@ def encode(K, V, base, double_after, k, bits, group, rows=None, ref_bits=0):
     }
     if ref_q is not None:
         out["ref_q"] = ref_q
+    signs = None
+    if latent_seed is not None:
+        assert bits > 0
+        signs = latent_signs(latent_seed, d)
+        out["signs"] = signs
     if bits > 0:
         out["scales"] = np.zeros((R, 2, d // group), dtype=np.float16)
         out["codes"] = np.zeros((R, 2, d), dtype=np.int64)
@@ -241,7 +319,8 @@ def encode(K, V, base, double_after, k, bits, group, rows=None, ref_bits=0):
             out["mean"][r, p] = m32
             out["delta"][r, p] = z32
             if bits > 0:
-                s, q = quantize_residual(z32, bits, group)
+                zq = latent_fc(z32, signs) if signs is not None else z32
+                s, q = quantize_residual(zq, bits, group)
                 out["scales"][r, p] = s
                 out["codes"][r, p] = q
             else:
@@ -300,7 +379,8 @@ def reconstruct(enc, K, V, bits):
     if bits > 0:
         g = enc["codes"].shape[-1] // enc["scales"].shape[-1]
         sc = np.repeat(enc["scales"].astype(np.float64), g, axis=-1)
-        out += sc * enc["codes"].astype(np.float64)
+        y = sc * enc["codes"].astype(np.float64)
+        out += latent_fd64(y, enc["signs"]) if "signs" in enc else y
     else:
         out += enc["resid64"]
     if "ref_q" in enc:

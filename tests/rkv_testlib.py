@@ -55,6 +55,7 @@ class GpuCache:
             self.resid = np.stack([ck.reshape(ih, self.N, self.D),
                                    cv.reshape(ih, self.N, self.D)], axis=2)
         self.ref_bits = c.ref_bits
+        self.latent_seed = int(c.latent_seed) if c.latent else None
         rk = cache.ref_kv.cpu()
         if self.ref_bits == 4:
             rb = rk[: cache.sizes["ref_kv"]].numpy().reshape(ih, 2, self.n_refs, self.D // 2)
@@ -103,7 +104,7 @@ def compare_encode(gc: GpuCache, ih: int, K: np.ndarray, V: np.ndarray, stride_b
 
     Returns a dict of counts; raises AssertionError on any failure."""
     enc = oracle.encode(K, V, stride_base, double_after, gc.k, gc.bits, gc.group, rows=rows,
-                        ref_bits=gc.ref_bits)
+                        ref_bits=gc.ref_bits, latent_seed=gc.latent_seed)
     T = enc["T"]
     assert T.shape[0] == gc.n_refs
     if gc.ref_bits == 4:

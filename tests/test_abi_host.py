@@ -95,6 +95,8 @@ def _cache(**kw):
     c.bits = kw.get("bits", 4)
     c.group = kw.get("group", 32)
     c.ref_bits = kw.get("ref_bits", 0)
+    c.latent = kw.get("latent", 0)
+    c.latent_seed = kw.get("latent_seed", 0)
     return c
 
 
@@ -122,6 +124,7 @@ def test_cache_init_and_sizes(lib):
     (dict(dtype=7), L.RKV_ERR_INVALID_ARG), (dict(H=0), L.RKV_ERR_INVALID_ARG),
     (dict(N=65536 * 2, base=2), L.RKV_ERR_RANGE), (dict(A=100, base=16), L.RKV_ERR_INVALID_ARG),
     (dict(ref_bits=2), L.RKV_ERR_INVALID_ARG), (dict(ref_bits=4, bits=0), L.RKV_ERR_INVALID_ARG),
+    (dict(latent=2), L.RKV_ERR_INVALID_ARG), (dict(latent=1, bits=0), L.RKV_ERR_INVALID_ARG),
 ])
 def test_cache_init_rejects(lib, bad, status):
     c = _cache(**bad)
@@ -182,3 +185,22 @@ def test_status_strings(lib):
     for s in range(6):
         assert lib.rkv_status_string(s)
     assert lib.rkv_version() >= 1
+
+
+def test_latent_decode_workspace_holds_two_rows_per_query_head(lib):
+    c = _cache()
+    assert lib.rkv_cache_init(C.byref(c)) == L.RKV_OK
+    plain, lat = C.c_size_t(), C.c_size_t()
+    assert lib.rkv_decode_workspace(C.byref(c), 32, 4, C.byref(plain)) == L.RKV_OK
+    c.latent, c.latent_seed = 1, 0xFFFFFFFFFFFFFFFF
+    assert lib.rkv_cache_init(C.byref(c)) == L.RKV_OK
+    assert lib.rkv_decode_workspace(C.byref(c), 32, 4, C.byref(lat)) == L.RKV_OK
+    # rotated queries and rotated residual outputs, fp32 [inst][n_q_heads][128] each
+    assert lat.value - plain.value >= 2 * 2 * 32 * 128 * 4
+    # the code sizes do not change
+    sz_p, sz_l = (C.c_size_t * 6)(), (C.c_size_t * 6)()
+    c.latent = 0
+    lib.rkv_cache_sizes(C.byref(c), sz_p)
+    c.latent = 1
+    lib.rkv_cache_sizes(C.byref(c), sz_l)
+    assert list(sz_p) == list(sz_l)

@@ -57,9 +57,15 @@ def make_q(cfg, n_inst, device="cuda"):
                         for i in range(n_inst)])
 
 
-def encode(cfg, K, V, bits, n_inst, seq_len, ref_bits=0):
+def _latent_kw(latent_seed):
+    return dict(latent=0, latent_seed=0) if latent_seed is None else \
+        dict(latent=1, latent_seed=latent_seed)
+
+
+def encode(cfg, K, V, bits, n_inst, seq_len, ref_bits=0, latent_seed=None):
     cache = rkv.Cache(n_inst, cfg.n_kv_heads, seq_len, cfg.dtype, cfg.stride_base, cfg.k,
-                      bits, cfg.group, double_after=cfg.double_after, ref_bits=ref_bits)
+                      bits, cfg.group, double_after=cfg.double_after, ref_bits=ref_bits,
+                      **_latent_kw(latent_seed))
     rkv.rkv_encode(K, V, cache)
     torch.cuda.synchronize()
     return cache
@@ -177,14 +183,14 @@ DECODE = [
 ]
 
 
-def _oracle_decode(cfg, K, V, q, bits, scale, ref_bits=0):
+def _oracle_decode(cfg, K, V, q, bits, scale, ref_bits=0, latent_seed=None):
     n_inst, H = K.shape[0], K.shape[1]
     out = np.zeros((n_inst, q.shape[1], q.shape[2]))
     for i in range(n_inst):
         kh, vh = [], []
         for h in range(H):
             enc = oracle.encode(K[i, h], V[i, h], cfg.stride_base, cfg.double_after, cfg.k,
-                                bits, cfg.group, ref_bits=ref_bits)
+                                bits, cfg.group, ref_bits=ref_bits, latent_seed=latent_seed)
             kv = oracle.reconstruct(enc, K[i, h], V[i, h], bits)
             kh.append(kv[:, 0])
             vh.append(kv[:, 1])
@@ -346,6 +352,77 @@ def test_quantized_refs_parity(case):
         assert err <= 2e-3
 
 
+# ------------------------------------------------------------------ latent residuals
+
+LATENT_CASES = [
+    # (id, config, bits, n_inst, N, ref_bits, seed)
+    ("tiny_f32_int8", get_config(0), 8, 1, 1024, 0, 0),
+    ("llama_bf16_int4_gqa4_ragged", _cfg(1, n_kv_heads=2, n_q_heads=8), 4, 1, 1000, 0, 1234567),
+    ("stress_int2_k16_g64", _cfg(4, n_kv_heads=2, n_q_heads=14, batch=2), 2, 2, 500, 0,
+     0xFFFFFFFFFFFFFFFF),
+    ("dynamic_int4_g128", _cfg(3, n_kv_heads=1, n_q_heads=4, group=128, double_after=512,
+                                drift_block=128), 4, 1, 1300, 0, 99),
+    ("llama_int4_quantised_refs", _cfg(1, n_kv_heads=2, n_q_heads=8), 4, 1, 700, 4, 7),
+]
+
+
+@pytest.mark.parametrize("case", LATENT_CASES, ids=[c[0] for c in LATENT_CASES])
+def test_latent_parity(case):
+    """Latent residuals f_c(KV - KV_R): codes and scales bit-exact (both sides
+    rotate the fp32 residual with the same butterfly order), reconstruction
+    through f_d and decode through the rotated query against the oracle."""
+    _need_gpu()
+    name, cfg, bits, n_inst, N, ref_bits, seed = case
+    say(f"[latent] {name}: N={N} bits={bits} ref_bits={ref_bits} seed={seed:#x}")
+    K, V = make_kv(cfg, n_inst, N)
+    q = make_q(cfg, n_inst)
+    cache = encode(cfg, K, V, bits, n_inst, N, ref_bits=ref_bits, latent_seed=seed)
+    gc = GpuCache(cache)
+    assert gc.latent_seed == seed
+    Kn, Vn, qn = to_np_f32(K), to_np_f32(V), to_np_f32(q)
+    Kh, Vh = rkv.rkv_reconstruct(cache)
+    Khn, Vhn = Kh.cpu().numpy(), Vh.cpu().numpy()
+    near = 0
+    for i in range(n_inst):
+        for h in range(cfg.n_kv_heads):
+            r = compare_encode(gc, i * cfg.n_kv_heads + h, Kn[i, h], Vn[i, h],
+                               cfg.stride_base, cfg.double_after)
+            near += r["near_ties"]
+            kv = oracle.reconstruct(r["enc"], Kn[i, h], Vn[i, h], bits)
+            m = r["matched"]
+            assert rel_l2(Khn[i, h][m], kv[m, 0]) <= 1e-5
+            assert rel_l2(Vhn[i, h][m], kv[m, 1]) <= 1e-5
+    say(f"  near-ties: {near}")
+    for scale in (1.0 / math.sqrt(cfg.head_dim), 1.0):
+        got = rkv.rkv_decode_attn(q, cfg.n_q_heads, cache, scale, n_split=3).cpu().numpy()
+        want = _oracle_decode(cfg, Kn, Vn, qn, bits, scale, ref_bits=ref_bits, latent_seed=seed)
+        err = rel_l2(got, want)
+        say(f"  decode scale={scale:.4f} rel L2 = {err:.2e}")
+        assert err <= 2e-3
+
+
+def test_latent_changes_codes_not_the_rebuilt_cache():
+    """Two seeds give different codes; both rebuild K, V about as well as the
+    plain residual codes (the rotation is orthogonal up to scaling)."""
+    _need_gpu()
+    cfg = _cfg(1, n_kv_heads=2)
+    N = 900
+    say(f"[latent seeds] N={N}")
+    K, V = make_kv(cfg, 1, N)
+    plain = encode(cfg, K, V, 4, 1, N)
+    a = encode(cfg, K, V, 4, 1, N, latent_seed=1)
+    b = encode(cfg, K, V, 4, 1, N, latent_seed=2)
+    assert not torch.equal(a.buffers["codes_k"], b.buffers["codes_k"])
+    assert torch.equal(a.buffers["ref_idx"], plain.buffers["ref_idx"])
+    Kn = to_np_f32(K)
+    errs = []
+    for c in (plain, a, b):
+        Kh, _ = rkv.rkv_reconstruct(c)
+        errs.append(rel_l2(Kh.cpu().numpy(), Kn))
+    say(f"  rel L2 of K^: plain {errs[0]:.3e}, latent {errs[1]:.3e} / {errs[2]:.3e}")
+    assert max(errs[1:]) <= 2 * errs[0]
+
+
 # ------------------------------------------------------------------ streaming encode
 
 APPEND_CASES = [
@@ -357,12 +434,14 @@ APPEND_CASES = [
      (3, 1, 40)),
     ("bf16_nobits", _cfg(1, n_kv_heads=1), 0, 1, 300, 37, (1, 2)),
     ("llama_int4_quantised_refs", _cfg(1, n_kv_heads=2), 4, 1, 700, 100, (1, 9)),
+    ("stress_int2_latent", _cfg(4, n_kv_heads=2, batch=2), 2, 2, 500, 77, (1, 40)),
 ]
 
 
-def _stream_encode(cfg, K, V, bits, n_inst, N, prefill, chunks, ref_bits=0):
+def _stream_encode(cfg, K, V, bits, n_inst, N, prefill, chunks, ref_bits=0, latent_seed=None):
     cache = rkv.Cache(n_inst, cfg.n_kv_heads, N, cfg.dtype, cfg.stride_base, cfg.k, bits,
-                      cfg.group, double_after=cfg.double_after, ref_bits=ref_bits)
+                      cfg.group, double_after=cfg.double_after, ref_bits=ref_bits,
+                      **_latent_kw(latent_seed))
     ws = torch.empty(rkv.rkv_encode_workspace(cache), dtype=torch.uint8, device="cuda")
     pos = 0
     if prefill:
@@ -388,8 +467,10 @@ def test_append_equals_batch_encode(case):
     say(f"[append] {name}: N={N} prefill={prefill} chunks={chunks}")
     K, V = make_kv(cfg, n_inst, N)
     ref_bits = 4 if "quantised_refs" in name else 0
-    whole = encode(cfg, K, V, bits, n_inst, N, ref_bits=ref_bits)
-    streamed = _stream_encode(cfg, K, V, bits, n_inst, N, prefill, chunks, ref_bits=ref_bits)
+    seed = 0x5EED if "latent" in name else None
+    whole = encode(cfg, K, V, bits, n_inst, N, ref_bits=ref_bits, latent_seed=seed)
+    streamed = _stream_encode(cfg, K, V, bits, n_inst, N, prefill, chunks, ref_bits=ref_bits,
+                              latent_seed=seed)
     for buf in rkv.Cache.BUFFERS:
         if (bits == 0 and buf == "scales") or (ref_bits == 0 and buf == "ref_scales"):
             continue

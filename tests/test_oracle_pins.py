@@ -402,3 +402,51 @@ def test_encode_with_quantized_refs_uses_the_dequantised_rows():
     kv = oracle.reconstruct(enc, K, V, 4)
     T = enc["T"]
     np.testing.assert_array_equal(kv[T, 0], deq[0].astype(np.float64))
+
+
+def test_splitmix64_published_vectors():
+    assert oracle.splitmix64(0, 3) == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    assert oracle.splitmix64(1234567, 1) == [0x599ED017FB08FC85]
+    sg = oracle.latent_signs(0)
+    assert sg.shape == (128,) and set(np.unique(sg)) == {-1.0, 1.0}
+    assert sg[0] == -1.0 and sg[1] == 1.0 and sg[2] == 1.0   # top bits of the vector above
+
+
+def test_hadamard_and_fwht():
+    Hm = oracle.hadamard(128)
+    np.testing.assert_array_equal(Hm @ Hm, 128 * np.eye(128))
+    e0 = np.zeros(128, np.float32)
+    e0[0] = 1
+    np.testing.assert_array_equal(oracle.fwht_f32(e0), np.ones(128))
+    rng = np.random.default_rng(3)
+    # small integers: every butterfly is exact, so the fast transform equals
+    # the matrix product exactly
+    x = rng.integers(-50, 50, 128).astype(np.float32)
+    np.testing.assert_array_equal(oracle.fwht_f32(x), (Hm @ x.astype(np.float64)).astype(np.float32))
+
+
+def test_latent_pair_inverts():
+    rng = np.random.default_rng(4)
+    sg = oracle.latent_signs(99)
+    x = rng.standard_normal(128).astype(np.float32)
+    y = oracle.latent_fc(x, sg)
+    back = oracle.latent_fd64(y.astype(np.float64), sg)
+    assert np.max(np.abs(back - x)) <= 1e-5 * np.max(np.abs(x))
+    # exact on integer data (no rounding anywhere)
+    xi = rng.integers(-8, 8, 128).astype(np.float32)
+    np.testing.assert_array_equal(oracle.latent_fd64(oracle.latent_fc(xi, sg).astype(np.float64), sg), xi)
+
+
+def test_latent_encode_reconstruct_within_bound():
+    rng = np.random.default_rng(8)
+    K = rng.standard_normal((200, 128)).astype(np.float32)
+    V = rng.standard_normal((200, 128)).astype(np.float32)
+    enc = oracle.encode(K, V, 16, 0, 4, 4, 32, latent_seed=7)
+    kv = oracle.reconstruct(enc, K, V, 4)
+    T = enc["T"]
+    nonref = np.setdiff1d(np.arange(200), T)
+    # error of the rotated codes is <= scale/2 per element; f_d scales norms by 1/sqrt(2)
+    sc = np.repeat(enc["scales"].astype(np.float64), 32, axis=-1)
+    err = kv[nonref, 0] - K[nonref].astype(np.float64)
+    bound = np.linalg.norm(sc[nonref, 0] / 2, axis=-1) * np.sqrt(128) / 8 + 1e-9
+    assert np.all(np.linalg.norm(err, axis=-1) <= bound)
