@@ -323,6 +323,28 @@ def main():
                "note": "QK table + split-K decode + combine of one layer's batch; "
                        "Infinity Cache flushed between repetitions"}
 
+    # latent residuals (codes of f_c(KV - KV_R), fixed seeded rotation): the
+    # same layer's quantise and decode against the plain residual codes
+    latent = None
+    if cfg.decode:
+        cl = rkv.Cache(cfg.batch, H, N, cfg.dtype, cfg.stride_base, cfg.k, bits, cfg.group,
+                       double_after=cfg.double_after, device=dev, latent=1, latent_seed=0x5EED)
+        Kl, Vl = K[: cfg.batch].contiguous(), V[: cfg.batch].contiguous()
+        ws_cl = torch.empty(rkv.rkv_encode_workspace(cl), dtype=torch.uint8, device=dev)
+        rkv.rkv_encode(Kl, Vl, cl, ws=ws_cl)
+        plain = cache.slice(0, cfg.batch)
+        _, qz_l = timed(lambda: rkv.rkv_quantize(Kl, Vl, cl), a.kernel_reps)
+        _, qz_p = timed(lambda: rkv.rkv_quantize(Kl, Vl, plain), a.kernel_reps)
+        ws_ld = torch.empty(rkv.rkv_decode_workspace(cl, cfg.n_q_heads, ns_layer),
+                            dtype=torch.uint8, device=dev)
+        _, dl_mean = timed(lambda: rkv.rkv_decode_attn(q0, cfg.n_q_heads, cl, scale, out=out_l,
+                                                       n_split=ns_layer, ws=ws_ld),
+                           max(a.kernel_reps, 10), flush_between=True)
+        latent = {"quantize_layer_ms": qz_l * 1e3, "quantize_layer_ms_plain": qz_p * 1e3,
+                  "decode_layer_us": dl_mean * 1e6, "decode_layer_us_plain": dmean * 1e6,
+                  "note": "latent=1: 128-point Walsh-Hadamard + seeded signs on the residual "
+                          "before quantising; decode rotates q and the merged output"}
+
     qz_gbps = alg["quantize_bytes"] / qz_mean / 1e9
     sel_tflops = alg["select_flops"] / sel_mean / 1e12
     kernels = {
@@ -387,6 +409,7 @@ def main():
         "decode_attn_sparse": dec_sparse,
         "stream_append": stream_append,
         "full_pipeline_quant": fpq,
+        "latent": latent,
         "kernels": kernels,
         "roofline": roof,
     }
