@@ -17,10 +17,17 @@
 //           tau on the row's k-th smallest distance;
 //   pass 2  recomputes the same MFMA tiles (bit-identical values) and appends
 //           candidates <= tau to a per-lane LDS list (about k per row; a
-//           list near capacity is cut to the lane's own k best);
-//   final   the two lanes of a row load their lists into registers and, with
-//           shuffles, take the k smallest by (distance, slot), lowest slot
-//           first on ties, written in ascending slot order.
+//           list near capacity is cut to the lane's own k best).  The append
+//           is branch-free: every candidate is written at the list's end and
+//           the end advances only for a survivor (a branch per candidate
+//           costs far more than the store, since some lane of the wave almost
+//           always takes it);
+//   final   one lane per token (the wave's 64 lanes hold two 32-token sets,
+//           each token split over lanes n and n + 32; one cross-half swap
+//           regroups them so that lower lanes finish set 0 and upper lanes
+//           set 1) loads the token's two lists and takes the k smallest by
+//           (distance, slot), lowest slot first on ties, written in ascending
+//           slot order.  tau is found the same way.
 #include <float.h>
 
 #include "rkv_common.h"
@@ -31,8 +38,9 @@ namespace rkv {
 // ------------------------------------------------------------------ refstore
 // One wave per new reference (slots s0 .. s0+ns-1 of every (instance,
 // head), at positions inside the input range that starts at p0): copies its
-// K and V rows into the cache's reference store, writes the bf16-rounded key
-// and its squared norm to the workspace.  Input rows are [ih][n_in][128].
+// K and V rows into the cache's reference store, writes -2 x the bf16-rounded
+// key (exact: a power-of-two scaling) and the squared norm of the bf16 key to
+// the workspace.  Input rows are [ih][n_in][128].
 // With ref_bits = 4 the rows are stored quantised (int4 nibbles, fp16 scale
 // per group of `group` dims, the residual quantiser's exact rounding); the
 // workspace keys and norms still come from the original key.
@@ -80,8 +88,8 @@ __global__ __launch_bounds__(256) void k_refstore(
   const __bf16 b0 = (__bf16)(float)kr[t];
   const __bf16 b1 = (__bf16)(float)kr[t + 1];
   const int64_t wr = ih * n_refs + slot;
-  refkey[wr * 128 + t] = b0;
-  refkey[wr * 128 + t + 1] = b1;
+  refkey[wr * 128 + t] = (__bf16)(-2.0f * (float)b0);
+  refkey[wr * 128 + t + 1] = (__bf16)(-2.0f * (float)b1);
   double s = (double)(float)b0 * (double)(float)b0 + (double)(float)b1 * (double)(float)b1;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
@@ -110,20 +118,22 @@ __device__ inline float topk_get(const float (&top)[KM], int k) {
 // Row of accumulator register r of a 32x32 MFMA tile for lane half `half`.
 __device__ inline int acc_row(int r, int half) { return (r & 3) + 8 * (r >> 2) + 4 * half; }
 
-// Survivor list capacity per (lane, token set): the lane's k best plus the 8
-// accumulator rows appended between two fullness checks.
+// Survivor lists: per (lane, token set) entries of two words, the distance
+// (fp32 bits) and the slot, laid out [entry][word][64 lanes] so that one
+// entry is a single two-address LDS store.  Capacity: the lane's k best plus
+// the kCheckRows accumulator rows appended between two fullness checks.
+constexpr int kCheckRows = 4;
 template <int KM>
-constexpr int surv_cap() { return KM + 8; }
+constexpr int surv_cap() { return KM + kCheckRows; }
+constexpr int kEntryWords = 128;  // stride of one list entry, in 32-bit words
 
-// Loads a lane's survivor list (stride 64 entries in LDS) into registers;
-// entries past cnt read as +inf.
+// Loads a lane's survivor list into registers; entries past cnt read as +inf.
 template <int CAP>
-__device__ inline void load_list(const float* be, const uint16_t* bj, int cnt, float (&e)[CAP],
-                                 float (&js)[CAP]) {
+__device__ inline void load_list(const uint32_t* bl, int cnt, float (&e)[CAP], float (&js)[CAP]) {
 #pragma unroll
   for (int c = 0; c < CAP; ++c) {
-    const float v = be[c * 64];
-    const uint16_t j = bj[c * 64];
+    const float v = __uint_as_float(bl[c * kEntryWords]);
+    const uint32_t j = bl[c * kEntryWords + 64];
     e[c] = c < cnt ? v : INFINITY;
     js[c] = (float)j;
   }
@@ -134,10 +144,10 @@ __device__ inline void load_list(const float* be, const uint16_t* bj, int cnt, f
 // k-th value: an entry dropped here is beaten by k kept ones, and every later
 // entry has a higher slot.
 template <int KM, int CAP>
-__device__ __forceinline__ void lane_compact(float* be, uint16_t* bj, int& cnt, float& tau, int k) {
+__device__ __forceinline__ void lane_compact(uint32_t* bl, int& cnt, float& tau, int k) {
   if (cnt <= k) return;
   float e[CAP], js[CAP];
-  load_list<CAP>(be, bj, cnt, e, js);
+  load_list<CAP>(bl, cnt, e, js);
   float top[KM];
 #pragma unroll
   for (int t = 0; t < KM; ++t) top[t] = INFINITY;
@@ -155,8 +165,8 @@ __device__ __forceinline__ void lane_compact(float* be, uint16_t* bj, int& cnt, 
     const bool take = e[c] < t || (tie && ties < quota);
     ties += tie;
     if (take) {
-      be[out * 64] = e[c];
-      bj[out * 64] = (uint16_t)js[c];
+      bl[out * kEntryWords] = __float_as_uint(e[c]);
+      bl[out * kEntryWords + 64] = (uint32_t)js[c];
       ++out;
     }
   }
@@ -164,62 +174,73 @@ __device__ __forceinline__ void lane_compact(float* be, uint16_t* bj, int& cnt, 
   tau = fminf(tau, t);
 }
 
-// The keff nearest references of one token from the survivor lists of its
-// two lanes (this lane and lane ^ 32, both calling), lowest slot first among
-// equal distances; returns them in ascending slot order, 65535 past keff.
+// The keff nearest references of one token from its two survivor lists
+// (la: cnt_a entries, lb: cnt_b entries), lowest slot first among equal
+// distances; returns them in ascending slot order, 65535 past keff.
 template <int KM, int CAP>
-__device__ __forceinline__ void row_select(const float* be, const uint16_t* bj, int cnt, int keff,
-                           float (&sel)[KM]) {
-  float e[CAP], js[CAP];
-  load_list<CAP>(be, bj, cnt, e, js);
+__device__ __forceinline__ void token_select(const uint32_t* la, int cnt_a, const uint32_t* lb,
+                                             int cnt_b, int keff, float (&sel)[KM]) {
+  float ea[CAP], ja[CAP], eb[CAP], jb[CAP];
+  load_list<CAP>(la, cnt_a, ea, ja);
+  load_list<CAP>(lb, cnt_b, eb, jb);
   float top[KM];
 #pragma unroll
   for (int t = 0; t < KM; ++t) top[t] = INFINITY;
 #pragma unroll
-  for (int c = 0; c < CAP; ++c) topk_insert(top, e[c]);
-  float mine[KM];
-#pragma unroll
-  for (int t = 0; t < KM; ++t) mine[t] = top[t];
-#pragma unroll
-  for (int t = 0; t < KM; ++t) topk_insert(top, __shfl_xor(mine[t], 32));
+  for (int c = 0; c < CAP; ++c) {
+    topk_insert(top, ea[c]);
+    topk_insert(top, eb[c]);
+  }
   const float th = topk_get(top, keff);
   int nless = 0, nties = 0;
 #pragma unroll
   for (int c = 0; c < CAP; ++c) {
-    nless += e[c] < th;
-    nties += e[c] == th;
+    nless += (ea[c] < th) + (eb[c] < th);
+    nties += (ea[c] == th) + (eb[c] == th);
   }
-  nless += __shfl_xor(nless, 32);
-  const int all_ties = nties + __shfl_xor(nties, 32);
   const int quota = keff - nless;  // >= 1: th is the keff-th smallest
   float slot_bound = 65536.f;      // ties at th are taken up to this slot
-  if (__any(all_ties > quota)) {
+  if (nties > quota) {
     float tl[KM];
 #pragma unroll
     for (int t = 0; t < KM; ++t) tl[t] = 65536.f;
 #pragma unroll
-    for (int c = 0; c < CAP; ++c) topk_insert(tl, e[c] == th ? js[c] : 65536.f);
-#pragma unroll
-    for (int t = 0; t < KM; ++t) mine[t] = tl[t];
-#pragma unroll
-    for (int t = 0; t < KM; ++t) topk_insert(tl, __shfl_xor(mine[t], 32));
+    for (int c = 0; c < CAP; ++c) {
+      topk_insert(tl, ea[c] == th ? ja[c] : 65536.f);
+      topk_insert(tl, eb[c] == th ? jb[c] : 65536.f);
+    }
     slot_bound = topk_get(tl, quota);
   }
 #pragma unroll
   for (int t = 0; t < KM; ++t) sel[t] = 65535.f;
 #pragma unroll
   for (int c = 0; c < CAP; ++c) {
-    const bool take = e[c] < th || (e[c] == th && js[c] <= slot_bound);
-    topk_insert(sel, take ? js[c] : 65535.f);
+    const bool ta = ea[c] < th || (ea[c] == th && ja[c] <= slot_bound);
+    const bool tb = eb[c] < th || (eb[c] == th && jb[c] <= slot_bound);
+    topk_insert(sel, ta ? ja[c] : 65535.f);
+    topk_insert(sel, tb ? jb[c] : 65535.f);
   }
-#pragma unroll
-  for (int t = 0; t < KM; ++t) mine[t] = sel[t];
-#pragma unroll
-  for (int t = 0; t < KM; ++t) topk_insert(sel, __shfl_xor(mine[t], 32));
 }
 
-template <typename T>
-__device__ inline bf16x8 load_key_frag(const T* p, bool valid) {
+// Exchange between the two lane halves: returns {x of lanes 0-31 | y of
+// lanes 0-31} in .a and {x of lanes 32-63 | y of lanes 32-63} in .b, i.e.
+// lane l < 32 gets (x[l], x[l + 32]) and lane l >= 32 gets (y[l - 32], y[l]).
+struct HalfPair {
+  uint32_t a, b;
+};
+__device__ inline HalfPair half_swap(uint32_t x, uint32_t y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  return HalfPair{r[0], r[1]};
+}
+
+// 8 consecutive key elements as a bf16 B fragment (zeros for an invalid row):
+// bf16 input as is, fp32 input rounded to nearest even.
+__device__ inline bf16x8 load_key_frag(const __bf16* p, bool valid) {
+  const uint4 w = valid ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ inline bf16x8 load_key_frag(const float* p, bool valid) {
   float x[8];
   if (valid) {
     load8(p, x);
@@ -229,10 +250,7 @@ __device__ inline bf16x8 load_key_frag(const T* p, bool valid) {
   }
   bf16x8 b;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float r = (float)(__bf16)x[e];  // RNE to bf16 (identity for bf16 input)
-    b[e] = (__bf16)(-2.0f * r);           // exact
-  }
+  for (int e = 0; e < 8; ++e) b[e] = (__bf16)x[e];
   return b;
 }
 
@@ -254,8 +272,7 @@ __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
   // positions [p0, p1) from input rows [ih][n_in][128]; idx rows at ih * N + position
   const int64_t p1 = p0 + n_in;
   constexpr int CAP = surv_cap<KM>();
-  __shared__ float sb_e[4][kSets][CAP][64];
-  __shared__ uint16_t sb_j[4][kSets][CAP][64];
+  __shared__ uint32_t sbl[4][kSets][CAP][2][64];
   __shared__ __attribute__((aligned(16))) __bf16 kbuf[2][32][kRowPad];
   __shared__ __attribute__((aligned(16))) float nbuf[2][32];
   const int tid = threadIdx.x;
@@ -275,7 +292,8 @@ __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
   const int full_tiles = active ? (int)(sched_count_le((int32_t)row0, sc) / 32) : 0;
   bool valid_row[kSets];
   int my_last[kSets];
-  // B operands: -2 * bf16(key) of token row0 + 32c + n, dims 16s + 8*half + [0,8).
+  // B operands: bf16(key) of token row0 + 32c + n, dims 16s + 8*half + [0,8);
+  // the A operands (staged reference keys) carry the factor -2.
   bf16x8 bfrag[kSets][8];
 #pragma unroll
   for (int c = 0; c < kSets; ++c) {
@@ -289,31 +307,30 @@ __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
   const __bf16* rk = refkey + ih * n_refs * 128;
   const float* rn = refnorm + ih * n_refs;
 
-  // cooperative staging: 512 chunks of 16 B per tile, 2 per thread
-  auto gload = [&](int rt, uint4 (&v)[2], float& nv) {
+  // cooperative staging: 512 chunks of 16 B per tile, 2 per thread.  Slots
+  // past the last reference read the last one instead: every score of such
+  // a slot is masked (it lies beyond every token's last candidate).
+  const uint32_t last_slot = (uint32_t)(n_refs - 1);
+  auto gload = [&](int rt, u32x4 (&v)[2], float& nv) RKV_INLINE {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int chunk = tid + 256 * c;
-      const int64_t slot = (int64_t)rt * 32 + (chunk >> 4);
-      v[c] = slot < n_refs ? *reinterpret_cast<const uint4*>(rk + slot * 128 + (chunk & 15) * 8)
-                           : make_uint4(0, 0, 0, 0);
+      const uint32_t slot = min((uint32_t)rt * 32 + (uint32_t)(chunk >> 4), last_slot);
+      v[c] = *reinterpret_cast<const u32x4*>(rk + slot * 128 + (chunk & 15) * 8);
     }
-    if (tid < 32) {
-      const int64_t slot = (int64_t)rt * 32 + tid;
-      nv = slot < n_refs ? rn[slot] : 0.f;
-    }
+    nv = rn[min((uint32_t)rt * 32 + (uint32_t)(tid & 31), last_slot)];
   };
-  auto lstore = [&](int b, const uint4 (&v)[2], float nv) {
+  auto lstore = [&](int b, const u32x4 (&v)[2], float nv) RKV_INLINE {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int chunk = tid + 256 * c;
-      *reinterpret_cast<uint4*>(&kbuf[b][chunk >> 4][(chunk & 15) * 8]) = v[c];
+      *reinterpret_cast<u32x4*>(&kbuf[b][chunk >> 4][(chunk & 15) * 8]) = v[c];
     }
     if (tid < 32) nbuf[b][tid] = nv;
   };
   // acc[c][r]: e = |ref|^2 - 2 k.ref of candidate slot rt*32 + acc_row(r, half)
   // for token row0 + 32c + n; +inf past the token's last candidate.
-  auto tile_scores = [&](int rt, int b, f32x16 (&acc)[kSets]) {
+  auto tile_scores = [&](int rt, int b, f32x16 (&acc)[kSets]) RKV_INLINE {
     f32x16 init;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
@@ -323,10 +340,14 @@ __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
       init[4 * q4 + 2] = nn.z;
       init[4 * q4 + 3] = nn.w;
     }
+    {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kbuf[b][n][8 * half]);
 #pragma unroll
-    for (int c = 0; c < kSets; ++c) acc[c] = init;
+      for (int c = 0; c < kSets; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[c][0], init, 0, 0, 0);
+    }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 1; s < 8; ++s) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kbuf[b][n][16 * s + 8 * half]);
 #pragma unroll
       for (int c = 0; c < kSets; ++c)
@@ -349,27 +370,30 @@ __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
   // ahead: tile rt + 2 is requested while tile rt is scored, and tile rt + 1
   // (requested one iteration earlier) is written to the free LDS buffer
   // after it.  The loop is unrolled by two so the two register sets of tiles
-  // in flight alternate without copies.
-  auto stream = [&](auto&& epi) {
-    uint4 pa[2], pb[2];
-    float na = 0.f, nb = 0.f;
+  // in flight alternate without copies.  Loads and stores are unconditional
+  // (tiles past the block's last read clamped slots and are never scored):
+  // with no branch around them the load counter waits only for the older
+  // tile, and the newer load stays in flight across the scoring.
+  auto stream = [&](auto&& epi) RKV_INLINE {
+    u32x4 pa[2], pb[2];
+    float na, nb;
     gload(0, pa, na);
     lstore(0, pa, na);
-    if (ntile_blk > 1) gload(1, pb, nb);
+    gload(1, pb, nb);
     __syncthreads();
-    auto step = [&](int rt, uint4 (&st)[2], float& sn, uint4 (&ld)[2], float& ln) {
-      if (rt + 2 < ntile_blk) gload(rt + 2, ld, ln);
+    auto step = [&](int rt, u32x4 (&st)[2], float& sn, u32x4 (&ld)[2], float& ln) RKV_INLINE {
+      gload(rt + 2, ld, ln);
       if (rt < ntile) {
         f32x16 acc[kSets];
         tile_scores(rt, rt & 1, acc);
         epi(rt, acc);
       }
-      if (rt + 1 < ntile_blk) lstore((rt + 1) & 1, st, sn);
+      lstore((rt + 1) & 1, st, sn);
       __syncthreads();
     };
     for (int rt = 0; rt < ntile_blk; rt += 2) {
       step(rt, pb, nb, pa, na);
-      if (rt + 1 < ntile_blk) step(rt + 1, pa, na, pb, nb);
+      step(rt + 1, pa, na, pb, nb);
     }
   };
 
@@ -379,68 +403,78 @@ __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
   for (int c = 0; c < kSets; ++c)
 #pragma unroll
     for (int r = 0; r < 16; ++r) bk[c][r] = INFINITY;
-  stream([&](int, const f32x16 (&acc)[kSets]) {
+  stream([&](int, const f32x16 (&acc)[kSets]) RKV_INLINE {
 #pragma unroll
     for (int c = 0; c < kSets; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) bk[c][r] = fminf(bk[c][r], acc[c][r]);
   });
+  // one token per lane: lower lanes take set 0, upper lanes set 1, each with
+  // the 16 bucket minima of both of its lanes
+  static_assert(kSets == 2, "the half swap pairs two token sets");
   float tau[kSets];
-#pragma unroll
-  for (int c = 0; c < kSets; ++c) {
+  {
     float top[KM];
 #pragma unroll
     for (int t = 0; t < KM; ++t) top[t] = INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      topk_insert(top, bk[c][r]);
-      topk_insert(top, __shfl_xor(bk[c][r], 32));
+      const HalfPair m = half_swap(__float_as_uint(bk[0][r]), __float_as_uint(bk[1][r]));
+      topk_insert(top, __uint_as_float(m.a));
+      topk_insert(top, __uint_as_float(m.b));
     }
-    tau[c] = topk_get(top, k);
-    if (!(tau[c] < INFINITY)) tau[c] = FLT_MAX;
+    float t = topk_get(top, k);
+    if (!(t < INFINITY)) t = FLT_MAX;
+    // back to every lane: tau of set 0 from the lower lane, set 1 from the upper
+    const HalfPair tt = half_swap(__float_as_uint(t), __float_as_uint(t));
+    tau[0] = __uint_as_float(tt.a);
+    tau[1] = __uint_as_float(tt.b);
   }
 
   // ---- pass 2: collect candidates <= tau
   int cnt[kSets];
 #pragma unroll
   for (int c = 0; c < kSets; ++c) cnt[c] = 0;
-  stream([&](int rt, const f32x16 (&acc)[kSets]) {
-    const int r0 = rt * 32;
+  stream([&](int rt, const f32x16 (&acc)[kSets]) RKV_INLINE {
+    const uint32_t r0 = (uint32_t)rt * 32 + 4 * half;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 16 / kCheckRows; ++h) {
 #pragma unroll
       for (int c = 0; c < kSets; ++c) {
-        float* be = &sb_e[w][c][0][lane];
-        uint16_t* bj = &sb_j[w][c][0][lane];
+        uint32_t* bl = &sbl[w][c][0][0][lane];
 #pragma unroll
-        for (int r = 8 * h; r < 8 * h + 8; ++r) {
-          if (acc[c][r] <= tau[c]) {
-            be[cnt[c] * 64] = acc[c][r];
-            bj[cnt[c] * 64] = (uint16_t)(r0 + acc_row(r, half));
-            ++cnt[c];
-          }
+        for (int r = kCheckRows * h; r < kCheckRows * h + kCheckRows; ++r) {
+          // cnt <= CAP - 1 here: at most kCheckRows - 1 appends since the
+          // last check left cnt <= CAP - kCheckRows
+          uint32_t* at = bl + cnt[c] * kEntryWords;
+          at[0] = __float_as_uint(acc[c][r]);
+          at[64] = r0 + (uint32_t)acc_row(r, 0);
+          cnt[c] += acc[c][r] <= tau[c] ? 1 : 0;
         }
       }
       bool full = false;
 #pragma unroll
-      for (int c = 0; c < kSets; ++c) full |= cnt[c] > CAP - 8;
+      for (int c = 0; c < kSets; ++c) full |= cnt[c] > CAP - kCheckRows;
       if (__any(full)) {
 #pragma unroll
         for (int c = 0; c < kSets; ++c)
-          lane_compact<KM, CAP>(&sb_e[w][c][0][lane], &sb_j[w][c][0][lane], cnt[c], tau[c], k);
+          lane_compact<KM, CAP>(&sbl[w][c][0][0][lane], cnt[c], tau[c], k);
       }
     }
   });
   if (!active) return;
 
-  // ---- final: each token's keff nearest from its two lanes' lists
-#pragma unroll
-  for (int c = 0; c < kSets; ++c) {
-    const int keff = (my_last[c] + 1 < k) ? my_last[c] + 1 : k;
+  // ---- final: one token per lane (set `half`, column n) from the lists of
+  //      lanes n and n + 32 of that set
+  {
+    const HalfPair cp = half_swap((uint32_t)cnt[0], (uint32_t)cnt[1]);
+    const int c = half;
+    const int last = c ? my_last[1] : my_last[0];
+    const int keff = (last + 1 < k) ? last + 1 : k;
     float sel[KM];
-    row_select<KM, CAP>(&sb_e[w][c][0][lane], &sb_j[w][c][0][lane], cnt[c],
-                        keff < 1 ? 1 : keff, sel);
-    if (half == 0 && valid_row[c]) {
+    token_select<KM, CAP>(&sbl[w][c][0][0][n], (int)cp.a, &sbl[w][c][0][0][n + 32], (int)cp.b,
+                          keff < 1 ? 1 : keff, sel);
+    if (c ? valid_row[1] : valid_row[0]) {
       uint16_t* orow = idx_out + (ih * N + row0 + 32 * c + n) * k;
 #pragma unroll
       for (int t = 0; t < KM; ++t)

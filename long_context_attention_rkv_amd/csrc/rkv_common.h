@@ -13,6 +13,10 @@
 
 namespace rkv {
 
+// Lambdas that take register arrays by reference must be inlined, or the
+// arrays are placed in scratch or LDS memory.
+#define RKV_INLINE __attribute__((always_inline))
+
 // Division by a constant d >= 1 for 0 <= n < 2^31 with one 32x32->64
 // multiply: l = ceil(log2 d), m = floor(2^(31+l)/d) + 1, n/d = (n*m) >> (31+l)
 // (Granlund-Montgomery: m*d lies in (2^(31+l), 2^(31+l) + 2^l]).
@@ -224,5 +228,6 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 }  // namespace rkv
