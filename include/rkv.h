@@ -64,6 +64,12 @@ typedef struct {
   int64_t double_after;
 } rkv_stride;
 
+/* Alignment: every device buffer handed to the library (K, V, q, outputs,
+ * workspaces, codes_k, codes_v, ref_kv) must be 16-byte aligned; ref_idx
+ * must be aligned to 2k bytes when k is 4, 8 or 16 (16 at most), scales to
+ * 4 and ref_scales to 2.  Any allocation from hipMalloc or torch satisfies
+ * this.  Misaligned buffers give RKV_ERR_INVALID_ARG. */
+
 /* Shape of a compressed cache and its device buffers (all caller-owned).
  *
  *   ref_idx  uint16 [inst][H][N][k]     slots (rank in the reference list) of

@@ -305,16 +305,28 @@ __global__ __launch_bounds__(256, 2) void k_decode(
   //      (q . f_d(y) = (H D q / 8) . y).
   f16x8 aq[4];
   {
+    // the lane's 32 query values are 4 runs of 8 dims (32*quad + 8*s): load
+    // them whole (one branch for the source), then permute and mask to the
+    // lane's scale group
     const int h = n / NG, g = n % NG;
-    const float* qr = qrot ? qrot + (inst * Hq + kvh * G) * 128 : nullptr;
+    const bool live = h < G;
+    const int hr = live ? h : 0;
+    float qv[4][8];
+    if (qrot) {
+      const float* qr = qrot + ((inst * Hq + kvh * G) + hr) * 128 + 32 * quad;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) load8(qr + 8 * s, qv[s]);
+    } else {
+      const T* qq = qh + hr * 128 + 32 * quad;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) load8(qq + 8 * s, qv[s]);
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int dim = 32 * quad + 8 * s + perm_of<BITS>(e);
-        float v = 0.f;
-        if (h < G && dim / GS == g) v = qr ? qr[h * 128 + dim] : (float)qh[h * 128 + dim];
-        aq[s][e] = (_Float16)v;
+        aq[s][e] = (_Float16)((live && dim / GS == g) ? qv[s][perm_of<BITS>(e)] : 0.f);
       }
     }
   }

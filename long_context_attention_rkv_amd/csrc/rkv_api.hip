@@ -68,6 +68,11 @@ rkv_status hip_status(hipError_t e) {
 
 size_t elt_bytes(rkv_dtype d) { return d == RKV_F32 ? 4 : 2; }
 
+// The kernels read rows with 16-byte (index rows: 2k-byte, at most 16)
+// vector loads; misaligned buffers are rejected up front.
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+inline bool al16(const void* p) { return aligned(p, 16); }
+
 rkv_status check_shape(const rkv_cache* c) {
   if (!c) return RKV_ERR_INVALID_ARG;
   if (c->dtype != RKV_F32 && c->dtype != RKV_BF16) return RKV_ERR_INVALID_ARG;
@@ -98,6 +103,10 @@ rkv_status check_ready(const rkv_cache* c) {
   if (!c->ref_idx || !c->codes_k || !c->codes_v || !c->ref_kv) return RKV_ERR_INVALID_ARG;
   if (c->bits != 0 && !c->scales) return RKV_ERR_INVALID_ARG;
   if (c->ref_bits != 0 && !c->ref_scales) return RKV_ERR_INVALID_ARG;
+  const uintptr_t idx_align = (c->k & (c->k - 1)) == 0 ? (c->k >= 8 ? 16 : 2 * c->k) : 2;
+  if (!al16(c->codes_k) || !al16(c->codes_v) || !al16(c->ref_kv) ||
+      !aligned(c->ref_idx, idx_align) || !aligned(c->scales, 4) || !aligned(c->ref_scales, 2))
+    return RKV_ERR_INVALID_ARG;
   return RKV_OK;
 }
 
@@ -182,6 +191,7 @@ static rkv_status select_range(const void* K, const void* V, const rkv_cache* c,
                                int64_t n_in, void* ws, size_t ws_bytes, hipStream_t st) {
   const size_t need = encode_ws(c);
   if (!ws || ws_bytes < need) return RKV_ERR_WORKSPACE;
+  if (!al16(ws)) return RKV_ERR_INVALID_ARG;
   const size_t nr = (size_t)c->n_inst * c->n_kv_heads * c->n_refs;
   char* refkey = (char*)ws;
   float* refnorm = (float*)((char*)ws + align_up(nr * 128 * 2));
@@ -211,7 +221,7 @@ rkv_status rkv_select_refs(const void* K, const void* V, const rkv_cache* c, voi
   rkv_status s = check_ready(c);
   if (s != RKV_OK) return s;
   if (c->n_inst == 0 || c->seq_len == 0) return RKV_OK;
-  if (!K || !V) return RKV_ERR_INVALID_ARG;
+  if (!K || !V || !al16(K) || !al16(V)) return RKV_ERR_INVALID_ARG;
   return select_range(K, V, c, 0, c->seq_len, ws, ws_bytes, (hipStream_t)stream);
 }
 
@@ -222,7 +232,7 @@ rkv_status rkv_quantize(const void* K, const void* V, const rkv_cache* c, void* 
   rkv_status s = check_ready(c);
   if (s != RKV_OK) return s;
   if (c->n_inst == 0 || c->seq_len == 0) return RKV_OK;
-  if (!K || !V) return RKV_ERR_INVALID_ARG;
+  if (!K || !V || !al16(K) || !al16(V)) return RKV_ERR_INVALID_ARG;
   return quantize_range(K, V, c, 0, c->seq_len, (hipStream_t)stream);
 }
 
@@ -239,7 +249,7 @@ rkv_status rkv_append(const void* K_new, const void* V_new, int64_t n_new, const
   if (s != RKV_OK) return s;
   if (n_new < 1 || pos0 < 0 || pos0 + n_new > c->seq_len) return RKV_ERR_INVALID_ARG;
   if (c->n_inst == 0) return RKV_OK;
-  if (!K_new || !V_new) return RKV_ERR_INVALID_ARG;
+  if (!K_new || !V_new || !al16(K_new) || !al16(V_new)) return RKV_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
   s = select_range(K_new, V_new, c, pos0, n_new, ws, ws_bytes, st);
   if (s != RKV_OK) return s;
@@ -250,7 +260,7 @@ rkv_status rkv_reconstruct(const rkv_cache* c, float* K_hat, float* V_hat, void*
   rkv_status s = check_ready(c);
   if (s != RKV_OK) return s;
   if (c->n_inst == 0 || c->seq_len == 0) return RKV_OK;
-  if (!K_hat || !V_hat) return RKV_ERR_INVALID_ARG;
+  if (!K_hat || !V_hat || !al16(K_hat) || !al16(V_hat)) return RKV_ERR_INVALID_ARG;
   const LatArg lat(c);
   hipError_t e = rkv::launch_reconstruct((int)c->dtype, c->bits, c->ref_idx, c->ref_kv,
                                          c->ref_scales, c->ref_bits,
@@ -288,11 +298,12 @@ static rkv_status decode_common(const void* q, int32_t n_q_heads, const rkv_cach
   if (G * (c->head_dim / c->group) > 16) return RKV_ERR_UNSUPPORTED;
   if (!rkv::decode_fits(G, c->group, c->n_refs, n_split)) return RKV_ERR_UNSUPPORTED;
   if (c->n_inst == 0) return RKV_OK;
-  if (!q || !out) return RKV_ERR_INVALID_ARG;
+  if (!q || !out || !al16(q) || !al16(out)) return RKV_ERR_INVALID_ARG;
   if (c->seq_len == 0) return RKV_ERR_INVALID_ARG;
   const size_t need = rkv::decode_ws_bytes(c->n_inst, c->n_kv_heads, n_q_heads, n_split, c->n_refs,
                                            c->latent != 0);
   if (!ws || ws_bytes < need) return RKV_ERR_WORKSPACE;
+  if (!al16(ws)) return RKV_ERR_INVALID_ARG;
   const LatArg lat(c);
   hipError_t e = rkv::launch_decode((int)c->dtype, c->bits, q, n_q_heads, c->ref_idx, c->ref_kv,
                                     c->ref_scales, c->ref_bits,

@@ -204,3 +204,35 @@ def test_latent_decode_workspace_holds_two_rows_per_query_head(lib):
     c.latent = 1
     lib.rkv_cache_sizes(C.byref(c), sz_l)
     assert list(sz_p) == list(sz_l)
+
+
+def test_misaligned_buffers_are_rejected(lib):
+    c = _cache()
+    assert lib.rkv_cache_init(C.byref(c)) == L.RKV_OK
+    for name in ("ref_idx", "codes_k", "codes_v", "scales", "ref_kv"):
+        setattr(c, name, 0x10000)
+    null = C.c_void_p(0)
+    ws = C.c_void_p(0x40000)
+    big = 1 << 40
+    K, V = C.c_void_p(0x20000), C.c_void_p(0x30000)
+    # aligned pointers pass validation up to the workspace check
+    assert lib.rkv_select_refs(K, V, C.byref(c), ws, 16, null) == L.RKV_ERR_WORKSPACE
+    # K, V, workspace off by 8 bytes
+    assert lib.rkv_select_refs(C.c_void_p(0x20008), V, C.byref(c), ws, big, null) == L.RKV_ERR_INVALID_ARG
+    assert lib.rkv_quantize(K, C.c_void_p(0x30008), C.byref(c), ws, big, null) == L.RKV_ERR_INVALID_ARG
+    assert lib.rkv_select_refs(K, V, C.byref(c), C.c_void_p(0x40008), big, null) == L.RKV_ERR_INVALID_ARG
+    assert lib.rkv_append(C.c_void_p(0x20004), V, 1, C.byref(c), 5, ws, big, null) == L.RKV_ERR_INVALID_ARG
+    # a cache buffer off by 8 bytes
+    for name in ("codes_k", "codes_v", "ref_kv", "ref_idx"):
+        setattr(c, name, 0x10008)
+        assert lib.rkv_quantize(K, V, C.byref(c), ws, big, null) == L.RKV_ERR_INVALID_ARG, name
+        setattr(c, name, 0x10000)
+    # decode: q and out
+    out = C.c_void_p(0x50000)
+    assert lib.rkv_decode_attn(C.c_void_p(0x60004), 32, C.byref(c), 0.1, out, 4, ws, big,
+                               null) == L.RKV_ERR_INVALID_ARG
+    assert lib.rkv_decode_attn(C.c_void_p(0x60000), 32, C.byref(c), 0.1, C.c_void_p(0x50004), 4,
+                               ws, big, null) == L.RKV_ERR_INVALID_ARG
+    # reconstruct outputs
+    assert lib.rkv_reconstruct(C.byref(c), C.c_void_p(0x70002), C.c_void_p(0x80000),
+                               null) == L.RKV_ERR_INVALID_ARG
