@@ -197,7 +197,7 @@ def main():
     ws_enc = torch.empty(max(1, rkv.rkv_encode_workspace(cache)), dtype=torch.uint8,
                          device=dev)
     scale = 1.0 / math.sqrt(D)
-    ns_all = max(1, min((N + 31) // 32, 512 // max(1, n_inst * H)))
+    ns_all = rkv.rkv_decode_split_hint(cache, cfg.n_q_heads)
     ws_dec = torch.empty(rkv.rkv_decode_workspace(cache, cfg.n_q_heads, ns_all),
                          dtype=torch.uint8, device=dev)
     out = torch.empty(n_inst, cfg.n_q_heads, D, dtype=torch.float32, device=dev)
@@ -260,7 +260,7 @@ def main():
         Kl, Vl = K[: cfg.batch].contiguous(), V[: cfg.batch].contiguous()
         ws_q = torch.empty(rkv.rkv_encode_workspace(cq), dtype=torch.uint8, device=dev)
         em, emean = timed(lambda: rkv.rkv_encode(Kl, Vl, cq, ws=ws_q), a.kernel_reps)
-        ns_q = max(1, min((N + 31) // 32, 512 // (cfg.batch * H)))
+        ns_q = rkv.rkv_decode_split_hint(cq, cfg.n_q_heads)
         ws_qd = torch.empty(rkv.rkv_decode_workspace(cq, cfg.n_q_heads, ns_q), dtype=torch.uint8,
                             device=dev)
         out_q = torch.empty(cfg.batch, cfg.n_q_heads, D, dtype=torch.float32, device=dev)
@@ -287,7 +287,7 @@ def main():
     if cfg.decode:
         layer0 = cache.slice(0, cfg.batch)
         q0 = q[: cfg.batch].contiguous()
-        ns_layer = max(1, min((N + 31) // 32, 512 // (cfg.batch * H)))
+        ns_layer = rkv.rkv_decode_split_hint(layer0, cfg.n_q_heads)
         ws_l = torch.empty(rkv.rkv_decode_workspace(layer0, cfg.n_q_heads, ns_layer),
                            dtype=torch.uint8, device=dev)
         out_l = torch.empty(cfg.batch, cfg.n_q_heads, D, dtype=torch.float32, device=dev)

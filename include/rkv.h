@@ -215,6 +215,12 @@ rkv_status rkv_reconstruct(const rkv_cache *c, float *K_hat, float *V_hat,
 rkv_status rkv_decode_workspace(const rkv_cache *c, int32_t n_q_heads,
                                 int32_t n_split, size_t *bytes);
 
+/* A split count for rkv_decode_attn* on the current device: about three
+ * decode blocks per compute unit over all (instance, KV head) pairs, at
+ * least 1, at most ceil(seq_len / 32) and 4096.  Host-only (queries the
+ * device's CU count); the result is a hint, any n_split >= 1 is valid. */
+rkv_status rkv_decode_split_hint(const rkv_cache *c, int32_t n_q_heads, int32_t *n_split);
+
 /* Decode attention straight from the compressed cache: one query per
  * instance, q dtype [inst][n_q_heads][D]; query head h reads KV head
  * h / (n_q_heads / H).  out float [inst][n_q_heads][D] =

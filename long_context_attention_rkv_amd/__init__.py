@@ -226,6 +226,13 @@ def rkv_reconstruct(cache: Cache, K_hat=None, V_hat=None, stream=None):
     return K_hat, V_hat
 
 
+def rkv_decode_split_hint(cache: Cache, n_q_heads: int) -> int:
+    n = C.c_int32()
+    _check(_load().rkv_decode_split_hint(C.byref(cache.c), int(n_q_heads), C.byref(n)),
+           "rkv_decode_split_hint")
+    return int(n.value)
+
+
 def rkv_decode_attn(q, n_q_heads: int, cache: Cache, softmax_scale: float, out=None,
                     n_split: int = 1, ws=None, stream=None):
     c = cache.c

@@ -61,6 +61,7 @@ SIGNATURES = {
     "rkv_reconstruct": (C.c_int, [C.POINTER(RkvCache), C.c_void_p, C.c_void_p, C.c_void_p]),
     "rkv_decode_workspace": (C.c_int, [C.POINTER(RkvCache), C.c_int32, C.c_int32,
                                        C.POINTER(C.c_size_t)]),
+    "rkv_decode_split_hint": (C.c_int, [C.POINTER(RkvCache), C.c_int32, C.POINTER(C.c_int32)]),
     "rkv_decode_attn": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(RkvCache), C.c_float,
                                   C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]),
     "rkv_decode_attn_tiles": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(RkvCache), C.c_float,

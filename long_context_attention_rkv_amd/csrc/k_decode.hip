@@ -334,8 +334,10 @@ __global__ __launch_bounds__(256, 2) void k_decode(
 
   _Float16* pst = pst_all + w * 16 * kDecTile;
   _Float16* sst = sst_all + w * NG * kDecTile;
-  const uint8_t* ck = codes_k + ih * N * (16 * BITS) + n * (16 * BITS) + quad * (4 * BITS);
-  const uint16_t* sc16 = scales + ih * N * 2 * NG + n * 2 * NG;
+  // per-row bases: K codes of row t at ck0 + t * 16*BITS (this lane's 32
+  // dims), scales at sc0 + t * 2*NG
+  const uint8_t* ck0 = codes_k + ih * N * (16 * BITS) + quad * (4 * BITS);
+  const uint16_t* sc0 = scales + ih * N * 2 * NG;
   const uint16_t* ix = idx + ih * N * k;
   const uint8_t* cv = codes_v + ih * tiles * 128 * (4 * BITS) + n * (4 * BITS) + quad * BITS;
   const int h0 = quad * HPL;
@@ -347,7 +349,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(
 #pragma unroll
   for (int b = 0; b < 8; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto load_slots_of = [&](int32_t tok, uint32_t (&iw)[KM / 2]) {
+  auto load_slots_of = [&](int32_t tok, uint32_t (&iw)[KM / 2]) RKV_INLINE {
     if constexpr (EX) {
       load_words<KM / 2>(ix + (uint32_t)tok * KM, iw);
     } else {
@@ -371,26 +373,21 @@ __global__ __launch_bounds__(256, 2) void k_decode(
     uint32_t sw[2][NG];
     uint32_t iw[2][KM / 2];
   };
-  auto loadA = [&](int32_t t, ARegs& r) {
+  // Loads are unconditional: a position at or past the attended length reads
+  // the last attended row instead (its logit is -inf and its p is 0, so the
+  // values never count).  With no branch around them the load counter waits
+  // only for the tile being used, and the next tile's loads stay in flight.
+  auto loadA = [&](int32_t t, ARegs& r) RKV_INLINE {
     const int32_t tb = tile_of(t) * kDecTile;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int32_t tok = tb + 16 * b + n;
-      if (tok < N32) {
-        load_words<BITS>(ck + (uint32_t)(tb + 16 * b) * (16 * BITS), r.kw[b]);
-        load_words<NG>(sc16 + (uint32_t)(tb + 16 * b) * (2 * NG), r.sw[b]);
-        load_slots_of(tok, r.iw[b]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < BITS; ++j) r.kw[b][j] = 0;
-#pragma unroll
-        for (int j = 0; j < NG; ++j) r.sw[b][j] = 0;
-#pragma unroll
-        for (int j = 0; j < KM / 2; ++j) r.iw[b][j] = 0;
-      }
+      const int32_t row = min(tb + 16 * b + n, N32 - 1);
+      load_words<BITS>(ck0 + (uint32_t)row * (16 * BITS), r.kw[b]);
+      load_words<NG>(sc0 + (uint32_t)row * (2 * NG), r.sw[b]);
+      load_slots_of(row, r.iw[b]);
     }
   };
-  auto computeA = [&](int32_t t, int32_t c0, const ARegs& r, float (&wmax)[HPL]) {
+  auto computeA = [&](int32_t t, int32_t c0, const ARegs& r, float (&wmax)[HPL]) RKV_INLINE {
     const int32_t tb = tile_of(t) * kDecTile;
     const TileRefs tr = tile_refs(tb, N32, sc);
     const bool ftile = EX && tr.cb >= KM;  // wave-uniform
@@ -424,9 +421,15 @@ __global__ __launch_bounds__(256, 2) void k_decode(
           // every position of the tile has k = KM references: no predicates
           // (positions past N read slot 0 and are masked to -inf)
           const float* qrow = qk_s + h * ls;
-          float rs = 0.f;
+          // all KM lookups first, then a pairwise sum: one LDS wait per token
+          float qv[KM];
 #pragma unroll
-          for (int j = 0; j < KM; ++j) rs += qrow[(r.iw[b][j >> 1] >> (16 * (j & 1))) & 0xFFFFu];
+          for (int j = 0; j < KM; ++j) qv[j] = qrow[(r.iw[b][j >> 1] >> (16 * (j & 1))) & 0xFFFFu];
+#pragma unroll
+          for (int w2 = 1; w2 < KM; w2 *= 2)
+#pragma unroll
+            for (int j = 0; j + w2 < KM; j += 2 * w2) qv[j] += qv[j + w2];
+          const float rs = qv[0];
           float res = 0.f;
 #pragma unroll
           for (int g = 0; g < NG; ++g) {
@@ -466,17 +469,14 @@ __global__ __launch_bounds__(256, 2) void k_decode(
       }
     }
   };
-  auto loadB = [&](int32_t t, BRegs& r) {
+  auto loadB = [&](int32_t t, BRegs& r) RKV_INLINE {
     const int32_t tb = tile_of(t) * kDecTile;
-    const bool tvalid = tb < N32;
-    const uint8_t* cvt = cv + (uint32_t)(tvalid ? tile_of(t) : 0) * (128 * 4 * BITS);
+    // a tile past the attended length reads tile 0 (all its p are 0)
+    const uint8_t* cvt = cv + (uint32_t)(tb < N32 ? tile_of(t) : 0) * (128 * 4 * BITS);
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
       const uint8_t* pp = cvt + 16 * blk * (4 * BITS);
-      if (!tvalid) {
-        r.vw[blk][0] = 0;
-        if constexpr (BITS == 8) r.vw[blk][1] = 0;
-      } else if constexpr (BITS == 8) {
+      if constexpr (BITS == 8) {
         const uint2 v = *reinterpret_cast<const uint2*>(pp);
         r.vw[blk][0] = v.x;
         r.vw[blk][1] = v.y;
@@ -488,19 +488,12 @@ __global__ __launch_bounds__(256, 2) void k_decode(
     }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int32_t tok = tb + 16 * b + n;
-      if (tok < N32) {
-        load_slots_of(tok, r.iw[b]);
-        load_words<NG>(sc16 + (uint32_t)(tb + 16 * b) * (2 * NG), r.sw[b]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < KM / 2; ++j) r.iw[b][j] = 0;
-#pragma unroll
-        for (int j = 0; j < NG; ++j) r.sw[b][j] = 0;
-      }
+      const int32_t row = min(tb + 16 * b + n, N32 - 1);
+      load_slots_of(row, r.iw[b]);
+      load_words<NG>(sc0 + (uint32_t)row * (2 * NG), r.sw[b]);
     }
   };
-  auto computeB = [&](int32_t t, int32_t c0, const BRegs& r, const float (&mh)[HPL]) {
+  auto computeB = [&](int32_t t, int32_t c0, const BRegs& r, const float (&mh)[HPL]) RKV_INLINE {
     const int32_t tb = tile_of(t) * kDecTile;
     const TileRefs tr = tile_refs(tb, N32, sc);
     const bool ftile = EX && tr.cb >= KM;  // wave-uniform
@@ -600,15 +593,16 @@ __global__ __launch_bounds__(256, 2) void k_decode(
     for (int hh = 0; hh < HPL; ++hh) wmax[hh] = -INFINITY;
     {
       // two register sets alternate (unrolled by 2): no copies of loads in flight
+      // entries past the chunk load its last entry (never computed)
       ARegs ra, rb;
       int32_t t = c0 + w;
-      if (t < c1) loadA(t, ra);
+      loadA(min(t, c1 - 1), ra);
       while (t < c1) {
-        if (t + 4 < c1) loadA(t + 4, rb);
+        loadA(min(t + 4, c1 - 1), rb);
         computeA(t, c0, ra, wmax);
         t += 4;
         if (t >= c1) break;
-        if (t + 4 < c1) loadA(t + 4, ra);
+        loadA(min(t + 4, c1 - 1), ra);
         computeA(t, c0, rb, wmax);
         t += 4;
       }
@@ -660,13 +654,13 @@ __global__ __launch_bounds__(256, 2) void k_decode(
     {
       BRegs ra, rb;
       int32_t t = c0 + w;
-      if (t < c1) loadB(t, ra);
+      loadB(min(t, c1 - 1), ra);
       while (t < c1) {
-        if (t + 4 < c1) loadB(t + 4, rb);
+        loadB(min(t + 4, c1 - 1), rb);
         computeB(t, c0, ra, mh);
         t += 4;
         if (t >= c1) break;
-        if (t + 4 < c1) loadB(t + 4, ra);
+        loadB(min(t + 4, c1 - 1), ra);
         computeB(t, c0, rb, mh);
         t += 4;
       }
@@ -705,12 +699,44 @@ __global__ __launch_bounds__(256, 2) void k_decode(
 }
 
 // ------------------------------------------------------------------ combine
-// One block per (instance, KV head, 32-dim chunk): merge the splits of its
-// G query heads, then add W . Vref for the chunk's dims.
-constexpr int kCombChunks = 4;
+// One block per (instance, KV head): merge the splits of its G query heads
+// (maximum, softmax sum, P.V partials and the reference weights W), then add
+// W . Vref.  W is merged once into LDS; each thread then takes DPT
+// consecutive dims of all G heads over a stride of the references, reading
+// each reference row chunk as one vector, and the stride groups are summed
+// in LDS.  W . Vref runs over the n_valid written references only.
+// GM bounds G: 8 (8 dims per thread) or 16 (4 dims per thread).
+template <int GM>
+struct CombShape {
+  static constexpr int DPT = GM > 8 ? 4 : 8;  // dims per thread
+  static constexpr int TPR = 128 / DPT;       // threads per reference row
+  static constexpr int RG = 256 / TPR;        // reference stride groups
+};
 
-// W . Vref runs over the n_valid written references only.
-template <typename T>
+// DPT dims (d0 ..) of reference row j as fp32: raw rows of T, or int4
+// nibbles times the row's group scale (exact).
+template <typename T, int DPT>
+__device__ inline void vref_chunk(const T* __restrict__ raw, const uint8_t* __restrict__ q4,
+                                  const uint16_t* __restrict__ rsc, int ng, int group,
+                                  int ref_bits, int64_t j, int d0, float (&x)[DPT]) {
+  if (ref_bits == 4) {
+    const float s = half_bits_to_f32(rsc[j * ng + d0 / group]);
+    const uint32_t w = DPT == 8 ? *reinterpret_cast<const uint32_t*>(q4 + j * 64 + d0 / 2)
+                                : (uint32_t)*reinterpret_cast<const uint16_t*>(q4 + j * 64 + d0 / 2);
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) x[e] = (float)((int32_t)(w << (28 - 4 * e)) >> 28) * s;
+  } else if constexpr (DPT == 8) {
+    load8(raw + j * 128 + d0, x);
+  } else if constexpr (sizeof(T) == 2) {
+    const uint2 w = *reinterpret_cast<const uint2*>(raw + j * 128 + d0);
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+  } else {
+    const float4 v = *reinterpret_cast<const float4*>(raw + j * 128 + d0);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  }
+}
+
+template <typename T, int GM>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
                                                  const T* __restrict__ ref_kv,
                                                  const uint16_t* __restrict__ ref_scales,
@@ -718,19 +744,36 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
                                                  float* __restrict__ out, int G, int H,
                                                  int64_t n_refs, int64_t n_valid, int n_split,
                                                  float* __restrict__ ores) {
+  using S = CombShape<GM>;
+  constexpr int DPT = S::DPT, TPR = S::TPR, RG = S::RG;
   extern __shared__ float cs[];
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
-  float* wt = cs;                   // [G][nrp]
+  float* wt = cs;                   // [G][nrp] merged W
   float* fs = wt + G * nrp;         // [G][n_split] split factors
-  float* red = fs + G * n_split;    // [8][G][32] partial W.Vref sums
-  float* ls_ = red + 8 * G * 32;    // [G] l
+  float* ls_ = fs + G * n_split;    // [16] l
+  float* red = ls_ + 16;            // [RG][G][128] partial W . Vref
   const int kvh = blockIdx.x;
   const int64_t inst = blockIdx.y;
-  const int chunk = blockIdx.z;
   const int Hq = H * G;
   const int tid = threadIdx.x;
   const int64_t rec = part_rec_floats(n_refs);
   const float* base = part + (inst * Hq + kvh * G) * n_split * rec;  // head h at + h*n_split*rec
+  // W . Vref operands: thread (dg, rg) takes dims d0 .. d0+DPT-1 of references
+  // rg, rg+RG, ...; the first kUnroll rows are requested before the merges
+  constexpr int kUnroll = 8;
+  const int dg = tid % TPR, rg = tid / TPR;
+  const int d0 = dg * DPT;
+  const int64_t row0 = ((inst * H + kvh) * 2 + 1) * n_refs;  // V plane
+  const int ngq = ref_bits == 4 ? 128 / group : 1;
+  const T* raw = ref_kv + row0 * 128;
+  const uint8_t* q4 = reinterpret_cast<const uint8_t*>(ref_kv) + row0 * 64;
+  const uint16_t* rsc = ref_bits == 4 ? ref_scales + row0 * ngq : nullptr;
+  float x[kUnroll][DPT];
+  if (rg + (kUnroll - 1) * RG < n_valid) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      vref_chunk<T, DPT>(raw, q4, rsc, ngq, group, ref_bits, rg + u * RG, d0, x[u]);
+  }
   if (tid < G) {
     const float* b = base + tid * n_split * rec;
     float M = -INFINITY;
@@ -770,56 +813,56 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
     *reinterpret_cast<float4*>(wt + h * nrp + 4 * c) = acc;
   }
   __syncthreads();
-  // W . Vref on dims chunk*32 + t: thread (t, g) sums references j = g mod 8
-  const int t = tid & 31;
-  const int g = tid >> 5;
-  const int dim = chunk * 32 + t;
-  const T* vref = ref_kv + ((inst * H + kvh) * 2 + 1) * n_refs * 128 + dim;
-  // quantised references: nibble of `dim` in row j, times its group's scale
-  const uint8_t* vq = reinterpret_cast<const uint8_t*>(ref_kv) +
-                      ((inst * H + kvh) * 2 + 1) * n_refs * 64 + (dim >> 1);
-  const int ngq = ref_bits == 4 ? 128 / group : 1;
-  const uint16_t* vs = ref_scales + ((inst * H + kvh) * 2 + 1) * n_refs * ngq + dim / (ref_bits == 4 ? group : 128);
-  auto vref_at = [&](int64_t jj) -> float {
-    if (ref_bits == 4) {
-      const int c = ((int)vq[jj * 64] >> (4 * (dim & 1))) & 0xF;
-      return (float)(c >= 8 ? c - 16 : c) * half_bits_to_f32(vs[jj * ngq]);
+  float a[GM][DPT];
+#pragma unroll
+  for (int h = 0; h < GM; ++h)
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) a[h][e] = 0.f;
+  int64_t j = rg;
+  for (; j + (kUnroll - 1) * RG < n_valid; j += kUnroll * RG) {
+    if (j != rg) {  // the first batch was requested before the merges
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        vref_chunk<T, DPT>(raw, q4, rsc, ngq, group, ref_bits, j + u * RG, d0, x[u]);
     }
-    return (float)vref[jj * 128];
-  };
-  float a[16];
 #pragma unroll
-  for (int h = 0; h < 16; ++h) a[h] = 0.f;
-  int64_t j = g;
-  for (; j + 8 * 7 < n_valid; j += 8 * 8) {
-    float v[8];
+    for (int u = 0; u < kUnroll; ++u) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = vref_at(j + 8 * u);
+      for (int h = 0; h < GM; ++h) {
+        if (h < G) {
+          const float wj = wt[h * nrp + j + u * RG];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-#pragma unroll
-      for (int h = 0; h < 16; ++h)
-        if (h < G) a[h] = __builtin_fmaf(wt[h * nrp + j + 8 * u], v[u], a[h]);
+          for (int e = 0; e < DPT; ++e) a[h][e] = __builtin_fmaf(wj, x[u][e], a[h][e]);
+        }
+      }
     }
   }
-  for (; j < n_valid; j += 8) {
-    const float v = vref_at(j);
+  for (; j < n_valid; j += RG) {
+    float x[DPT];
+    vref_chunk<T, DPT>(raw, q4, rsc, ngq, group, ref_bits, j, d0, x);
 #pragma unroll
-    for (int h = 0; h < 16; ++h)
-      if (h < G) a[h] = __builtin_fmaf(wt[h * nrp + j], v, a[h]);
+    for (int h = 0; h < GM; ++h) {
+      if (h < G) {
+        const float wj = wt[h * nrp + j];
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) a[h][e] = __builtin_fmaf(wj, x[e], a[h][e]);
+      }
+    }
   }
 #pragma unroll
-  for (int h = 0; h < 16; ++h)
-    if (h < G) red[(g * G + h) * 32 + t] = a[h];
+  for (int h = 0; h < GM; ++h)
+    if (h < G)
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) red[(rg * G + h) * 128 + d0 + e] = a[h][e];
   __syncthreads();
-  for (int e = tid; e < G * 32; e += 256) {
-    const int h = e / 32, tt = e % 32;
+  for (int e = tid; e < G * 128; e += 256) {
+    const int h = e / 128, d = e % 128;
     float s = 0.f;
-    for (int x = 0; x < 8; ++x) s += red[(x * G + h) * 32 + tt];
-    const float* b = base + h * n_split * rec + 4 + chunk * 32 + tt;
+    for (int x = 0; x < RG; ++x) s += red[(x * G + h) * 128 + d];
+    const float* b = base + h * n_split * rec + 4 + d;
     float o = 0.f;
     for (int x = 0; x < n_split; ++x) o += fs[h * n_split + x] * b[x * rec];
-    const int64_t at = (inst * Hq + kvh * G + h) * 128 + chunk * 32 + tt;
+    const int64_t at = (inst * Hq + kvh * G + h) * 128 + d;
     if (ores) {
       // latent codes: the residual part is still rotated; f_d is applied
       // to the whole row afterwards
@@ -913,7 +956,8 @@ size_t decode_lds_bytes(int G, int NG, int64_t n_refs) {
 
 size_t combine_lds_bytes(int G, int64_t n_refs, int n_split) {
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
-  return (size_t)(G * nrp + G * n_split + 8 * G * 32 + G) * 4;
+  const int RG = G > 8 ? CombShape<16>::RG : CombShape<8>::RG;
+  return (size_t)(G * nrp + G * n_split + 16 + RG * G * 128) * 4;
 }
 
 // Whether the decode kernels' LDS fits one CU (160 KiB).
@@ -964,14 +1008,13 @@ hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t clds = combine_lds_bytes(G, n_refs, n_split);
+  auto comb = G > 8 ? k_combine<T, 16> : k_combine<T, 8>;
   if (clds > 64 * 1024) {
-    e = hipFuncSetAttribute((const void*)k_combine<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)clds);
+    e = hipFuncSetAttribute((const void*)comb, hipFuncAttributeMaxDynamicSharedMemorySize, (int)clds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_combine<T>, dim3(H, (unsigned)n_inst, kCombChunks), dim3(256), clds, st,
-                     part, (const T*)ref_kv, ref_scales, ref_bits, group_r, out, G, H, n_refs,
-                     n_valid, n_split, ores);
+  hipLaunchKernelGGL(comb, dim3(H, (unsigned)n_inst), dim3(256), clds, st, part, (const T*)ref_kv,
+                     ref_scales, ref_bits, group_r, out, G, H, n_refs, n_valid, n_split, ores);
   e = hipGetLastError();
   if (e != hipSuccess || !lm) return e;
   hipLaunchKernelGGL(k_latent_out, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, ores, *lm,

@@ -284,6 +284,27 @@ rkv_status rkv_decode_workspace(const rkv_cache* c, int32_t n_q_heads, int32_t n
   return RKV_OK;
 }
 
+rkv_status rkv_decode_split_hint(const rkv_cache* c, int32_t n_q_heads, int32_t* n_split) {
+  if (!n_split) return RKV_ERR_INVALID_ARG;
+  rkv_status s = check_shape(c);
+  if (s != RKV_OK) return s;
+  if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0) return RKV_ERR_INVALID_ARG;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  // about three decode blocks per compute unit: the kernel holds three per
+  // CU, and more splits only add partial records to merge
+  const int64_t heads = c->n_inst * (int64_t)c->n_kv_heads;
+  const int64_t tiles = (c->seq_len + 31) / 32;
+  int64_t ns = heads > 0 ? (3 * (int64_t)cus + heads - 1) / heads : 1;
+  if (ns > tiles) ns = tiles;
+  if (ns > 4096) ns = 4096;
+  *n_split = (int32_t)(ns < 1 ? 1 : ns);
+  return RKV_OK;
+}
+
 static rkv_status decode_common(const void* q, int32_t n_q_heads, const rkv_cache* c,
                                 int64_t length, float softmax_scale, float* out,
                                 const int32_t* tiles, int32_t n_tiles, int32_t n_split, void* ws,

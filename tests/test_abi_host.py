@@ -236,3 +236,24 @@ def test_misaligned_buffers_are_rejected(lib):
     # reconstruct outputs
     assert lib.rkv_reconstruct(C.byref(c), C.c_void_p(0x70002), C.c_void_p(0x80000),
                                null) == L.RKV_ERR_INVALID_ARG
+
+
+def test_decode_split_hint(lib):
+    ns = C.c_int32()
+    # 8 sequences x 8 KV heads of 32K: about three blocks per CU (256 CUs
+    # when the device cannot be queried, as on a host without a GPU)
+    c = _cache(n_inst=8, H=8, N=32768, base=64)
+    assert lib.rkv_cache_init(C.byref(c)) == L.RKV_OK
+    assert lib.rkv_decode_split_hint(C.byref(c), 32, C.byref(ns)) == L.RKV_OK
+    assert 1 <= ns.value <= 1024
+    many = _cache(n_inst=256, H=8, N=32768, base=64)
+    assert lib.rkv_cache_init(C.byref(many)) == L.RKV_OK
+    assert lib.rkv_decode_split_hint(C.byref(many), 32, C.byref(ns)) == L.RKV_OK
+    assert ns.value >= 1
+    short = _cache(n_inst=1, H=1, N=100, base=16)
+    assert lib.rkv_cache_init(C.byref(short)) == L.RKV_OK
+    assert lib.rkv_decode_split_hint(C.byref(short), 4, C.byref(ns)) == L.RKV_OK
+    assert ns.value == 4   # capped at ceil(100 / 32) tiles
+    two = _cache(n_inst=1, H=2, N=100, base=16)
+    assert lib.rkv_cache_init(C.byref(two)) == L.RKV_OK
+    assert lib.rkv_decode_split_hint(C.byref(two), 3, C.byref(ns)) == L.RKV_ERR_INVALID_ARG
