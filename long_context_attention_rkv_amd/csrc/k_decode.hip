@@ -33,6 +33,8 @@
 //              normalises.
 #include <float.h>
 
+#include <type_traits>
+
 #include "rkv_common.h"
 
 namespace rkv {
@@ -225,6 +227,15 @@ __device__ inline void pos_info(int32_t tok, const TileRefs& tr, const Sched& sc
   keff = cnt < k ? cnt : k;
 }
 
+// Slot of position `tok` if it is one of the tile's references, else -1 (the
+// k_eff of a fast tile is KM for every position).
+__device__ inline int32_t ref_slot_in_tile(int32_t tok, const TileRefs& tr, const Sched& sc) {
+  int32_t slot = -1;
+  for (int32_t r = tr.cb; r < tr.ce; ++r)
+    if (sched_pos(r, sc) == tok) slot = r;
+  return slot;
+}
+
 // EX: every row of ref_idx holds exactly KM slots (k == KM).
 template <typename T, int BITS, int NG, int KM, bool EX>
 __global__ __launch_bounds__(256, 2) void k_decode(
@@ -387,10 +398,12 @@ __global__ __launch_bounds__(256, 2) void k_decode(
       load_slots_of(row, r.iw[b]);
     }
   };
-  auto computeA = [&](int32_t t, int32_t c0, const ARegs& r, float (&wmax)[HPL]) RKV_INLINE {
-    const int32_t tb = tile_of(t) * kDecTile;
-    const TileRefs tr = tile_refs(tb, N32, sc);
-    const bool ftile = EX && tr.cb >= KM;  // wave-uniform
+  // Phase A of one tile.  FT (a fast tile: every position has k = KM
+  // references) is chosen per tile, wave-uniformly, so each variant is
+  // straight-line code.
+  auto computeA_t = [&](auto ft_c, int32_t tb, int32_t t, int32_t c0, const TileRefs& tr,
+                        const ARegs& r, float (&wmax)[HPL]) RKV_INLINE {
+    constexpr bool FT = decltype(ft_c)::value;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int32_t tok = tb + 16 * b + n;
@@ -410,14 +423,19 @@ __global__ __launch_bounds__(256, 2) void k_decode(
       }
       int32_t slot;
       int keff;
-      pos_info(tok, tr, sc, k, slot, keff);
-      if (!valid) { slot = -1; keff = 0; }
+      if constexpr (FT) {
+        slot = ref_slot_in_tile(tok, tr, sc);
+        keff = KM;
+      } else {
+        pos_info(tok, tr, sc, k, slot, keff);
+        if (!valid) { slot = -1; keff = 0; }
+      }
       const float inv_keff = keff > 0 ? 1.0f / (float)keff : 0.f;
       const int u = (t - c0) * kDecTile + 16 * b + n;
 #pragma unroll
       for (int hh = 0; hh < HPL; ++hh) {
         const int h = h0 + hh;
-        if (h < G && ftile) {
+        if (FT && h < G) {
           // every position of the tile has k = KM references: no predicates
           // (positions past N read slot 0 and are masked to -inf)
           const float* qrow = qk_s + h * ls;
@@ -441,7 +459,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(
           const float lg = valid ? alpha * sc_ : -INFINITY;
           lg_s[h * CTP + u] = lg;
           wmax[hh] = fmaxf(wmax[hh], lg);
-        } else if (h < G) {
+        } else if (!FT && h < G) {
           float lg = -INFINITY;
           if (valid) {
             const float* qrow = qk_s + h * ls;
@@ -469,6 +487,14 @@ __global__ __launch_bounds__(256, 2) void k_decode(
       }
     }
   };
+  auto computeA = [&](int32_t t, int32_t c0, const ARegs& r, float (&wmax)[HPL]) RKV_INLINE {
+    const int32_t tb = tile_of(t) * kDecTile;
+    const TileRefs tr = tile_refs(tb, N32, sc);
+    if (EX && tr.cb >= KM)
+      computeA_t(std::true_type{}, tb, t, c0, tr, r, wmax);
+    else
+      computeA_t(std::false_type{}, tb, t, c0, tr, r, wmax);
+  };
   auto loadB = [&](int32_t t, BRegs& r) RKV_INLINE {
     const int32_t tb = tile_of(t) * kDecTile;
     // a tile past the attended length reads tile 0 (all its p are 0)
@@ -493,10 +519,9 @@ __global__ __launch_bounds__(256, 2) void k_decode(
       load_words<NG>(sc0 + (uint32_t)row * (2 * NG), r.sw[b]);
     }
   };
-  auto computeB = [&](int32_t t, int32_t c0, const BRegs& r, const float (&mh)[HPL]) RKV_INLINE {
-    const int32_t tb = tile_of(t) * kDecTile;
-    const TileRefs tr = tile_refs(tb, N32, sc);
-    const bool ftile = EX && tr.cb >= KM;  // wave-uniform
+  auto computeB_t = [&](auto ft_c, int32_t tb, int32_t t, int32_t c0, const TileRefs& tr,
+                        const BRegs& r, const float (&mh)[HPL]) RKV_INLINE {
+    constexpr bool FT = decltype(ft_c)::value;
     float psum[HPL];
 #pragma unroll
     for (int hh = 0; hh < HPL; ++hh) psum[hh] = 0.f;
@@ -506,15 +531,20 @@ __global__ __launch_bounds__(256, 2) void k_decode(
       const bool valid = tok < N32;
       int32_t slot;
       int keff;
-      pos_info(tok, tr, sc, k, slot, keff);
-      if (!valid) { slot = -1; keff = 0; }
+      if constexpr (FT) {
+        slot = ref_slot_in_tile(tok, tr, sc);
+        keff = KM;
+      } else {
+        pos_info(tok, tr, sc, k, slot, keff);
+        if (!valid) { slot = -1; keff = 0; }
+      }
       const int u = 16 * b + n;
       const int pos = 8 * (u >> 3) + invperm_of<BITS>(u & 7);
       const int uc = (t - c0) * kDecTile + u;
 #pragma unroll
       for (int hh = 0; hh < HPL; ++hh) {
         const int h = h0 + hh;
-        if (h < G && ftile) {
+        if (FT && h < G) {
           const float lg = lg_s[h * CTP + uc];
           const float pv = valid ? __expf(lg - mh[hh]) : 0.f;
           psum[hh] += pv;
@@ -527,7 +557,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(
             atomicAdd(wrow + ((r.iw[b][j >> 1] >> (16 * (j & 1))) & 0xFFFFu), pw);
           if (isref) atomicAdd(wrow + slot, to_fixed32(pv));
           pst[h * kDecTile + pos] = (_Float16)(isref ? 0.f : pv);
-        } else if (h < G) {
+        } else if (!FT && h < G) {
           const float lg = lg_s[h * CTP + uc];
           const float pv = (valid && lg > -INFINITY) ? __expf(lg - mh[hh]) : 0.f;
           psum[hh] += pv;
@@ -583,6 +613,14 @@ __global__ __launch_bounds__(256, 2) void k_decode(
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
+  };
+  auto computeB = [&](int32_t t, int32_t c0, const BRegs& r, const float (&mh)[HPL]) RKV_INLINE {
+    const int32_t tb = tile_of(t) * kDecTile;
+    const TileRefs tr = tile_refs(tb, N32, sc);
+    if (EX && tr.cb >= KM)
+      computeB_t(std::true_type{}, tb, t, c0, tr, r, mh);
+    else
+      computeB_t(std::false_type{}, tb, t, c0, tr, r, mh);
   };
 
   for (int32_t c0 = t0; c0 < t1; c0 += kChunkTiles) {

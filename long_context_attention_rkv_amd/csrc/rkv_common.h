@@ -147,7 +147,7 @@ __device__ inline bool is_pow2(int v) { return (v & (v - 1)) == 0; }
 
 // Lane exchanges inside a DPP row (16 lanes), no LDS traffic.
 #define RKV_DPP_F32(v, ctrl) \
-  __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), (ctrl), 0xF, 0xF, false))
+  __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), (ctrl), 0xF, 0xF, true))
 
 // Maximum over aligned groups of `lanes` consecutive lanes (4, 8 or 16):
 // swaps within quads (xor 1, xor 2), then half-row and row mirrors.
