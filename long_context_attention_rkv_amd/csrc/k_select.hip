@@ -120,11 +120,13 @@ __device__ inline int acc_row(int r, int half) { return (r & 3) + 8 * (r >> 2) +
 
 // Survivor lists: per (lane, token set) entries of two words, the distance
 // (fp32 bits) and the slot, laid out [entry][word][64 lanes] so that one
-// entry is a single two-address LDS store.  Capacity: the lane's k best plus
-// the kCheckRows accumulator rows appended between two fullness checks.
+// entry is a single two-address LDS store.  Capacity: the lane's k best, 3
+// more (a lane holds about k/2 + 1 survivors on average, rarely more than
+// k + 3, so a list seldom needs cutting), plus the kCheckRows accumulator
+// rows appended between two fullness checks.
 constexpr int kCheckRows = 4;
 template <int KM>
-constexpr int surv_cap() { return KM + kCheckRows; }
+constexpr int surv_cap() { return KM + 3 + kCheckRows; }
 constexpr int kEntryWords = 128;  // stride of one list entry, in 32-bit words
 
 // Loads a lane's survivor list into registers; entries past cnt read as +inf.
@@ -183,20 +185,35 @@ __device__ __forceinline__ void token_select(const uint32_t* la, int cnt_a, cons
   float ea[CAP], ja[CAP], eb[CAP], jb[CAP];
   load_list<CAP>(la, cnt_a, ea, ja);
   load_list<CAP>(lb, cnt_b, eb, jb);
+  // Entries past a list's count read +inf and change nothing below, so
+  // groups of four entries past every lane's counts are skipped (the test
+  // is wave-uniform); lists hold about k/2 entries against a capacity of
+  // k + 7.
+  const int cmax = cnt_a > cnt_b ? cnt_a : cnt_b;
   float top[KM];
 #pragma unroll
   for (int t = 0; t < KM; ++t) top[t] = INFINITY;
 #pragma unroll
-  for (int c = 0; c < CAP; ++c) {
-    topk_insert(top, ea[c]);
-    topk_insert(top, eb[c]);
+  for (int c0 = 0; c0 < CAP; c0 += 4) {
+    if (__any(c0 < cmax)) {
+#pragma unroll
+      for (int c = c0; c < c0 + 4 && c < CAP; ++c) {
+        topk_insert(top, ea[c]);
+        topk_insert(top, eb[c]);
+      }
+    }
   }
   const float th = topk_get(top, keff);
   int nless = 0, nties = 0;
 #pragma unroll
-  for (int c = 0; c < CAP; ++c) {
-    nless += (ea[c] < th) + (eb[c] < th);
-    nties += (ea[c] == th) + (eb[c] == th);
+  for (int c0 = 0; c0 < CAP; c0 += 4) {
+    if (__any(c0 < cmax)) {
+#pragma unroll
+      for (int c = c0; c < c0 + 4 && c < CAP; ++c) {
+        nless += (ea[c] < th) + (eb[c] < th);
+        nties += (ea[c] == th) + (eb[c] == th);
+      }
+    }
   }
   const int quota = keff - nless;  // >= 1: th is the keff-th smallest
   float slot_bound = 65536.f;      // ties at th are taken up to this slot
@@ -214,11 +231,16 @@ __device__ __forceinline__ void token_select(const uint32_t* la, int cnt_a, cons
 #pragma unroll
   for (int t = 0; t < KM; ++t) sel[t] = 65535.f;
 #pragma unroll
-  for (int c = 0; c < CAP; ++c) {
-    const bool ta = ea[c] < th || (ea[c] == th && ja[c] <= slot_bound);
-    const bool tb = eb[c] < th || (eb[c] == th && jb[c] <= slot_bound);
-    topk_insert(sel, ta ? ja[c] : 65535.f);
-    topk_insert(sel, tb ? jb[c] : 65535.f);
+  for (int c0 = 0; c0 < CAP; c0 += 4) {
+    if (__any(c0 < cmax)) {
+#pragma unroll
+      for (int c = c0; c < c0 + 4 && c < CAP; ++c) {
+        const bool ta = ea[c] < th || (ea[c] == th && ja[c] <= slot_bound);
+        const bool tb = eb[c] < th || (eb[c] == th && jb[c] <= slot_bound);
+        topk_insert(sel, ta ? ja[c] : 65535.f);
+        topk_insert(sel, tb ? jb[c] : 65535.f);
+      }
+    }
   }
 }
 
