@@ -454,9 +454,11 @@ __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
   }
 
   // ---- pass 2: collect candidates <= tau
-  int cnt[kSets];
+  // ends[c]: word offset of the end of list c (count * kEntryWords); a
+  // survivor moves it by one entry (compare, select, add per candidate)
+  uint32_t ends[kSets];
 #pragma unroll
-  for (int c = 0; c < kSets; ++c) cnt[c] = 0;
+  for (int c = 0; c < kSets; ++c) ends[c] = 0;
   stream([&](int rt, const f32x16 (&acc)[kSets]) RKV_INLINE {
     const uint32_t r0 = (uint32_t)rt * 32 + 4 * half;
 #pragma unroll
@@ -466,24 +468,30 @@ __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
         uint32_t* bl = &sbl[w][c][0][0][lane];
 #pragma unroll
         for (int r = kCheckRows * h; r < kCheckRows * h + kCheckRows; ++r) {
-          // cnt <= CAP - 1 here: at most kCheckRows - 1 appends since the
-          // last check left cnt <= CAP - kCheckRows
-          uint32_t* at = bl + cnt[c] * kEntryWords;
+          // at most CAP - 1 entries here: at most kCheckRows - 1 appends
+          // since the last check left at most CAP - kCheckRows
+          uint32_t* at = bl + ends[c];
           at[0] = __float_as_uint(acc[c][r]);
           at[64] = r0 + (uint32_t)acc_row(r, 0);
-          cnt[c] += acc[c][r] <= tau[c] ? 1 : 0;
+          ends[c] += acc[c][r] <= tau[c] ? (uint32_t)kEntryWords : 0u;
         }
       }
       bool full = false;
 #pragma unroll
-      for (int c = 0; c < kSets; ++c) full |= cnt[c] > CAP - kCheckRows;
+      for (int c = 0; c < kSets; ++c) full |= ends[c] > (uint32_t)((CAP - kCheckRows) * kEntryWords);
       if (__any(full)) {
 #pragma unroll
-        for (int c = 0; c < kSets; ++c)
-          lane_compact<KM, CAP>(&sbl[w][c][0][0][lane], cnt[c], tau[c], k);
+        for (int c = 0; c < kSets; ++c) {
+          int cnt = (int)(ends[c] / kEntryWords);
+          lane_compact<KM, CAP>(&sbl[w][c][0][0][lane], cnt, tau[c], k);
+          ends[c] = (uint32_t)cnt * kEntryWords;
+        }
       }
     }
   });
+  int cnt[kSets];
+#pragma unroll
+  for (int c = 0; c < kSets; ++c) cnt[c] = (int)(ends[c] / kEntryWords);
   if (!active) return;
 
   // ---- final: one token per lane (set `half`, column n) from the lists of
