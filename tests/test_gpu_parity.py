@@ -180,6 +180,9 @@ DECODE = [
     ("gqa7_g64_int2", _cfg(4, n_kv_heads=2, n_q_heads=14, batch=1), 2, 2, 500),
     ("gqa7_g64_int4", _cfg(4, n_kv_heads=2, n_q_heads=14, batch=1), 4, 1, 500),
     ("g128_gqa4", _cfg(1, n_kv_heads=1, n_q_heads=4, group=128), 4, 1, 300),
+    # more than 8 query heads per KV head: the combine's 4-dims-per-thread form
+    ("g128_gqa16_bf16", _cfg(1, n_kv_heads=2, n_q_heads=32, group=128), 4, 1, 700),
+    ("g128_gqa12_f32_int8", _cfg(0, n_kv_heads=1, n_q_heads=12, group=128), 8, 1, 500),
 ]
 
 
@@ -315,6 +318,7 @@ REFQ_CASES = [
     ("tiny_f32_int8", get_config(0), 8, 1, 1024),
     ("llama_bf16_int4_gqa4", _cfg(1, n_kv_heads=2, n_q_heads=8), 4, 1, 1000),
     ("stress_int2_k16_g64", _cfg(4, n_kv_heads=2, n_q_heads=14, batch=2), 2, 2, 500),
+    ("gqa16_g128_f32", _cfg(0, n_kv_heads=1, n_q_heads=16, group=128), 4, 1, 800),
 ]
 
 
@@ -363,6 +367,7 @@ LATENT_CASES = [
     ("dynamic_int4_g128", _cfg(3, n_kv_heads=1, n_q_heads=4, group=128, double_after=512,
                                 drift_block=128), 4, 1, 1300, 0, 99),
     ("llama_int4_quantised_refs", _cfg(1, n_kv_heads=2, n_q_heads=8), 4, 1, 700, 4, 7),
+    ("gqa16_g128_quantised_refs", _cfg(1, n_kv_heads=1, n_q_heads=16, group=128), 4, 1, 600, 4, 3),
 ]
 
 
