@@ -27,40 +27,8 @@
 
 namespace rkv {
 
-template <int BITS>
-__device__ inline void store_codes(uint8_t* p, const uint32_t (&c)[8]) {
-  if constexpr (BITS == 4) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) w |= (c[t] & 0xF) << (4 * t);
-    *reinterpret_cast<uint32_t*>(p) = w;
-  } else if constexpr (BITS == 8) {
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      w0 |= (c[t] & 0xFF) << (8 * t);
-      w1 |= (c[t + 4] & 0xFF) << (8 * t);
-    }
-    *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
-  } else {
-    uint32_t w = 0;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) w |= (c[t] & 0x3) << (2 * t);
-    *reinterpret_cast<uint16_t*>(p) = (uint16_t)w;
-  }
-}
-
-// The codes of 8 consecutive positions of one transposed V row as one word
-// (BITS bytes), and stores of it: whole, or only the fields of positions
-// lo .. hi-1 (the others keep their bits).
-template <int BITS>
-__device__ inline uint64_t pack_codes8(const int (&c)[8]) {
-  uint64_t w = 0;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) w |= (uint64_t)(c[t] & ((1 << BITS) - 1)) << (BITS * t);
-  return w;
-}
-
+// A word of packed codes (BITS bytes: 8 codes) and stores of it: whole, or
+// only the fields of elements lo .. hi-1 (the others keep their bits).
 template <int BITS>
 __device__ inline void store_word(uint8_t* p, uint64_t w) {
   if constexpr (BITS == 8) *reinterpret_cast<uint64_t*>(p) = w;
@@ -83,29 +51,6 @@ __device__ inline void store_word_range(uint8_t* p, uint64_t w, int lo, int hi) 
   } else {
     uint16_t* q = reinterpret_cast<uint16_t*>(p);
     *q = (uint16_t)((*q & ~m) | (w & m));
-  }
-}
-
-template <int BITS>
-__device__ inline void store_codes(uint8_t* p, const int (&c)[8]) {
-  if constexpr (BITS == 4) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) w |= (uint32_t)(c[t] & 0xF) << (4 * t);
-    *reinterpret_cast<uint32_t*>(p) = w;
-  } else if constexpr (BITS == 8) {
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      w0 |= (uint32_t)(c[t] & 0xFF) << (8 * t);
-      w1 |= (uint32_t)(c[t + 4] & 0xFF) << (8 * t);
-    }
-    *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
-  } else {
-    uint32_t w = 0;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) w |= (uint32_t)(c[t] & 0x3) << (2 * t);
-    *reinterpret_cast<uint16_t*>(p) = (uint16_t)w;
   }
 }
 
@@ -262,111 +207,124 @@ __device__ inline void ref_mean8_src(const RefSrc<T, RQ>& src, const uint16_t* _
 }
 
 
-constexpr int kQTokens = 16;   // tokens per step (512 threads)
-constexpr int kVTile = 32;     // tokens per transposed V tile
+constexpr int kQTokens = 16;   // positions per step (512 threads)
+constexpr int kVTile = 32;     // positions per transposed V tile
 
-// Slots of one token when it has all k = KM candidates (one or two 16-byte
-// loads; k = 4 takes 8 bytes).
-template <int KM>
-__device__ inline void load_slots_full(const uint16_t* __restrict__ irow, uint32_t (&sl)[KM]) {
-  if constexpr (KM == 4) {
-    const uint2 v = *reinterpret_cast<const uint2*>(irow);
-    sl[0] = v.x & 0xFFFF; sl[1] = v.x >> 16; sl[2] = v.y & 0xFFFF; sl[3] = v.y >> 16;
+// 16 (8) bytes at byte offset `off` from a block-uniform base: one global
+// load with the base in scalar registers and a 32-bit lane offset.
+RKV_INLINE __device__ inline u32x4 ld16(const void* base, uint32_t off) {
+  return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + off);
+}
+RKV_INLINE __device__ inline uint2 ld8(const void* base, uint32_t off) {
+  return *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(base) + off);
+}
+
+// Largest of non-negative floats over aligned groups of `lanes` lanes (4, 8
+// or 16).  For such values the bit patterns order like the values, so each
+// stage is one unsigned max with a DPP operand: swaps within quads, then
+// half-row and row mirrors.
+__device__ inline float group_max_nonneg(float v, int lanes) {
+  uint32_t u = __float_as_uint(v);
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, true));
+  if (lanes >= 8) u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, true));
+  if (lanes >= 16) u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x140, 0xF, 0xF, true));
+  return __uint_as_float(u);
+}
+
+// Low bytes of a, b, c, d as bytes 0..3 of one word (v_perm_b32 takes
+// bytes 0-3 from its second operand and 4-7 from its first; selector 0x0C
+// gives a zero byte).
+RKV_INLINE __device__ inline uint32_t low_bytes4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_amdgcn_perm(b, a, 0x0C0C0400u) | __builtin_amdgcn_perm(d, c, 0x04000C0Cu);
+}
+
+// The two's complement codes in the low bits of w[0..7], packed BITS to a
+// field in element order (element 0 lowest).  For 4 bits the even elements'
+// low nibbles stay in place and the odd elements' move up into the high
+// nibble of the same byte.
+template <int BITS>
+RKV_INLINE __device__ inline uint64_t pack8(const uint32_t (&w)[8]) {
+  if constexpr (BITS == 8) {
+    return (uint64_t)low_bytes4(w[4], w[5], w[6], w[7]) << 32 | low_bytes4(w[0], w[1], w[2], w[3]);
+  } else if constexpr (BITS == 4) {
+    const uint32_t ev = low_bytes4(w[0], w[2], w[4], w[6]);
+    const uint32_t od = low_bytes4(w[1], w[3], w[5], w[7]);
+    return (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
   } else {
+    uint32_t v = 0;
 #pragma unroll
-    for (int c = 0; c < KM / 8; ++c) {
-      const uint4 v = *reinterpret_cast<const uint4*>(irow + 8 * c);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sl[8 * c + 2 * e] = w[e] & 0xFFFF;
-        sl[8 * c + 2 * e + 1] = w[e] >> 16;
-      }
-    }
+    for (int t = 0; t < 8; ++t) v |= (w[t] & 0x3u) << (2 * t);
+    return v;
   }
 }
 
-// Mean of exactly KM selected rows (8 dims each): fixed ascending-slot fp32
-// sum, then one multiply by 1/KM (a power of two, exact) or a division.
-template <typename T, int KM, bool RQ>
-__device__ inline void ref_mean8_full(const RefSrc<T, RQ>& src, const uint32_t (&sl)[KM],
-                                      float (&m)[8]) {
-  float acc[8];
-  if constexpr (RQ) {
-    uint32_t w[KM];
-    uint16_t sb[KM];
-#pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      w[j] = *reinterpret_cast<const uint32_t*>(src.codes + sl[j] * 64u);
-      sb[j] = src.sc[sl[j] * (uint32_t)src.ng];
-    }
-    dequant8(w[0], sb[0], acc);
-#pragma unroll
-    for (int j = 1; j < KM; ++j) {
-      float r[8];
-      dequant8(w[j], sb[j], r);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + r[e];
-    }
-  } else {
-    Raw8<T> raw[KM];
-#pragma unroll
-    for (int j = 0; j < KM; ++j) load_raw8(src.raw + sl[j] * 128u, raw[j]);
-    widen8(raw[0], acc);
-#pragma unroll
-    for (int j = 1; j < KM; ++j) {
-      float r[8];
-      widen8(raw[j], r);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + r[e];
-    }
-  }
-  constexpr float inv = 1.0f / KM;  // KM is 4, 8 or 16: exact
-#pragma unroll
-  for (int e = 0; e < 8; ++e) m[e] = acc[e] * inv;
+// Raw buffer descriptor of a byte range starting at p (no range limit).
+RKV_INLINE __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, -1, 0x00020000);
 }
 
-// Loads of one position issued a step ahead on the fast path: its K or V row
-// (8 dims) and its KM slots.
+// One word of packed codes (BITS bytes) at byte offset off of a buffer.
+template <int BITS>
+RKV_INLINE __device__ inline void buffer_store_word(__amdgpu_buffer_rsrc_t r, uint32_t off, uint64_t w) {
+  if constexpr (BITS == 8) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{(uint32_t)w, (uint32_t)(w >> 32)}, r, (int)off, 0, 0);
+  } else if constexpr (BITS == 4) {
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)w, r, (int)off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)w, r, (int)off, 0, 0);
+  }
+}
+
+// Eight elements as fp32 from their raw 16 bytes (bf16) or 32 bytes (fp32).
+RKV_INLINE __device__ inline void widen(const u32x4 (&r)[1], float (&x)[8]) {
+  x[0] = bf16_lo(r[0].x); x[1] = bf16_hi(r[0].x);
+  x[2] = bf16_lo(r[0].y); x[3] = bf16_hi(r[0].y);
+  x[4] = bf16_lo(r[0].z); x[5] = bf16_hi(r[0].z);
+  x[6] = bf16_lo(r[0].w); x[7] = bf16_hi(r[0].w);
+}
+RKV_INLINE __device__ inline void widen(const u32x4 (&r)[2], float (&x)[8]) {
+  x[0] = __uint_as_float(r[0].x); x[1] = __uint_as_float(r[0].y);
+  x[2] = __uint_as_float(r[0].z); x[3] = __uint_as_float(r[0].w);
+  x[4] = __uint_as_float(r[1].x); x[5] = __uint_as_float(r[1].y);
+  x[6] = __uint_as_float(r[1].z); x[7] = __uint_as_float(r[1].w);
+}
+
+// Loads of one position issued a step ahead on the fast path: its 8
+// elements of the row and its KM slots (KM = 4: the first 8 bytes).
 template <typename T, int KM>
 struct PosLoads {
-  Raw8<T> x;
-  uint4 sl[(KM + 7) / 8];
+  u32x4 x[sizeof(T) / 2];
+  u32x4 sl[(KM + 7) / 8];
 };
 
+// The word holding slots j & ~1 and j | 1 of a position.
 template <typename T, int KM>
-__device__ inline void issue_pos_loads(const T* __restrict__ src, const uint16_t* __restrict__ idx_h,
-                                       int tok, int row, PosLoads<T, KM>& p) {
-  load_raw8(src + (uint32_t)row * 128u, p.x);
-  const uint16_t* irow = idx_h + (uint32_t)tok * KM;
-  if constexpr (KM == 4) {
-    const uint2 v = *reinterpret_cast<const uint2*>(irow);
-    p.sl[0] = make_uint4(v.x, v.y, 0, 0);
-  } else {
-#pragma unroll
-    for (int c = 0; c < KM / 8; ++c) p.sl[c] = *reinterpret_cast<const uint4*>(irow + 8 * c);
-  }
+RKV_INLINE __device__ inline uint32_t slot_word(const PosLoads<T, KM>& p, int j) {
+  const u32x4 v = p.sl[j >> 3];
+  const int q = (j >> 1) & 3;
+  return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
 }
 
-template <typename T, int KM>
-__device__ inline void unpack_slots(const PosLoads<T, KM>& p, uint32_t (&sl)[KM]) {
-#pragma unroll
-  for (int c = 0; c < (KM + 7) / 8; ++c) {
-    const uint32_t w[4] = {p.sl[c].x, p.sl[c].y, p.sl[c].z, p.sl[c].w};
-#pragma unroll
-    for (int e = 0; e < 4 && 8 * c + 2 * e < KM; ++e) {
-      sl[8 * c + 2 * e] = w[e] & 0xFFFF;
-      sl[8 * c + 2 * e + 1] = w[e] >> 16;
-    }
-  }
+// Byte offset of this lane's piece of the raw reference row whose slot is
+// the low (half = 0) or high half of w: slot * 128 * sizeof(T) + 8 * dl *
+// sizeof(T), from lane16 = 16 * dl < 256.  The bf16 offset is one byte
+// permute (byte 0 = lane16, bytes 1-2 = the slot, byte 3 = 0); fp32 doubles it.
+template <typename T>
+RKV_INLINE __device__ inline uint32_t ref_piece_off(uint32_t w, int half, uint32_t lane16) {
+  const uint32_t o = __builtin_amdgcn_perm(w, lane16, half ? 0x0C070600u : 0x0C050400u);
+  return sizeof(T) == 2 ? o : o << 1;
 }
 
-// One block = one chunk of positions of one (instance, head); 16 positions
-// per step, 32 lanes per position (16 on the K row, 16 on the V row, 8 dims
-// each).  When every position of the chunk has k = KM candidates (all but
-// the first chunks of a sequence) a position's row and slots are loaded one
-// step ahead and its mean is the unpredicated fast form; otherwise k_eff is
-// taken per position.
+// One block = one chunk of positions of one (instance, head).  Waves 0-3
+// take the K rows and waves 4-7 the V rows, so every branch on the plane is
+// uniform in a wave; a wave holds 4 positions, 16 lanes per position with 8
+// dims each, and a step covers 16 positions.  When every position of the
+// chunk has k = KM candidates (all but the first chunks of a sequence) a
+// position's row and slots are loaded one step ahead and every load is
+// unconditional (positions outside the range reread a row of the range and
+// store nothing); otherwise k_eff is taken per position.
 template <typename T, int BITS, int KM, bool RQ, bool LAT>
 __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
     const T* __restrict__ K, const T* __restrict__ V, const uint16_t* __restrict__ idx,
@@ -377,8 +335,8 @@ __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
     LatMask lm) {
   __shared__ int8_t vt[128][kVTile + 1];  // odd pitch: the 16 writing lanes hit 16 banks
   const int tid = threadIdx.x;
-  const int tok_l = tid >> 5;          // position within the step
-  const int plane = (tid >> 4) & 1;    // 0 = K, 1 = V
+  const int plane = __builtin_amdgcn_readfirstlane(tid >> 8);  // 0 = K, 1 = V
+  const int tok_l = (tid >> 4) & 15;   // position within the step
   const int dl = tid & 15;             // dims [8*dl, 8*dl+8)
   const int64_t ih = (int64_t)blockIdx.z * H + blockIdx.y;
   // positions [p0, p1) from input rows [ih][n_in][128]; chunks start on
@@ -390,83 +348,168 @@ __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
   const int v0 = c0 > p0 ? c0 : p0;
   const int n_groups = 128 / group;
   const int lanes_per_group = group >> 3;
-  // per-(instance, head) bases; positions below index them with 32-bit offsets
-  // row of position t: src + t * 128 (the base is offset by -p0 rows; only
-  // positions >= p0 are read)
-  const T* src = (plane ? V : K) + (ih * n_in - p0) * 128 + 8 * dl;
   const uint32_t vspan = (uint32_t)(c1 - v0);  // t is ours iff (uint32_t)(t - v0) < vspan
+  // Block-uniform bases at position c0: position t of the chunk is reached
+  // with the 32-bit offset (t - c0) * (bytes per position).  Positions below
+  // p0 have no input row and are never read.
+  constexpr uint32_t kRowBytes = 128 * sizeof(T);
+  const uint32_t lane16 = 16u * dl;
+  const uint32_t lane_off = 8u * dl * sizeof(T);
+  const T* xb = (plane ? V : K) + (ih * n_in + (c0 - p0)) * 128;
+  const uint16_t* ib = idx + (ih * N + c0) * k;
+  // the K codes and the scales are written through buffer descriptors (the
+  // base stays in scalar registers; each store takes a 32-bit lane offset)
+  const __amdgpu_buffer_rsrc_t kb =
+      make_rsrc(codes_k + (ih * N + c0) * (128 * BITS / 8));
+  const uint32_t k_lane = dl * BITS;
+  const __amdgpu_buffer_rsrc_t sbb =
+      make_rsrc(scales + (ih * N + c0) * 2 * n_groups + plane * n_groups);
+  const uint32_t s_lane = 2u * (dl / lanes_per_group);
+  const bool scale_lane = (dl & (lanes_per_group - 1)) == 0;
+  const T* rb = ref_kv + (ih * 2 + plane) * n_refs * 128;  // raw rows of this plane
   RefSrc<T, RQ> refs;
   refs.ng = n_groups;
   if constexpr (RQ) {
     refs.codes = reinterpret_cast<const uint8_t*>(ref_kv) + (ih * 2 + plane) * n_refs * 64 + 4 * dl;
     refs.sc = ref_scales + (ih * 2 + plane) * n_refs * n_groups + (8 * dl) / group;
   } else {
-    refs.raw = ref_kv + (ih * 2 + plane) * n_refs * 128 + 8 * dl;
+    refs.raw = rb + 8 * dl;
   }
-  const uint16_t* idx_h = idx + ih * N * k;
-  uint8_t* ck_h = codes_k + ih * N * (128 * BITS / 8) + dl * BITS;
-  uint16_t* sc_h = scales + ih * N * 2 * n_groups + plane * n_groups + dl / lanes_per_group;
   constexpr float qmax = BITS ? (float)((1 << (BITS - 1)) - 1) : 0.f;
   constexpr float inv_qmax = BITS ? 1.0f / qmax : 0.f;
   constexpr float tol = (qmax + 1.f) * 0x1p-21f;  // >= 2x the error of z * rcp(s)
   const bool fast = k == KM && sched_count_le(c0, sc) >= KM;
 
-  // Residual, scale and codes of position `tok` from its row x and mean m;
-  // writes the K codes and the scale, returns the codes (V lanes stage them).
-  auto finish = [&](int tok, const float (&x)[8], const float (&m)[8], uint32_t (&u)[8]) {
-    float z[8];
+  // Scale and codes of position c0 + r from its residual z (fp32, exact);
+  // stores the scale and (K rows) the codes when `mine`, and leaves the
+  // codes in the low bits of u (V rows stage them).
+  auto finish = [&](uint32_t r, bool mine, float (&z)[8], uint32_t (&u)[8]) RKV_INLINE {
+    if constexpr (LAT) {
+      // latent residual f_c(z) = H D z / 16 (the 16 lanes of the row share r)
+      lat_signs8(z, lm, dl);
+      fwht128_8(z, dl);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) z[e] = x[e] - m[e];
-    if constexpr (BITS == 0) {
-      double* dst = reinterpret_cast<double*>(plane ? codes_v : codes_k) +
-                    (ih * N + tok) * 128 + 8 * dl;
+      for (int e = 0; e < 8; ++e) z[e] *= 0.0625f;
+    }
+    float a = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dst[e] = (double)x[e] - (double)m[e];
+    for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(z[e]));
+    a = group_max_nonneg(a, lanes_per_group);
+    bool plain;
+    const uint16_t sbits = exact_scale_bits_plain(a, qmax, inv_qmax, plain);
+    const float s = half_bits_to_f32(sbits);
+    const float rs = s > 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;  // within 1 ulp of 1/s
+    // a scale that is not plain (rare) has every code decided exactly and clamped
+    codes8<false>(z, s, rs, qmax, tol, u, !plain);
+    if (mine && scale_lane)
+      __builtin_amdgcn_raw_buffer_store_b16(sbits, sbb, (int)(r * (4u * n_groups) + s_lane), 0, 0);
+    if (plane == 0 && mine) buffer_store_word<BITS>(kb, r * (16u * BITS) + k_lane, pack8<BITS>(u));
+  };
+  // BITS = 0: the residual kept as fp64 x - fp64 mean.
+  auto store_delta = [&](uint32_t r, const float (&x)[8], const float (&m)[8]) RKV_INLINE {
+    double* dst = reinterpret_cast<double*>(plane ? codes_v : codes_k) +
+                  (ih * N + c0 + r) * 128 + 8 * dl;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e] = (double)x[e] - (double)m[e];
+  };
+  auto issue = [&](int t, PosLoads<T, KM>& p) RKV_INLINE {
+    const uint32_t r = (uint32_t)(t - c0);
+#pragma unroll
+    for (int c = 0; c < (int)(sizeof(T) / 2); ++c)
+      p.x[c] = ld16(xb, r * kRowBytes + lane_off + 16u * c);
+    if constexpr (KM == 4) {
+      const uint2 v = ld8(ib, r * 8u);
+      p.sl[0] = u32x4{v.x, v.y, 0u, 0u};
     } else {
-      if constexpr (LAT) {
-        // latent residual f_c(z) = H D z / 16 (the 16 lanes of the row take
-        // the same branch: they share `tok`)
-        lat_signs8(z, lm, dl);
-        fwht128_8(z, dl);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] *= 0.0625f;
+      for (int c = 0; c < KM / 8; ++c) p.sl[c] = ld16(ib, r * (2u * KM) + 16u * c);
+    }
+  };
+  auto clamp_pos = [&](int t) RKV_INLINE { return min(max(t, v0), c1 - 1); };
+  // One step of the fast path: request the loads of position t + 16 into
+  // `nxt`, then finish position t from `cur`.
+  auto fast_step = [&](int t, PosLoads<T, KM>& cur, PosLoads<T, KM>& nxt,
+                       uint32_t (&u)[8]) RKV_INLINE {
+    issue(clamp_pos(t + kQTokens), nxt);
+    const bool mine = (uint32_t)(t - v0) < vspan;
+    const uint32_t r = (uint32_t)(t - c0);
+    // fixed ascending-slot fp32 sum of the KM rows (all loads first)
+    float acc[8];
+    if constexpr (RQ) {
+      uint32_t w[KM];
+      uint16_t sbr[KM];
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        const uint32_t slot = (slot_word(cur, j) >> (16 * (j & 1))) & 0xFFFFu;
+        w[j] = *reinterpret_cast<const uint32_t*>(refs.codes + slot * 64u);
+        sbr[j] = refs.sc[slot * (uint32_t)n_groups];
       }
-      float a = 0.f;
+      dequant8(w[0], sbr[0], acc);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(z[e]));
-      a = group_max(a, lanes_per_group);
-      const uint16_t sb = exact_scale_bits(a, qmax, inv_qmax);
-      const float s = half_bits_to_f32(sb);
-      const float rs = s > 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;  // within 1 ulp of 1/s
-      codes8(z, s, rs, qmax, tol, u);
-      if ((dl & (lanes_per_group - 1)) == 0) sc_h[(uint32_t)tok * (2 * n_groups)] = sb;
-      if (plane == 0) store_codes<BITS>(ck_h + (uint32_t)tok * (16 * BITS), u);
+      for (int j = 1; j < KM; ++j) {
+        float rr[8];
+        dequant8(w[j], sbr[j], rr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + rr[e];
+      }
+    } else {
+      u32x4 g[KM][sizeof(T) / 2];
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        const uint32_t o = ref_piece_off<T>(slot_word(cur, j), j & 1, lane16);
+#pragma unroll
+        for (int c = 0; c < (int)(sizeof(T) / 2); ++c) g[j][c] = ld16(rb, o + 16u * c);
+      }
+      widen(g[0], acc);
+#pragma unroll
+      for (int j = 1; j < KM; ++j) {
+        float rr[8];
+        widen(g[j], rr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + rr[e];
+      }
+    }
+    float x[8];
+    widen(cur.x, x);
+    constexpr float inv = 1.0f / KM;  // KM is 4, 8 or 16: exact
+    if constexpr (BITS == 0) {
+      float m[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m[e] = acc[e] * inv;
+      if (mine) store_delta(r, x, m);
+    } else {
+      float z[8];
+      if constexpr (sizeof(T) == 2 || RQ) {
+        // acc / KM is exact here (bf16 rows and dequantised rows are
+        // multiples of 2^-133 and 2^-24, and so is their fp32 sum), so one
+        // fma gives fl(x - fl(acc / KM)).
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = __builtin_fmaf(acc[e], -inv, x[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = x[e] - acc[e] * inv;
+      }
+      finish(r, mine, z, u);
     }
   };
-  // One step of the fast path: use the loads in `cur`, request the next
-  // step's into `nxt`.
-  auto fast_step = [&](int tok, PosLoads<T, KM>& cur, PosLoads<T, KM>& nxt, uint32_t (&u)[8]) {
-    const int tn = tok + kQTokens;
-    if ((uint32_t)(tn - v0) < vspan) issue_pos_loads<T, KM>(src, idx_h, tn, tn, nxt);
-    if ((uint32_t)(tok - v0) < vspan) {
-      uint32_t sl[KM];
-      unpack_slots<T, KM>(cur, sl);
+  auto slow_step = [&](int t, uint32_t (&u)[8]) RKV_INLINE {
+    if ((uint32_t)(t - v0) < vspan) {
+      const uint32_t r = (uint32_t)(t - c0);
       float x[8], m[8];
-      ref_mean8_full<T, KM, RQ>(refs, sl, m);
-      widen8(cur.x, x);
-      finish(tok, x, m, u);
+      load8(xb + r * 128u + 8 * dl, x);
+      const int keff = min(k, sched_count_le(t, sc));
+      ref_mean8_src<T, KM, RQ>(refs, ib + r * (uint32_t)k, k, keff, m);
+      if constexpr (BITS == 0) {
+        store_delta(r, x, m);
+      } else {
+        float z[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = x[e] - m[e];
+        finish(r, true, z, u);
+      }
     }
   };
-  auto slow_step = [&](int tok, uint32_t (&u)[8]) {
-    if ((uint32_t)(tok - v0) < vspan) {
-      float x[8], m[8];
-      load8(src + (uint32_t)tok * 128u, x);
-      const int keff = min(k, sched_count_le(tok, sc));
-      ref_mean8_src<T, KM, RQ>(refs, idx_h + (uint32_t)tok * k, k, keff, m);
-      finish(tok, x, m, u);
-    }
-  };
-  auto stage_v = [&](int sub, const uint32_t (&u)[8]) {
+  auto stage_v = [&](int sub, const uint32_t (&u)[8]) RKV_INLINE {
     if constexpr (BITS != 0) {
       if (plane == 1) {
 #pragma unroll
@@ -474,20 +517,20 @@ __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
       }
     }
   };
-  auto store_v_tile = [&](int tb) {
+  auto store_v_tile = [&](int tb) RKV_INLINE {
     if constexpr (BITS != 0) {
       __syncthreads();
-      // 512 threads: dim = tid/4, tokens 8*(tid%4) .. +7 of the tile
+      // 512 threads: dim = tid/4, positions 8*(tid%4) .. +7 of the tile
       const int dim = tid >> 2;
       const int uu = tid & 3;
-      int cc[8];
+      uint32_t cc[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) cc[e] = vt[dim][8 * uu + e];
+      for (int e = 0; e < 8; ++e) cc[e] = (uint8_t)vt[dim][8 * uu + e];
       const int64_t tile = tb / kVTile;
       uint8_t* dst = codes_v + ((ih * ((N + kVTile - 1) / kVTile) + tile) * 128 + dim) *
                                    (kVTile * BITS / 8) + uu * BITS;
       const int g0 = tb + 8 * uu;  // positions g0 .. g0+7
-      const uint64_t wv = pack_codes8<BITS>(cc);
+      const uint64_t wv = pack8<BITS>(cc);
       if (g0 >= v0 && g0 + 8 <= c1) {
         store_word<BITS>(dst, wv);
       } else {
@@ -502,10 +545,9 @@ __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
 
   if (fast) {
     PosLoads<T, KM> pa, pb;
-    if ((uint32_t)(c0 + tok_l - v0) < vspan)
-      issue_pos_loads<T, KM>(src, idx_h, c0 + tok_l, c0 + tok_l, pa);
+    issue(clamp_pos(c0 + tok_l), pa);
     for (int tb = c0; tb < c1; tb += kVTile) {
-      uint32_t u0[8] = {0, 0, 0, 0, 0, 0, 0, 0}, u1[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      uint32_t u0[8], u1[8];
       fast_step(tb + tok_l, pa, pb, u0);
       stage_v(0, u0);
       fast_step(tb + kQTokens + tok_l, pb, pa, u1);

@@ -44,6 +44,19 @@ __device__ inline uint16_t exact_scale_bits(float a, float qmax, float inv_qmax)
   return exact_scale_bits_slow(a, qmax, inv_qmax);
 }
 
+// exact_scale_bits, also telling whether the scale came from the plain
+// rounding of a normal-range estimate.  Then the scale is within a relative
+// 2^-11 of a/qmax, so |z/scale| < qmax + 1/2 for every element of the group
+// (qmax <= 127) and no code of the group needs clamping.
+__device__ inline uint16_t exact_scale_bits_plain(float a, float qmax, float inv_qmax,
+                                                  bool& plain) {
+  const float y = a * inv_qmax;
+  const int low = (int)(__float_as_uint(y) & 0x1FFFu) - 0x1000;
+  plain = y >= 0x1p-14f && y < 65504.f && (low > 3 || low < -3);
+  if (plain) return f32_to_half_bits_rne(y);
+  return exact_scale_bits_slow(a, qmax, inv_qmax);
+}
+
 // Integer nearest to z/s (ties to even), clamped to [-qmax, qmax].  s > 0.
 __device__ inline int exact_code(float z, float s, float rs, float qmax, float tol) {
   const float q = z * rs;
@@ -67,11 +80,15 @@ __device__ inline int exact_code(float z, float s, float rs, float qmax, float t
 // that rounding's remainder.  When every remainder is clear of 1/2 by more
 // than the product's error, z*rs and z/s round alike; otherwise the lane
 // decides each code exactly.  Returned as M + code (so the low bits are the
-// two's complement code), clamped to [-qmax, qmax].
+// two's complement code), clamped to [-qmax, qmax].  kClamp = false skips
+// the clamp of the estimated codes, for callers that pass exact = true
+// unless the scale keeps every code in range (exact_scale_bits_plain): the
+// exactly decided codes are always clamped.
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 
+template <bool kClamp = true>
 __device__ inline void codes8(const float (&z)[8], float s, float rs, float qmax, float tol,
-                              uint32_t (&u)[8]) {
+                              uint32_t (&u)[8], bool exact = false) {
   float t[8];
   float emax = 0.f;
 #pragma unroll
@@ -80,13 +97,14 @@ __device__ inline void codes8(const float (&z)[8], float s, float rs, float qmax
     const float r = __builtin_fmaf(z[e], rs, kMagic - t[e]);
     emax = fmaxf(emax, fabsf(r));
   }
-  if (emax > 0.5f - tol) {
+  if (exact || emax > 0.5f - tol) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[e] = kMagic + (float)exact_code(z[e], s, rs, qmax, tol);
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e)
-    u[e] = __float_as_uint(__builtin_amdgcn_fmed3f(t[e], kMagic - qmax, kMagic + qmax));
+    u[e] = __float_as_uint(kClamp ? __builtin_amdgcn_fmed3f(t[e], kMagic - qmax, kMagic + qmax)
+                                  : t[e]);
 }
 
 // Exact group quantisation of one value: scale bits of the group (a = the
