@@ -28,9 +28,9 @@
 //              as unsigned 64-bit fixed point (units of 2^-32: integer LDS
 //              atomics are far faster than float ones here).  The block
 //              writes (m, l, O, W) per query head.
-//   k_combine  one block per (instance, KV head): merges the splits, adds
-//              W . Vref (each Vref row read once for all query heads) and
-//              normalises.
+//   k_combine  one block per (instance, query head): merges the splits,
+//              adds W . Vref and normalises, with its loads requested up
+//              front.
 #include <float.h>
 
 #include <type_traits>
@@ -737,177 +737,215 @@ __global__ __launch_bounds__(256, 2) void k_decode(
 }
 
 // ------------------------------------------------------------------ combine
-// One block per (instance, KV head): merge the splits of its G query heads
-// (maximum, softmax sum, P.V partials and the reference weights W), then add
-// W . Vref.  W is merged once into LDS; each thread then takes DPT
-// consecutive dims of all G heads over a stride of the references, reading
-// each reference row chunk as one vector, and the stride groups are summed
-// in LDS.  W . Vref runs over the n_valid written references only.
-// GM bounds G: 8 (8 dims per thread) or 16 (4 dims per thread).
-template <int GM>
-struct CombShape {
-  static constexpr int DPT = GM > 8 ? 4 : 8;  // dims per thread
-  static constexpr int TPR = 128 / DPT;       // threads per reference row
-  static constexpr int RG = 256 / TPR;        // reference stride groups
+// One block of 1024 threads per (instance, query head): merge the head's
+// splits (maximum, softmax sum, P.V partials and the reference weights W),
+// then add W . Vref over the n_valid written references and normalise.
+// Every global load is requested up front (the first comb_rows reference
+// rows of each thread, the first kCombSplits partial records of W and of
+// P.V), so the merge costs about two memory round trips.  Thread (dg, rg)
+// takes dims 8*dg .. 8*dg+7 of references rg, rg + 64, ...; the 64 stride
+// groups are summed in LDS.
+constexpr int kCombThreads = 1024;
+constexpr int kCombRG = kCombThreads / 16;  // reference stride groups
+template <typename T>
+constexpr int comb_rows() { return sizeof(T) == 2 ? 8 : 4; }  // reference rows per thread requested up front
+constexpr int kCombSplits = 8;              // partial records requested up front
+
+// Dims d0 .. d0+7 of V reference row j, loaded as raw bits (bf16: one
+// 16-byte word; fp32: two; int4 rows: the nibble word and the group scale)
+// and widened to fp32 at use (exact).
+template <typename T>
+struct VRow {
+  u32x4 v[sizeof(T) / 2];
 };
 
-// DPT dims (d0 ..) of reference row j as fp32: raw rows of T, or int4
-// nibbles times the row's group scale (exact).
-template <typename T, int DPT>
-__device__ inline void vref_chunk(const T* __restrict__ raw, const uint8_t* __restrict__ q4,
-                                  const uint16_t* __restrict__ rsc, int ng, int group,
-                                  int ref_bits, int64_t j, int d0, float (&x)[DPT]) {
+template <typename T>
+__device__ inline void vrow_load(const T* __restrict__ raw, const uint8_t* __restrict__ q4,
+                                 const uint16_t* __restrict__ rsc, int ng, int group, int ref_bits,
+                                 int64_t j, int d0, VRow<T>& r) {
   if (ref_bits == 4) {
-    const float s = half_bits_to_f32(rsc[j * ng + d0 / group]);
-    const uint32_t w = DPT == 8 ? *reinterpret_cast<const uint32_t*>(q4 + j * 64 + d0 / 2)
-                                : (uint32_t)*reinterpret_cast<const uint16_t*>(q4 + j * 64 + d0 / 2);
-#pragma unroll
-    for (int e = 0; e < DPT; ++e) x[e] = (float)((int32_t)(w << (28 - 4 * e)) >> 28) * s;
-  } else if constexpr (DPT == 8) {
-    load8(raw + j * 128 + d0, x);
-  } else if constexpr (sizeof(T) == 2) {
-    const uint2 w = *reinterpret_cast<const uint2*>(raw + j * 128 + d0);
-    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    r.v[0].x = *reinterpret_cast<const uint32_t*>(q4 + j * 64 + d0 / 2);
+    r.v[0].y = rsc[j * ng + d0 / group];
   } else {
-    const float4 v = *reinterpret_cast<const float4*>(raw + j * 128 + d0);
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+#pragma unroll
+    for (int c = 0; c < (int)(sizeof(T) / 2); ++c)
+      r.v[c] = *reinterpret_cast<const u32x4*>(raw + j * 128 + d0 + c * (16 / sizeof(T)));
   }
 }
 
-template <typename T, int GM>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
-                                                 const T* __restrict__ ref_kv,
-                                                 const uint16_t* __restrict__ ref_scales,
-                                                 int ref_bits, int group,
-                                                 float* __restrict__ out, int G, int H,
-                                                 int64_t n_refs, int64_t n_valid, int n_split,
-                                                 float* __restrict__ ores) {
-  using S = CombShape<GM>;
-  constexpr int DPT = S::DPT, TPR = S::TPR, RG = S::RG;
+template <typename T>
+__device__ inline void vrow_widen(const VRow<T>& r, int ref_bits, float (&x)[8]) {
+  if (ref_bits == 4) {
+    const float s = half_bits_to_f32((uint16_t)r.v[0].y);
+    const uint32_t w = r.v[0].x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)((int32_t)(w << (28 - 4 * e)) >> 28) * s;
+  } else if constexpr (sizeof(T) == 2) {
+    x[0] = bf16_lo(r.v[0].x); x[1] = bf16_hi(r.v[0].x);
+    x[2] = bf16_lo(r.v[0].y); x[3] = bf16_hi(r.v[0].y);
+    x[4] = bf16_lo(r.v[0].z); x[5] = bf16_hi(r.v[0].z);
+    x[6] = bf16_lo(r.v[0].w); x[7] = bf16_hi(r.v[0].w);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      x[4 * c + 0] = __uint_as_float(r.v[c].x); x[4 * c + 1] = __uint_as_float(r.v[c].y);
+      x[4 * c + 2] = __uint_as_float(r.v[c].z); x[4 * c + 3] = __uint_as_float(r.v[c].w);
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kCombThreads) void k_combine(const float* __restrict__ part,
+                                                          const T* __restrict__ ref_kv,
+                                                          const uint16_t* __restrict__ ref_scales,
+                                                          int ref_bits, int group,
+                                                          float* __restrict__ out, int G, int H,
+                                                          int64_t n_refs, int64_t n_valid,
+                                                          int n_split, float* __restrict__ ores) {
   extern __shared__ float cs[];
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
-  float* wt = cs;                   // [G][nrp] merged W
-  float* fs = wt + G * nrp;         // [G][n_split] split factors
-  float* ls_ = fs + G * n_split;    // [16] l
-  float* red = ls_ + 16;            // [RG][G][128] partial W . Vref
+  float* wt = cs;               // [nrp] merged W
+  float* fs = wt + nrp;         // [n_split] split factors
+  float* sm = fs + n_split;     // [2]: l, and [128] merged P.V at sm + 4
+  float* red = sm + 132;        // [kCombRG][128] partial W . Vref
   const int kvh = blockIdx.x;
   const int64_t inst = blockIdx.y;
+  const int hq = kvh * G + (int)blockIdx.z;
   const int Hq = H * G;
   const int tid = threadIdx.x;
   const int64_t rec = part_rec_floats(n_refs);
-  const float* base = part + (inst * Hq + kvh * G) * n_split * rec;  // head h at + h*n_split*rec
-  // W . Vref operands: thread (dg, rg) takes dims d0 .. d0+DPT-1 of references
-  // rg, rg+RG, ...; the first kUnroll rows are requested before the merges
-  constexpr int kUnroll = 8;
-  const int dg = tid % TPR, rg = tid / TPR;
-  const int d0 = dg * DPT;
+  const float* base = part + (inst * Hq + hq) * n_split * rec;  // split s at base + s * rec
+
+  // reference rows for W . Vref
+  const int dg = tid & 15, rg = tid >> 4;
+  const int d0 = dg * 8;
   const int64_t row0 = ((inst * H + kvh) * 2 + 1) * n_refs;  // V plane
   const int ngq = ref_bits == 4 ? 128 / group : 1;
   const T* raw = ref_kv + row0 * 128;
   const uint8_t* q4 = reinterpret_cast<const uint8_t*>(ref_kv) + row0 * 64;
   const uint16_t* rsc = ref_bits == 4 ? ref_scales + row0 * ngq : nullptr;
-  float x[kUnroll][DPT];
-  if (rg + (kUnroll - 1) * RG < n_valid) {
+  constexpr int kCombRows = comb_rows<T>();
+  VRow<T> xr[kCombRows];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      vref_chunk<T, DPT>(raw, q4, rsc, ngq, group, ref_bits, rg + u * RG, d0, x[u]);
+  for (int u = 0; u < kCombRows; ++u) {
+    const int64_t j = rg + (int64_t)u * kCombRG;
+    if (j < n_valid) vrow_load<T>(raw, q4, rsc, ngq, group, ref_bits, j, d0, xr[u]);
   }
-  if (tid < G) {
-    const float* b = base + tid * n_split * rec;
+  // roles for the merges: wave 0 the maximum and the sum, threads 64 .. 64 +
+  // nrp/4 - 1 a float4 of W each (while nrp/4 <= 896), threads 960 .. 1023
+  // two dims of P.V each
+  const int64_t wc = tid - 64;  // W chunk of this thread
+  const bool w_role = wc >= 0 && wc < nrp / 4 && wc < 896;
+  const int od = 2 * (tid - 960);  // P.V dims od, od + 1
+  const bool o_role = tid >= 960;
+  float4 wv[kCombSplits];
+  float2 ov[kCombSplits];
+  if (w_role) {
+#pragma unroll
+    for (int s = 0; s < kCombSplits; ++s)
+      if (s < n_split) wv[s] = *reinterpret_cast<const float4*>(base + s * rec + 132 + 4 * wc);
+  }
+  if (o_role) {
+#pragma unroll
+    for (int s = 0; s < kCombSplits; ++s)
+      if (s < n_split) ov[s] = *reinterpret_cast<const float2*>(base + s * rec + 4 + od);
+  }
+  if (tid < 64) {
     float M = -INFINITY;
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, b[s * rec]);
+    for (int s = tid; s < n_split; s += 64) M = fmaxf(M, base[s * rec]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     float l = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      const float m = b[s * rec];
+    for (int s = tid; s < n_split; s += 64) {
+      const float m = base[s * rec];
       const float f = m > -INFINITY ? __expf(m - M) : 0.f;
-      fs[tid * n_split + s] = f;
-      l += f * b[s * rec + 1];
+      fs[s] = f;
+      l += f * base[s * rec + 1];
     }
-    ls_[tid] = l;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+    if (tid == 0) sm[0] = l;
   }
   __syncthreads();
-  // merged W, float4 at a time
-  for (int64_t e = tid; e < (int64_t)G * (nrp / 4); e += 256) {
-    const int h = (int)(e / (nrp / 4));
-    const int64_t c = e - (int64_t)h * (nrp / 4);
-    const float* b = base + h * n_split * rec + 132 + 4 * c;
+  // merged W (float4 chunks) and merged P.V
+  for (int64_t c = wc; wc >= 0 && wc < 896 && c < nrp / 4; c += 896) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     int s = 0;
-    for (; s + 8 <= n_split; s += 8) {
-      float4 v[8];
+    if (c == wc && w_role) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(b + (s + u) * rec);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float f = fs[h * n_split + s + u];
-        acc.x += f * v[u].x; acc.y += f * v[u].y; acc.z += f * v[u].z; acc.w += f * v[u].w;
-      }
-    }
-    for (; s < n_split; ++s) {
-      const float f = fs[h * n_split + s];
-      const float4 v = *reinterpret_cast<const float4*>(b + s * rec);
-      acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
-    }
-    *reinterpret_cast<float4*>(wt + h * nrp + 4 * c) = acc;
-  }
-  __syncthreads();
-  float a[GM][DPT];
-#pragma unroll
-  for (int h = 0; h < GM; ++h)
-#pragma unroll
-    for (int e = 0; e < DPT; ++e) a[h][e] = 0.f;
-  int64_t j = rg;
-  for (; j + (kUnroll - 1) * RG < n_valid; j += kUnroll * RG) {
-    if (j != rg) {  // the first batch was requested before the merges
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-        vref_chunk<T, DPT>(raw, q4, rsc, ngq, group, ref_bits, j + u * RG, d0, x[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-#pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        if (h < G) {
-          const float wj = wt[h * nrp + j + u * RG];
-#pragma unroll
-          for (int e = 0; e < DPT; ++e) a[h][e] = __builtin_fmaf(wj, x[u][e], a[h][e]);
+      for (int u = 0; u < kCombSplits; ++u) {
+        if (u < n_split) {
+          const float f = fs[u];
+          acc.x += f * wv[u].x; acc.y += f * wv[u].y; acc.z += f * wv[u].z; acc.w += f * wv[u].w;
         }
       }
+      s = kCombSplits;
     }
+    for (; s < n_split; ++s) {
+      const float f = fs[s];
+      const float4 v = *reinterpret_cast<const float4*>(base + s * rec + 132 + 4 * c);
+      acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
+    }
+    *reinterpret_cast<float4*>(wt + 4 * c) = acc;
   }
-  for (; j < n_valid; j += RG) {
-    float x[DPT];
-    vref_chunk<T, DPT>(raw, q4, rsc, ngq, group, ref_bits, j, d0, x);
+  if (o_role) {
+    float2 acc = make_float2(0.f, 0.f);
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      if (h < G) {
-        const float wj = wt[h * nrp + j];
-#pragma unroll
-        for (int e = 0; e < DPT; ++e) a[h][e] = __builtin_fmaf(wj, x[e], a[h][e]);
+    for (int u = 0; u < kCombSplits; ++u) {
+      if (u < n_split) {
+        acc.x += fs[u] * ov[u].x;
+        acc.y += fs[u] * ov[u].y;
       }
     }
+    for (int s = kCombSplits; s < n_split; ++s) {
+      const float2 v = *reinterpret_cast<const float2*>(base + s * rec + 4 + od);
+      acc.x += fs[s] * v.x;
+      acc.y += fs[s] * v.y;
+    }
+    sm[4 + od] = acc.x;
+    sm[4 + od + 1] = acc.y;
+  }
+  __syncthreads();
+  // W . Vref
+  float a[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = 0.f;
+#pragma unroll
+  for (int u = 0; u < kCombRows; ++u) {
+    const int64_t j = rg + (int64_t)u * kCombRG;
+    if (j < n_valid) {
+      const float wj = wt[j];
+      float x[8];
+      vrow_widen<T>(xr[u], ref_bits, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = __builtin_fmaf(wj, x[e], a[e]);
+    }
+  }
+  for (int64_t j = rg + (int64_t)kCombRows * kCombRG; j < n_valid; j += kCombRG) {
+    float y[8];
+    VRow<T> yr;
+    vrow_load<T>(raw, q4, rsc, ngq, group, ref_bits, j, d0, yr);
+    vrow_widen<T>(yr, ref_bits, y);
+    const float wj = wt[j];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = __builtin_fmaf(wj, y[e], a[e]);
   }
 #pragma unroll
-  for (int h = 0; h < GM; ++h)
-    if (h < G)
-#pragma unroll
-      for (int e = 0; e < DPT; ++e) red[(rg * G + h) * 128 + d0 + e] = a[h][e];
+  for (int e = 0; e < 8; ++e) red[rg * 128 + d0 + e] = a[e];
   __syncthreads();
-  for (int e = tid; e < G * 128; e += 256) {
-    const int h = e / 128, d = e % 128;
+  if (tid < 128) {
     float s = 0.f;
-    for (int x = 0; x < RG; ++x) s += red[(x * G + h) * 128 + d];
-    const float* b = base + h * n_split * rec + 4 + d;
-    float o = 0.f;
-    for (int x = 0; x < n_split; ++x) o += fs[h * n_split + x] * b[x * rec];
-    const int64_t at = (inst * Hq + kvh * G + h) * 128 + d;
+    for (int g = 0; g < kCombRG; ++g) s += red[g * 128 + tid];
+    const float l = sm[0];
+    const float o = sm[4 + tid];
+    const int64_t at = (inst * Hq + hq) * 128 + tid;
     if (ores) {
       // latent codes: the residual part is still rotated; f_d is applied
       // to the whole row afterwards
-      ores[at] = o / ls_[h];
-      out[at] = s / ls_[h];
+      ores[at] = o / l;
+      out[at] = s / l;
     } else {
-      out[at] = (o + s) / ls_[h];
+      out[at] = (o + s) / l;
     }
   }
 }
@@ -993,9 +1031,9 @@ size_t decode_lds_bytes(int G, int NG, int64_t n_refs) {
 }
 
 size_t combine_lds_bytes(int G, int64_t n_refs, int n_split) {
+  (void)G;
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
-  const int RG = G > 8 ? CombShape<16>::RG : CombShape<8>::RG;
-  return (size_t)(G * nrp + G * n_split + 16 + RG * G * 128) * 4;
+  return (size_t)(nrp + n_split + 132 + kCombRG * 128) * 4;
 }
 
 // Whether the decode kernels' LDS fits one CU (160 KiB).
@@ -1046,13 +1084,14 @@ hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t clds = combine_lds_bytes(G, n_refs, n_split);
-  auto comb = G > 8 ? k_combine<T, 16> : k_combine<T, 8>;
+  auto comb = k_combine<T>;
   if (clds > 64 * 1024) {
     e = hipFuncSetAttribute((const void*)comb, hipFuncAttributeMaxDynamicSharedMemorySize, (int)clds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(comb, dim3(H, (unsigned)n_inst), dim3(256), clds, st, part, (const T*)ref_kv,
-                     ref_scales, ref_bits, group_r, out, G, H, n_refs, n_valid, n_split, ores);
+  hipLaunchKernelGGL(comb, dim3(H, (unsigned)n_inst, G), dim3(kCombThreads), clds, st, part,
+                     (const T*)ref_kv, ref_scales, ref_bits, group_r, out, G, H, n_refs, n_valid,
+                     n_split, ores);
   e = hipGetLastError();
   if (e != hipSuccess || !lm) return e;
   hipLaunchKernelGGL(k_latent_out, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, ores, *lm,
