@@ -180,9 +180,13 @@ DECODE = [
     ("gqa7_g64_int2", _cfg(4, n_kv_heads=2, n_q_heads=14, batch=1), 2, 2, 500),
     ("gqa7_g64_int4", _cfg(4, n_kv_heads=2, n_q_heads=14, batch=1), 4, 1, 500),
     ("g128_gqa4", _cfg(1, n_kv_heads=1, n_q_heads=4, group=128), 4, 1, 300),
-    # more than 8 query heads per KV head: the combine's 4-dims-per-thread form
+    # more than 8 query heads per KV head
     ("g128_gqa16_bf16", _cfg(1, n_kv_heads=2, n_q_heads=32, group=128), 4, 1, 700),
     ("g128_gqa12_f32_int8", _cfg(0, n_kv_heads=1, n_q_heads=12, group=128), 8, 1, 500),
+    # more references than the combine requests up front per thread (512 bf16
+    # rows, 256 fp32 rows): the rest of W . Vref is read in its tail loop
+    ("many_refs_bf16", _cfg(1, n_kv_heads=1, n_q_heads=4, stride_base=4), 4, 1, 3000),
+    ("many_refs_f32", _cfg(0, n_kv_heads=1, n_q_heads=4, stride_base=4), 4, 1, 1500),
 ]
 
 
