@@ -737,16 +737,16 @@ __global__ __launch_bounds__(256, 2) void k_decode(
 }
 
 // ------------------------------------------------------------------ combine
-// One block of 1024 threads per (instance, query head): merge the head's
+// One block of CT threads per (instance, query head): merge the head's
 // splits (maximum, softmax sum, P.V partials and the reference weights W),
 // then add W . Vref over the n_valid written references and normalise.
 // Every global load is requested up front (the first comb_rows reference
 // rows of each thread, the first kCombSplits partial records of W and of
 // P.V), so the merge costs about two memory round trips.  Thread (dg, rg)
-// takes dims 8*dg .. 8*dg+7 of references rg, rg + 64, ...; the 64 stride
-// groups are summed in LDS.
-constexpr int kCombThreads = 1024;
-constexpr int kCombRG = kCombThreads / 16;  // reference stride groups
+// takes dims 8*dg .. 8*dg+7 of references rg, rg + CT/16, ...; the CT/16
+// stride groups are summed in LDS.
+// CT threads per block: 1024 when the launch has few blocks (one layer),
+// 256 when it has many (several blocks per CU then hide the latency).
 template <typename T>
 constexpr int comb_rows() { return sizeof(T) == 2 ? 8 : 4; }  // reference rows per thread requested up front
 constexpr int kCombSplits = 8;              // partial records requested up front
@@ -794,14 +794,16 @@ __device__ inline void vrow_widen(const VRow<T>& r, int ref_bits, float (&x)[8])
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(kCombThreads) void k_combine(const float* __restrict__ part,
+template <typename T, int CT>
+__global__ __launch_bounds__(CT) void k_combine(const float* __restrict__ part,
                                                           const T* __restrict__ ref_kv,
                                                           const uint16_t* __restrict__ ref_scales,
                                                           int ref_bits, int group,
                                                           float* __restrict__ out, int G, int H,
                                                           int64_t n_refs, int64_t n_valid,
                                                           int n_split, float* __restrict__ ores) {
+  constexpr int kCombRG = CT / 16;  // reference stride groups
+  constexpr int kWThreads = CT - 128;  // threads merging W (float4 chunks)
   extern __shared__ float cs[];
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
   float* wt = cs;               // [nrp] merged W
@@ -831,13 +833,13 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(const float* __restric
     const int64_t j = rg + (int64_t)u * kCombRG;
     if (j < n_valid) vrow_load<T>(raw, q4, rsc, ngq, group, ref_bits, j, d0, xr[u]);
   }
-  // roles for the merges: wave 0 the maximum and the sum, threads 64 .. 64 +
-  // nrp/4 - 1 a float4 of W each (while nrp/4 <= 896), threads 960 .. 1023
-  // two dims of P.V each
-  const int64_t wc = tid - 64;  // W chunk of this thread
-  const bool w_role = wc >= 0 && wc < nrp / 4 && wc < 896;
-  const int od = 2 * (tid - 960);  // P.V dims od, od + 1
-  const bool o_role = tid >= 960;
+  // roles for the merges: wave 0 the maximum and the sum, threads 64 ..
+  // CT - 65 float4 chunks of W (chunk c, c + CT - 128, ...), the last 64
+  // threads two dims of P.V each
+  const int64_t wc = tid - 64;  // first W chunk of this thread
+  const bool w_role = wc >= 0 && wc < nrp / 4 && wc < kWThreads;
+  const int od = 2 * (tid - (CT - 64));  // P.V dims od, od + 1
+  const bool o_role = tid >= CT - 64;
   float4 wv[kCombSplits];
   float2 ov[kCombSplits];
   if (w_role) {
@@ -868,7 +870,7 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(const float* __restric
   }
   __syncthreads();
   // merged W (float4 chunks) and merged P.V
-  for (int64_t c = wc; wc >= 0 && wc < 896 && c < nrp / 4; c += 896) {
+  for (int64_t c = wc; wc >= 0 && wc < kWThreads && c < nrp / 4; c += kWThreads) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     int s = 0;
     if (c == wc && w_role) {
@@ -921,14 +923,25 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(const float* __restric
       for (int e = 0; e < 8; ++e) a[e] = __builtin_fmaf(wj, x[e], a[e]);
     }
   }
-  for (int64_t j = rg + (int64_t)kCombRows * kCombRG; j < n_valid; j += kCombRG) {
-    float y[8];
-    VRow<T> yr;
-    vrow_load<T>(raw, q4, rsc, ngq, group, ref_bits, j, d0, yr);
-    vrow_widen<T>(yr, ref_bits, y);
-    const float wj = wt[j];
+  // the rest in batches of kCombRows rows, all of a batch's loads first
+  for (int64_t j0 = rg + (int64_t)kCombRows * kCombRG; j0 < n_valid; j0 += (int64_t)kCombRows * kCombRG) {
+    VRow<T> yr[kCombRows];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a[e] = __builtin_fmaf(wj, y[e], a[e]);
+    for (int u = 0; u < kCombRows; ++u) {
+      const int64_t j = j0 + (int64_t)u * kCombRG;
+      if (j < n_valid) vrow_load<T>(raw, q4, rsc, ngq, group, ref_bits, j, d0, yr[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kCombRows; ++u) {
+      const int64_t j = j0 + (int64_t)u * kCombRG;
+      if (j < n_valid) {
+        float y[8];
+        vrow_widen<T>(yr[u], ref_bits, y);
+        const float wj = wt[j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = __builtin_fmaf(wj, y[e], a[e]);
+      }
+    }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[rg * 128 + d0 + e] = a[e];
@@ -1033,7 +1046,7 @@ size_t decode_lds_bytes(int G, int NG, int64_t n_refs) {
 size_t combine_lds_bytes(int G, int64_t n_refs, int n_split) {
   (void)G;
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
-  return (size_t)(nrp + n_split + 132 + kCombRG * 128) * 4;
+  return (size_t)(nrp + n_split + 132 + (1024 / 16) * 128) * 4;  // the 1024-thread form
 }
 
 // Whether the decode kernels' LDS fits one CU (160 KiB).
@@ -1083,13 +1096,15 @@ hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
                      n_split, tile_list, n_list, qrot);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // 1024-thread blocks while the launch has at most about two blocks per CU
+  const bool wide = (int64_t)H * n_inst * G <= 512;
   const size_t clds = combine_lds_bytes(G, n_refs, n_split);
-  auto comb = k_combine<T>;
+  auto comb = wide ? k_combine<T, 1024> : k_combine<T, 256>;
   if (clds > 64 * 1024) {
     e = hipFuncSetAttribute((const void*)comb, hipFuncAttributeMaxDynamicSharedMemorySize, (int)clds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(comb, dim3(H, (unsigned)n_inst, G), dim3(kCombThreads), clds, st, part,
+  hipLaunchKernelGGL(comb, dim3(H, (unsigned)n_inst, G), dim3(wide ? 1024 : 256), clds, st, part,
                      (const T*)ref_kv, ref_scales, ref_bits, group_r, out, G, H, n_refs, n_valid,
                      n_split, ores);
   e = hipGetLastError();

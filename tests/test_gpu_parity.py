@@ -205,6 +205,25 @@ def _oracle_decode(cfg, K, V, q, bits, scale, ref_bits=0, latent_seed=None):
     return out
 
 
+def test_decode_parity_many_blocks():
+    """More than 512 (instance, query head) pairs: the combine runs as
+    256-thread blocks instead of 1024-thread ones."""
+    _need_gpu()
+    cfg = _cfg(1, n_kv_heads=8, n_q_heads=32, batch=17)
+    n_inst, N, bits = 17, 300, 4
+    say(f"[decode parity, many blocks] inst={n_inst} Hkv=8 Hq=32 N={N}")
+    K, V = make_kv(cfg, n_inst, N)
+    q = make_q(cfg, n_inst)
+    cache = encode(cfg, K, V, bits, n_inst, N)
+    Kn, Vn, qn = to_np_f32(K), to_np_f32(V), to_np_f32(q)
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    got = rkv.rkv_decode_attn(q, cfg.n_q_heads, cache, scale, n_split=3).cpu().numpy()
+    want = _oracle_decode(cfg, Kn, Vn, qn, bits, scale)
+    err = rel_l2(got, want)
+    say(f"  rel L2 = {err:.2e}")
+    assert err <= 2e-3
+
+
 @pytest.mark.parametrize("case", DECODE, ids=[c[0] for c in DECODE])
 def test_decode_parity(case):
     _need_gpu()
