@@ -108,6 +108,30 @@ def test_encode_parity_small(case):
     say(f"  near-ties: {near} of {n_inst * cfg.n_kv_heads * N} tokens")
 
 
+# (dtype, bits, log2 of the input scaling): residual scales in the fp16
+# subnormal range, rounded to zero, or saturated at 65504.  Those scales are
+# not the plain rounding of a normal-range estimate, so every code of their
+# groups is decided exactly and clamped.
+EXTREME = [("bf16", 4, -20), ("bf16", 2, -22), ("f32", 4, -30), ("bf16", 4, 20), ("f32", 8, 24)]
+
+
+@pytest.mark.parametrize("case", EXTREME, ids=[f"{d}_int{b}_2^{e}" for d, b, e in EXTREME])
+def test_encode_parity_extreme_magnitudes(case):
+    _need_gpu()
+    dtype, bits, e = case
+    cfg = _cfg(1, n_kv_heads=1, dtype=dtype)
+    N = 800
+    say(f"[encode parity, inputs x 2^{e}] {dtype} bits={bits}")
+    K, V = make_kv(cfg, 1, N)
+    K.mul_(2.0 ** e)  # a power of two: exact at these magnitudes
+    V.mul_(2.0 ** e)
+    cache = encode(cfg, K, V, bits, 1, N)
+    gc = GpuCache(cache)
+    r = compare_encode(gc, 0, to_np_f32(K[0, 0]), to_np_f32(V[0, 0]), cfg.stride_base,
+                       cfg.double_after)
+    say(f"  near-ties: {r['near_ties']}")
+
+
 @pytest.mark.parametrize("case", SMALL[:6], ids=[c[0] for c in SMALL[:6]])
 def test_reconstruct_parity_small(case):
     _need_gpu()
