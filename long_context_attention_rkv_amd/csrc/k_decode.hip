@@ -136,10 +136,11 @@ __host__ __device__ inline int64_t part_rec_floats(int64_t n_refs) {
 }
 
 // ------------------------------------------------------------------ QK table
-// QK[inst][hq][slot] = q_hq . Kref_slot in fp32; one thread per reference,
-// whole row loaded before the dot products.  Rows of the table are padded to
-// a multiple of 4 (nrp) with zeros.
-// Rows from n_valid on (references not written yet) are zero.
+// QK[inst][hq][slot] = q_hq . Kref_slot in fp32.  Four lanes per reference
+// (32 dims each, the row piece loaded whole before the products), summed
+// across the quad with DPP.  Rows of the table are padded to a multiple of 4
+// (nrp) with zeros; rows from n_valid on (references not written yet) are
+// zero.
 template <typename T>
 __global__ __launch_bounds__(256) void k_qk_table(const T* __restrict__ q,
                                                   const T* __restrict__ ref_kv,
@@ -147,46 +148,44 @@ __global__ __launch_bounds__(256) void k_qk_table(const T* __restrict__ q,
                                                   int ref_bits, int group,
                                                   float* __restrict__ qk, int G, int H,
                                                   int64_t n_refs, int64_t n_valid) {
-  __shared__ float qs[16 * 128];
+  // q rows as [head][part][33]: the four parts of a quad read different banks
+  __shared__ float qs[16 * 4 * 33];
   const int kvh = blockIdx.y;
   const int64_t inst = blockIdx.z;
   const int Hq = H * G;
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
   const T* qh = q + (inst * Hq + kvh * G) * 128;
-  for (int e = threadIdx.x; e < G * 128; e += 256) qs[e] = (float)qh[e];
+  for (int e = threadIdx.x; e < G * 128; e += 256)
+    qs[(e >> 5) * 33 + (e & 31)] = (float)qh[e];
   __syncthreads();
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (j >= nrp) return;
+  const int part = threadIdx.x & 3;  // dims 32*part .. +31
+  const int64_t j = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+  if (j >= nrp) return;  // whole quads leave together
   float* out = qk + (inst * Hq + kvh * G) * nrp + j;
-  if (j >= n_valid) {
-    for (int h = 0; h < G; ++h) out[h * nrp] = 0.f;
-    return;
-  }
-  float x[128];
+  const bool live = j < n_valid;
+  const int64_t jr = live ? j : 0;  // rows past n_valid compute on row 0 and store 0
+  float x[32];
   if (ref_bits == 4) {
     // quantised reference: nibbles times the fp16 scale of their group (exact)
     const int ng = 128 / group;
-    const int64_t r = ((inst * H + kvh) * 2 + 0) * n_refs + j;
-    const uint4* cw = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(ref_kv) + r * 64);
+    const int64_t r = ((inst * H + kvh) * 2 + 0) * n_refs + jr;
+    const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(ref_kv) +
+                                                    r * 64 + 16 * part);
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
     const uint16_t* sr = ref_scales + r * ng;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint4 v = cw[c];
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    for (int u = 0; u < 4; ++u) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int t = 32 * c + 8 * u + e;
-          const float s = half_bits_to_f32(sr[t / group]);
-          x[t] = (float)((int32_t)(w4[u] << (28 - 4 * e)) >> 28) * s;
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int t = 8 * u + e;
+        const float s = half_bits_to_f32(sr[(32 * part + t) / group]);
+        x[t] = (float)((int32_t)(w4[u] << (28 - 4 * e)) >> 28) * s;
       }
     }
   } else {
-    const T* row = ref_kv + ((inst * H + kvh) * 2 + 0) * n_refs * 128 + j * 128;
+    const T* row = ref_kv + ((inst * H + kvh) * 2 + 0) * n_refs * 128 + jr * 128 + 32 * part;
 #pragma unroll
-    for (int t = 0; t < 128; t += 8) {
+    for (int t = 0; t < 32; t += 8) {
       float v[8];
       load8(row + t, v);
 #pragma unroll
@@ -196,8 +195,10 @@ __global__ __launch_bounds__(256) void k_qk_table(const T* __restrict__ q,
   for (int h = 0; h < G; ++h) {
     float acc = 0.f;
 #pragma unroll
-    for (int t = 0; t < 128; ++t) acc = __builtin_fmaf(qs[h * 128 + t], x[t], acc);
-    out[h * nrp] = acc;
+    for (int t = 0; t < 32; ++t) acc = __builtin_fmaf(qs[(4 * h + part) * 33 + t], x[t], acc);
+    acc += RKV_DPP_F32(acc, 0xB1);  // quad_perm [1,0,3,2]
+    acc += RKV_DPP_F32(acc, 0x4E);  // quad_perm [2,3,0,1]
+    if (part == 0) out[h * nrp] = live ? acc : 0.f;
   }
 }
 
@@ -1080,7 +1081,7 @@ hipError_t launch_decode_t(const void* q, int n_q_heads, const uint16_t* idx,
   }
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
   const int64_t n_valid = sched_count((int32_t)len, sc);
-  hipLaunchKernelGGL(k_qk_table<T>, dim3((unsigned)((nrp + 255) / 256), H, (unsigned)n_inst),
+  hipLaunchKernelGGL(k_qk_table<T>, dim3((unsigned)((nrp + 63) / 64), H, (unsigned)n_inst),
                      dim3(256), 0, st, (const T*)q, (const T*)ref_kv, ref_scales, ref_bits,
                      group_r, qk, G, H, n_refs, n_valid);
   hipError_t e = hipGetLastError();
