@@ -506,9 +506,25 @@ __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
                           keff < 1 ? 1 : keff, sel);
     if (c ? valid_row[1] : valid_row[0]) {
       uint16_t* orow = idx_out + (ih * N + row0 + 32 * c + n) * k;
+      if (k == KM) {
+        // the whole row as 16-byte words (rows are 2k-byte aligned)
+        uint32_t wv[KM / 2];
 #pragma unroll
-      for (int t = 0; t < KM; ++t)
-        if (t < k) orow[t] = (uint16_t)sel[t];
+        for (int t = 0; t < KM / 2; ++t)
+          wv[t] = (uint32_t)sel[2 * t] | ((uint32_t)sel[2 * t + 1] << 16);
+        if constexpr (KM == 4) {
+          *reinterpret_cast<uint2*>(orow) = make_uint2(wv[0], wv[1]);
+        } else {
+#pragma unroll
+          for (int t = 0; t < KM / 8; ++t)
+            reinterpret_cast<uint4*>(orow)[t] =
+                make_uint4(wv[4 * t], wv[4 * t + 1], wv[4 * t + 2], wv[4 * t + 3]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < KM; ++t)
+          if (t < k) orow[t] = (uint16_t)sel[t];
+      }
     }
   }
 }
