@@ -15,11 +15,12 @@
 // rational value: a cheap fp32 estimate is corrected with comparisons that
 // are exact in fp32 (products of short significands, fma remainders).
 //
-// Layout: 32 lanes per (token): lanes 0..15 take the K row, 16..31 the V row,
-// 8 dims per lane.  A block of 512 threads covers 16 tokens per step; V codes
-// are staged in LDS per tile of 32 tokens and stored transposed (for each
-// dim, the tile's 32 codes are one bit string) so decode can feed them to the
-// MFMA that contracts over tokens.
+// Layout: 16 lanes per (token, plane), 8 dims per lane; waves 0-3 of a
+// 512-thread block take the K rows and waves 4-7 the V rows of the same 16
+// tokens per step.  V codes are staged in LDS per tile of 32 tokens and
+// stored transposed (for each dim, the tile's 32 codes are one bit string) so
+// decode can feed them to the MFMA that contracts over tokens.  The
+// reconstruction kernel keeps 32 lanes per token (16 for K, 16 for V).
 #include <type_traits>
 
 #include "rkv_common.h"
