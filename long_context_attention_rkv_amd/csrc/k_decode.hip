@@ -52,7 +52,6 @@ __host__ __device__ constexpr int invperm_of(int o) {
 }
 
 __device__ inline f16x2 as_h2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
-__device__ inline uint32_t h2_bits(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
 // 8 two's-complement codes (BITS each) -> f16x8 exact integers, in
 // perm_of<BITS> order.  Offset-binary plus the f16 exponent of 1024 puts each

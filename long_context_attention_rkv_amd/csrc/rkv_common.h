@@ -106,10 +106,6 @@ __host__ __device__ inline int32_t sched_slot(int32_t i, const Sched& s) {
 
 // ---------------------------------------------------------------- numbers
 
-__device__ inline float bf16_bits_to_f32(uint32_t b16) {
-  return __uint_as_float(b16 << 16);
-}
-
 // The two bf16 halves of a 32-bit word as fp32 (exact).
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -148,16 +144,6 @@ __device__ inline bool is_pow2(int v) { return (v & (v - 1)) == 0; }
 // Lane exchanges inside a DPP row (16 lanes), no LDS traffic.
 #define RKV_DPP_F32(v, ctrl) \
   __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), (ctrl), 0xF, 0xF, true))
-
-// Maximum over aligned groups of `lanes` consecutive lanes (4, 8 or 16):
-// swaps within quads (xor 1, xor 2), then half-row and row mirrors.
-__device__ inline float group_max(float v, int lanes) {
-  v = fmaxf(v, RKV_DPP_F32(v, 0xB1));    // quad_perm [1,0,3,2]
-  v = fmaxf(v, RKV_DPP_F32(v, 0x4E));    // quad_perm [2,3,0,1]
-  if (lanes >= 8) v = fmaxf(v, RKV_DPP_F32(v, 0x141));   // row_half_mirror
-  if (lanes >= 16) v = fmaxf(v, RKV_DPP_F32(v, 0x140));  // row_mirror
-  return v;
-}
 
 // ------------------------------------------------------- latent transform
 // Latent variant of the residual (paper page, "DeltaKV Framework
