@@ -53,30 +53,45 @@ __host__ __device__ constexpr int invperm_of(int o) {
 
 __device__ inline f16x2 as_h2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
 
+// Offset of a code decoded without the final subtract: 1024 + 2^(BITS-1).
+template <int BITS>
+constexpr float code_bias() { return 1024.f + (float)(1 << (BITS - 1)); }
+
 // 8 two's-complement codes (BITS each) -> f16x8 exact integers, in
 // perm_of<BITS> order.  Offset-binary plus the f16 exponent of 1024 puts each
-// code in a mantissa; one packed subtract removes the offset.
-template <int BITS>
+// code in a mantissa; one packed subtract removes the offset.  RAW skips that
+// subtract: the values are then code + code_bias<BITS>() (still exact).
+template <int BITS, bool RAW = false>
 __device__ inline f16x8 decode_codes(uint32_t w0, uint32_t w1) {
   f16x2 p[4];
   if constexpr (BITS == 4) {
     const uint32_t t = w0 ^ 0x88888888u;
     const f16x2 off = {(_Float16)-1032.f, (_Float16)-1032.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = as_h2(((t >> (4 * j)) & 0x000F000Fu) | 0x64006400u) + off;
+    for (int j = 0; j < 4; ++j) {
+      p[j] = as_h2(((t >> (4 * j)) & 0x000F000Fu) | 0x64006400u);
+      if constexpr (!RAW) p[j] = p[j] + off;
+    }
   } else if constexpr (BITS == 8) {
     const uint32_t t0 = w0 ^ 0x80808080u, t1 = w1 ^ 0x80808080u;
     const f16x2 off = {(_Float16)-1152.f, (_Float16)-1152.f};
-    p[0] = as_h2((t0 & 0x00FF00FFu) | 0x64006400u) + off;
-    p[1] = as_h2(((t0 >> 8) & 0x00FF00FFu) | 0x64006400u) + off;
-    p[2] = as_h2((t1 & 0x00FF00FFu) | 0x64006400u) + off;
-    p[3] = as_h2(((t1 >> 8) & 0x00FF00FFu) | 0x64006400u) + off;
+    p[0] = as_h2((t0 & 0x00FF00FFu) | 0x64006400u);
+    p[1] = as_h2(((t0 >> 8) & 0x00FF00FFu) | 0x64006400u);
+    p[2] = as_h2((t1 & 0x00FF00FFu) | 0x64006400u);
+    p[3] = as_h2(((t1 >> 8) & 0x00FF00FFu) | 0x64006400u);
+    if constexpr (!RAW) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = p[j] + off;
+    }
   } else {
     const uint32_t t = (w0 ^ 0xAAAAu) & 0xFFFFu;
     const uint32_t u = (t & 0xFFu) | ((t & 0xFF00u) << 8);
     const f16x2 off = {(_Float16)-1026.f, (_Float16)-1026.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = as_h2(((u >> (2 * j)) & 0x00030003u) | 0x64006400u) + off;
+    for (int j = 0; j < 4; ++j) {
+      p[j] = as_h2(((u >> (2 * j)) & 0x00030003u) | 0x64006400u);
+      if constexpr (!RAW) p[j] = p[j] + off;
+    }
   }
   f16x8 r;
 #pragma unroll
@@ -114,20 +129,20 @@ __device__ inline void load_words(const void* p, uint32_t (&w)[NW]) {
   }
 }
 
-// Unsigned fixed point with 32 fractional bits, for 0 <= x < 2^31.
-__device__ inline unsigned long long to_fixed32(float x) {
-  const float y = x * 4294967296.0f;           // exact scaling
-  const float hi = floorf(y * 0x1p-32f);
-  const uint32_t h = (uint32_t)hi;
-  const uint32_t l = (uint32_t)(y - hi * 4294967296.0f);
-  return ((unsigned long long)h << 32) | l;
+// W of one softmax chunk is accumulated in LDS as unsigned fixed point with
+// 21 fractional bits, two query heads per 64-bit word (head 2m in the low
+// half, 2m+1 in the high half).  Every addend is p or p / k_eff with
+// p <= 1, and a chunk holds at most 1024 positions, so a half stays below
+// 2^31 and never carries into its neighbour.
+constexpr float kWFix = 0x1p21f;
+__device__ inline uint32_t to_fixed21(float x) {  // 0 <= x <= 1, rounded to nearest
+  return (uint32_t)__builtin_rintf(x * kWFix);
 }
-__device__ inline float from_fixed32(unsigned long long v) {
-  return (float)((double)v * 0x1p-32);
+__device__ inline unsigned long long pack_pair(uint32_t lo, uint32_t hi) {
+  return (unsigned long long)lo | ((unsigned long long)hi << 32);
 }
 
 constexpr int kDecTile = 32;
-constexpr float kLazyRescale = 8.0f;
 
 // Partial record per (instance, query head, split): m, l, 2 pad, O[128], W[nrp].
 __host__ __device__ inline int64_t part_rec_floats(int64_t n_refs) {
@@ -236,9 +251,19 @@ __device__ inline int32_t ref_slot_in_tile(int32_t tok, const TileRefs& tr, cons
   return slot;
 }
 
+// Blocks per CU the register allocation aims at.  The bf16 int4 forms with
+// 32-dim groups and exactly KM slots per row fit three (168 VGPRs; the few
+// values live across the whole position loop are spilled once before it and
+// reloaded once after); the other forms keep two so that nothing spills
+// inside the loop.
+template <typename T, int BITS, int NG, int KM, bool EX>
+constexpr int kDecodeBlocksPerCU() {
+  return (sizeof(T) == 2 && BITS == 4 && NG == 4 && KM <= 8 && EX) ? 3 : 2;
+}
+
 // EX: every row of ref_idx holds exactly KM slots (k == KM).
 template <typename T, int BITS, int NG, int KM, bool EX>
-__global__ __launch_bounds__(256, 2) void k_decode(
+__global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) void k_decode(
     const T* __restrict__ q, const T* __restrict__ ref_kv, const uint16_t* __restrict__ idx,
     const uint8_t* __restrict__ codes_k, const uint8_t* __restrict__ codes_v,
     const uint16_t* __restrict__ scales, const float* __restrict__ qk, float* __restrict__ part,
@@ -257,12 +282,13 @@ __global__ __launch_bounds__(256, 2) void k_decode(
   // Per-head LDS rows are nrp + 8 floats apart: the G heads of one token touch
   // the same slot, and this puts their words in different banks.
   const int64_t ls = nrp + 8;
+  const int GP = (G + 1) / 2;                                     // head pairs
   float* qk_s = lds;                                              // [G][ls]
-  unsigned long long* w_s =
-      reinterpret_cast<unsigned long long*>(qk_s + G * ls);       // [G][ls] fixed point
-  float* lg_s = reinterpret_cast<float*>(w_s + G * ls);           // [G][CT] logits of a chunk
-  float* o_s = lg_s + G * CTP;                                    // [G][128]
-  float* m_s = o_s + G * 128;                                     // [16] block max per head
+  unsigned long long* wc_s =
+      reinterpret_cast<unsigned long long*>(qk_s + G * ls);       // [GP][ls] chunk W, fixed point
+  float* wt_s = reinterpret_cast<float*>(wc_s + GP * ls);         // [G][ls] W of earlier chunks
+  float* lg_s = wt_s + G * ls;                                    // [G][CT] logits of a chunk
+  float* m_s = lg_s + G * CTP;                                    // [16] block max per head
   float* wm_s = m_s + 16;                                         // [4][16] wave maxima
   float* sc_s = wm_s + 64;                                        // [16] rescale factors
   _Float16* pst_all = reinterpret_cast<_Float16*>(sc_s + 16);     // [4][16][32]
@@ -300,12 +326,12 @@ __global__ __launch_bounds__(256, 2) void k_decode(
   // ---- prologue: QK table into LDS, clears
   {
     const float4* src = reinterpret_cast<const float4*>(qk + (inst * Hq + kvh * G) * nrp);
-    for (int64_t e = tid; e < G * nrp / 4; e += 256) {
-      const int64_t h = e / (nrp / 4), c = e - h * (nrp / 4);
-      *reinterpret_cast<float4*>(qk_s + h * ls + 4 * c) = src[e];
-    }
-    for (int64_t e = tid; e < G * ls; e += 256) w_s[e] = 0ull;
-    for (int e = tid; e < G * 128; e += 256) o_s[e] = 0.f;
+    const int nq = (int)(nrp / 4);
+    for (int h = 0; h < G; ++h)
+      for (int c = tid; c < nq; c += 256)
+        *reinterpret_cast<float4*>(qk_s + h * ls + 4 * c) = src[h * nq + c];
+    for (int64_t e = tid; e < GP * ls; e += 256) wc_s[e] = 0ull;
+    for (int64_t e = tid; e < G * ls; e += 256) wt_s[e] = 0.f;
     for (int e = tid; e < 4 * 16 * kDecTile; e += 256) pst_all[e] = (_Float16)0.f;
     if (tid < 16) m_s[tid] = -INFINITY;
   }
@@ -340,6 +366,21 @@ __global__ __launch_bounds__(256, 2) void k_decode(
         aq[s][e] = (_Float16)((live && dim / GS == g) ? qv[s][perm_of<BITS>(e)] : 0.f);
       }
     }
+  }
+  // The score MFMA takes codes without their offset (decode_codes RAW: code +
+  // code_bias), so each accumulator row starts at -code_bias * (sum of that
+  // A row).  Lane (n, quad) accumulates rows 4*quad + i of column n.
+  f32x4 qbias;
+  {
+    float rsum = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rsum += (float)aq[s][e];
+    rsum += __shfl_xor(rsum, 16);
+    rsum += __shfl_xor(rsum, 32);  // row n's sum over all 128 dims
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qbias[i] = -code_bias<BITS>() * __shfl(rsum, 4 * quad + i);
   }
   __syncthreads();
 
@@ -408,7 +449,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(
     for (int b = 0; b < 2; ++b) {
       const int32_t tok = tb + 16 * b + n;
       const bool valid = tok < N32;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc = qbias;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         uint32_t w0, w1;
@@ -419,7 +460,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(
         } else {
           w0 = (r.kw[b][s >> 1] >> (16 * (s & 1))) & 0xFFFFu; w1 = 0;
         }
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], decode_codes<BITS>(w0, w1), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], decode_codes<BITS, true>(w0, w1), acc, 0, 0, 0);
       }
       int32_t slot;
       int keff;
@@ -541,38 +582,78 @@ __global__ __launch_bounds__(256, 2) void k_decode(
       const int u = 16 * b + n;
       const int pos = 8 * (u >> 3) + invperm_of<BITS>(u & 7);
       const int uc = (t - c0) * kDecTile + u;
+      uint32_t fx[HPL];  // fast tiles: this position's W addend per head
 #pragma unroll
       for (int hh = 0; hh < HPL; ++hh) {
         const int h = h0 + hh;
-        if (FT && h < G) {
-          const float lg = lg_s[h * CTP + uc];
-          const float pv = valid ? __expf(lg - mh[hh]) : 0.f;
-          psum[hh] += pv;
-          unsigned long long* wrow = w_s + h * ls;
-          // a reference position adds p to its own slot and 0 to its row's
-          const bool isref = slot >= 0;
-          const unsigned long long pw = to_fixed32(isref ? 0.f : pv * (1.0f / KM));
-#pragma unroll
-          for (int j = 0; j < KM; ++j)
-            atomicAdd(wrow + ((r.iw[b][j >> 1] >> (16 * (j & 1))) & 0xFFFFu), pw);
-          if (isref) atomicAdd(wrow + slot, to_fixed32(pv));
-          pst[h * kDecTile + pos] = (_Float16)(isref ? 0.f : pv);
-        } else if (!FT && h < G) {
+        if (FT) {
+          float pv = 0.f;
+          if (h < G) {
+            const float lg = lg_s[h * CTP + uc];
+            pv = valid ? __expf(lg - mh[hh]) : 0.f;
+            psum[hh] += pv;
+            pst[h * kDecTile + pos] = (_Float16)(slot >= 0 ? 0.f : pv);
+          }
+          // a reference position adds p to its own slot; any other position
+          // adds p / KM to each of its KM slots
+          fx[hh] = to_fixed21(slot >= 0 ? pv : pv * (1.0f / KM));
+        } else if (h < G) {
           const float lg = lg_s[h * CTP + uc];
           const float pv = (valid && lg > -INFINITY) ? __expf(lg - mh[hh]) : 0.f;
           psum[hh] += pv;
-          unsigned long long* wrow = w_s + h * ls;
+          unsigned long long* wrow = wc_s + (h >> 1) * ls;
+          const int sh = 32 * (h & 1);  // this head's half of the pair word
           if (slot >= 0) {
-            if (pv > 0.f) atomicAdd(wrow + slot, to_fixed32(pv));
+            if (pv > 0.f) atomicAdd(wrow + slot, (unsigned long long)to_fixed21(pv) << sh);
             pst[h * kDecTile + pos] = (_Float16)0.f;
           } else {
             if (keff > 0 && pv > 0.f) {
-              const unsigned long long pw = to_fixed32(pv / (float)keff);
+              const unsigned long long pw = (unsigned long long)to_fixed21(pv / (float)keff) << sh;
 #pragma unroll
               for (int j = 0; j < KM; ++j)
                 if (j < keff) atomicAdd(wrow + ((r.iw[b][j >> 1] >> (16 * (j & 1))) & 0xFFFFu), pw);
             }
             pst[h * kDecTile + pos] = (_Float16)pv;
+          }
+        }
+      }
+      if constexpr (FT) {
+        const bool isref = slot >= 0;
+        if constexpr (HPL == 1) {
+          // lane quads 2m and 2m+1 hold heads 2m and 2m+1 of one position:
+          // after the swap both hold the pair word, and each adds it to half
+          // of the position's slots
+          const auto pr = __builtin_amdgcn_permlane16_swap(fx[0], fx[0], false, false);
+          const unsigned long long v = pack_pair(pr[0], pr[1]);
+          const int pp = quad >> 1;
+          const bool odd = (quad & 1) != 0;
+          if (2 * pp < G) {
+            unsigned long long* wrow = wc_s + pp * ls;
+            if (isref) {
+              if (!odd) atomicAdd(wrow + slot, v);
+            } else {
+#pragma unroll
+              for (int j = 0; j < KM / 2; ++j) {
+                const uint32_t wd = odd ? r.iw[b][KM / 4 + (j >> 1)] : r.iw[b][j >> 1];
+                atomicAdd(wrow + ((wd >> (16 * (j & 1))) & 0xFFFFu), v);
+              }
+            }
+          }
+        } else {
+          // the lane holds both heads of each of its pairs
+#pragma unroll
+          for (int pp = 0; pp < HPL / 2; ++pp) {
+            if (h0 + 2 * pp < G) {
+              const unsigned long long v = pack_pair(fx[2 * pp], fx[2 * pp + 1]);
+              unsigned long long* wrow = wc_s + ((h0 >> 1) + pp) * ls;
+              if (isref) {
+                atomicAdd(wrow + slot, v);
+              } else {
+#pragma unroll
+                for (int j = 0; j < KM; ++j)
+                  atomicAdd(wrow + ((r.iw[b][j >> 1] >> (16 * (j & 1))) & 0xFFFFu), v);
+              }
+            }
           }
         }
       }
@@ -668,10 +749,10 @@ __global__ __launch_bounds__(256, 2) void k_decode(
       bool any = false;
       for (int h = 0; h < G; ++h) any |= sc_s[h] != 1.f;
       if (any) {
-        for (int64_t e = tid; e < (int64_t)G * nrp; e += 256) {
-          const int64_t h = e / nrp, j = e - h * nrp;
+        for (int h = 0; h < G; ++h) {
           const float f = sc_s[h];
-          if (f != 1.f) w_s[h * ls + j] = (unsigned long long)((double)w_s[h * ls + j] * (double)f);
+          if (f != 1.f)
+            for (int j = tid; j < (int)nrp; j += 256) wt_s[h * ls + j] *= f;
         }
 #pragma unroll
         for (int hh = 0; hh < HPL; ++hh)
@@ -704,35 +785,49 @@ __global__ __launch_bounds__(256, 2) void k_decode(
       }
     }
     __syncthreads();
+    // add the chunk's fixed-point W to the fp32 totals and clear it (each
+    // thread owns whole pair words; the next use of either buffer is behind
+    // the next chunk's barriers)
+    for (int pp = 0; pp < GP; ++pp) {
+      for (int j = tid; j < (int)nrp; j += 256) {
+        const unsigned long long v = wc_s[pp * ls + j];
+        wt_s[2 * pp * ls + j] += (float)(uint32_t)v * (1.0f / kWFix);
+        if (2 * pp + 1 < G) wt_s[(2 * pp + 1) * ls + j] += (float)(uint32_t)(v >> 32) * (1.0f / kWFix);
+        wc_s[pp * ls + j] = 0ull;
+      }
+    }
   }
 
-  // ---- merge the four waves (same maximum), write the partial records
+  // ---- merge the four waves (same maximum), write the partial records.
+  // Each wave stores its P.V rows in the logit buffer (free after the last
+  // chunk's barrier); the four are then summed in a fixed order.
   float* lw = wm_s;  // reuse [4][16]
 #pragma unroll
   for (int hh = 0; hh < HPL; ++hh)
     if (h0 + hh < G && n == 0) lw[w * 16 + h0 + hh] = l_mine[hh];
+  float* ow = lg_s;  // [4][G][128]
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int h = 4 * quad + j;
     if (h < G) {
 #pragma unroll
-      for (int blk = 0; blk < 8; ++blk) atomicAdd(&o_s[h * 128 + 16 * blk + n], o[blk][j]);
+      for (int blk = 0; blk < 8; ++blk) ow[(w * G + h) * 128 + 16 * blk + n] = o[blk][j];
     }
   }
   __syncthreads();
   const int64_t rec = part_rec_floats(n_refs);
-  for (int64_t e = tid; e < (int64_t)G * nrp; e += 256) {
-    const int64_t h = e / nrp, j = e - h * nrp;
-    part[((inst * Hq + kvh * G + h) * n_split + split) * rec + 132 + j] = from_fixed32(w_s[h * ls + j]);
-  }
+  float* pr0 = part + ((inst * Hq + kvh * G) * n_split + split) * rec;  // head 0's record
+  const int64_t hstride = (int64_t)n_split * rec;                         // next head's
+  for (int h = 0; h < G; ++h)
+    for (int j = tid; j < (int)nrp; j += 256) pr0[h * hstride + 132 + j] = wt_s[h * ls + j];
   if (tid < G) {
-    float* r = part + ((inst * Hq + kvh * G + tid) * n_split + split) * rec;
-    r[0] = m_s[tid];
-    r[1] = lw[tid] + lw[16 + tid] + lw[32 + tid] + lw[48 + tid];
+    pr0[tid * hstride] = m_s[tid];
+    pr0[tid * hstride + 1] = lw[tid] + lw[16 + tid] + lw[32 + tid] + lw[48 + tid];
   }
   for (int e = tid; e < G * 128; e += 256) {
-    const int h = e / 128;
-    part[((inst * Hq + kvh * G + h) * n_split + split) * rec + 4 + (e % 128)] = o_s[e];
+    const int h = e >> 7, d = e & 127;
+    pr0[h * hstride + 4 + d] = ((ow[h * 128 + d] + ow[(G + h) * 128 + d]) + ow[(2 * G + h) * 128 + d]) +
+                               ow[(3 * G + h) * 128 + d];
   }
 }
 
@@ -1039,7 +1134,8 @@ size_t decode_ws_bytes(int64_t n_inst, int H, int n_q_heads, int n_split, int64_
 
 size_t decode_lds_bytes(int G, int NG, int64_t n_refs) {
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
-  return (size_t)(3 * G * (nrp + 8) + G * (kChunkTiles * kDecTile + kLgPad) + G * 128 + 96) * 4 +
+  return (size_t)((2 * G + 2 * ((G + 1) / 2)) * (nrp + 8) + G * (kChunkTiles * kDecTile + kLgPad) +
+                  96) * 4 +
          (size_t)(4 * 16 + 4 * NG) * kDecTile * 2;
 }
 
