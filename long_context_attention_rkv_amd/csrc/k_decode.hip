@@ -480,10 +480,14 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
           // every position of the tile has k = KM references: no predicates
           // (positions past N read slot 0 and are masked to -inf)
           const float* qrow = qk_s + h * ls;
-          // all KM lookups first, then a pairwise sum: one LDS wait per token
+          // all KM lookups (and the reference position's own entry) first,
+          // then a pairwise sum: one LDS wait per token.  The scheduling
+          // barrier keeps the reads together when registers are tight.
           float qv[KM];
 #pragma unroll
           for (int j = 0; j < KM; ++j) qv[j] = qrow[(r.iw[b][j >> 1] >> (16 * (j & 1))) & 0xFFFFu];
+          const float sref = qrow[slot >= 0 ? slot : 0];
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int w2 = 1; w2 < KM; w2 *= 2)
 #pragma unroll
@@ -495,7 +499,6 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
             const float sk = half_bits_to_f32((uint16_t)(r.sw[b][g >> 1] >> (16 * (g & 1))));
             res = __builtin_fmaf(sk, acc[hh * NG + g], res);
           }
-          const float sref = qrow[slot >= 0 ? slot : 0];
           const float sc_ = slot >= 0 ? sref : res + rs * (1.0f / KM);
           const float lg = valid ? alpha * sc_ : -INFINITY;
           lg_s[h * CTP + u] = lg;
