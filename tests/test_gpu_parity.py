@@ -204,6 +204,9 @@ DECODE = [
     ("gqa7_g64_int2", _cfg(4, n_kv_heads=2, n_q_heads=14, batch=1), 2, 2, 500),
     ("gqa7_g64_int4", _cfg(4, n_kv_heads=2, n_q_heads=14, batch=1), 4, 1, 500),
     ("g128_gqa4", _cfg(1, n_kv_heads=1, n_q_heads=4, group=128), 4, 1, 300),
+    # an odd number of query heads per KV head with 32-dim groups: the last
+    # head pair of the reference weights has no partner
+    ("gqa3_g32", _cfg(1, n_kv_heads=2, n_q_heads=6), 4, 1, 700),
     # more than 8 query heads per KV head
     ("g128_gqa16_bf16", _cfg(1, n_kv_heads=2, n_q_heads=32, group=128), 4, 1, 700),
     ("g128_gqa12_f32_int8", _cfg(0, n_kv_heads=1, n_q_heads=12, group=128), 8, 1, 500),
@@ -608,12 +611,15 @@ def test_full_size_decode_one_kv_head(index):
     q = make_q(cfg, 1)
     cache = encode(cfg, K, V, 4, 1, N)
     scale = 1.0 / math.sqrt(cfg.head_dim)
-    got = rkv.rkv_decode_attn(q, cfg.n_q_heads, cache, scale, n_split=16).cpu().numpy()
     G = cfg.n_q_heads // cfg.n_kv_heads
     Kn, Vn = to_np_f32(K[0, 0]), to_np_f32(V[0, 0])
     enc = oracle.encode(Kn, Vn, cfg.stride_base, cfg.double_after, cfg.k, 4, cfg.group)
     kv = oracle.reconstruct(enc, Kn, Vn, 4)
     want = oracle.decode_attn(to_np_f32(q[0, :G]), kv[None, :, 0], kv[None, :, 1], scale)
-    err = rel_l2(got[0, :G], want)
-    say(f"  rel L2 = {err:.2e}")
-    assert err <= 2e-3
+    # 16 splits, and one split that walks the whole context (N / 1024 softmax
+    # chunks, each folding its fixed-point reference weights into the totals)
+    for n_split in (16, 1):
+        got = rkv.rkv_decode_attn(q, cfg.n_q_heads, cache, scale, n_split=n_split).cpu().numpy()
+        err = rel_l2(got[0, :G], want)
+        say(f"  n_split={n_split} rel L2 = {err:.2e}")
+        assert err <= 2e-3
