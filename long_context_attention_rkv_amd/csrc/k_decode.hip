@@ -20,14 +20,16 @@
 //              sequence), which it walks in chunks of 1024 positions.
 //              Phase A: the waves stream the K codes of 32-token tiles,
 //              q.codes on 16x16x32 f16 MFMAs (codes are exact small
-//              integers in f16), scales in fp32, the reference term from the
-//              QK table in LDS; every logit goes to LDS.  The block takes the
-//              chunk maximum per query head (rescaling what it holds only if
-//              the maximum grew).  Phase B: the waves stream the V codes,
-//              p = exp(logit - max) <= 1, P.codes on the MFMA, and W in LDS
-//              as unsigned 64-bit fixed point (units of 2^-32: integer LDS
-//              atomics are far faster than float ones here).  The block
-//              writes (m, l, O, W) per query head.
+//              integers in f16, taken with a fixed offset that the
+//              accumulators start without), scales in fp32, the reference
+//              term from the QK table in LDS; every logit goes to LDS.  The
+//              block takes the chunk maximum per query head (rescaling what
+//              it holds only if the maximum grew).  Phase B: the waves stream
+//              the V codes, p = exp(logit - max) <= 1, P.codes on the MFMA,
+//              and the chunk's W in LDS as 21-bit fixed point, two query
+//              heads per 64-bit atomic (integer LDS atomics are far faster
+//              than float ones here), added to fp32 totals at the chunk end.
+//              The block writes (m, l, O, W) per query head.
 //   k_combine  one block per (instance, query head): merges the splits,
 //              adds W . Vref and normalises, with its loads requested up
 //              front.
