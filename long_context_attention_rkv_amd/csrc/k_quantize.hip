@@ -339,12 +339,24 @@ __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
   const int plane = __builtin_amdgcn_readfirstlane(tid >> 8);  // 0 = K, 1 = V
   const int tok_l = (tid >> 4) & 15;   // position within the step
   const int dl = tid & 15;             // dims [8*dl, 8*dl+8)
-  const int64_t ih = (int64_t)blockIdx.z * H + blockIdx.y;
+  // Workgroups are dealt to the 8 XCDs in turn.  When the heads split evenly
+  // over them, the i-th workgroup of XCD x takes chunk i % C of head
+  // 8 (i / C) + x, so the chunks of one head run together on one XCD and
+  // share its L2 copy of the head's reference rows.
+  int64_t ih = (int64_t)blockIdx.z * H + blockIdx.y;
+  int chunk_id = (int)blockIdx.x;
+  if (((gridDim.y * gridDim.z) & 7u) == 0) {
+    const int64_t nc = gridDim.x;
+    const int64_t L = blockIdx.x + nc * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+    const int64_t i = L >> 3;
+    ih = 8 * (i / nc) + (L & 7);
+    chunk_id = (int)(i % nc);
+  }
   // positions [p0, p1) from input rows [ih][n_in][128]; chunks start on
   // tile boundaries (no two blocks share a transposed V tile); positions of
   // a chunk outside [p0, p1) are skipped and keep their codes
   const int p1 = p0 + n_in;
-  const int c0 = (p0 & ~(kVTile - 1)) + (int)blockIdx.x * chunk;
+  const int c0 = (p0 & ~(kVTile - 1)) + chunk_id * chunk;
   const int c1 = c0 + chunk < p1 ? c0 + chunk : p1;
   const int v0 = c0 > p0 ? c0 : p0;
   const int n_groups = 128 / group;

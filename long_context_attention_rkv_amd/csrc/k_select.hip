@@ -300,8 +300,21 @@ __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int blk = n_blocks - 1 - (int)blockIdx.x;
-  const int64_t ih = (int64_t)blockIdx.z * H + blockIdx.y;
+  // Workgroups are dealt to the 8 XCDs in turn.  When the heads split evenly
+  // over them, the i-th workgroup of XCD x takes block i % n_blocks of head
+  // 8 (i / n_blocks) + x, so the blocks of one head run together on one XCD
+  // and share its L2 copy of the head's reference keys.  Within a head the
+  // blocks still start from the end of the sequence (the most candidates).
+  int64_t ih = (int64_t)blockIdx.z * H + blockIdx.y;
+  int bx = (int)blockIdx.x;
+  if (((gridDim.y * gridDim.z) & 7u) == 0) {
+    const int64_t nb = gridDim.x;
+    const int64_t L = blockIdx.x + nb * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+    const int64_t i = L >> 3;
+    ih = 8 * (i / nb) + (L & 7);
+    bx = (int)(i % nb);
+  }
+  const int blk = n_blocks - 1 - bx;
   const int64_t blk0 = p0 + (int64_t)blk * kBlockRows;
   const int64_t row0 = blk0 + w * 32 * kSets;
   const bool active = row0 < p1;
