@@ -146,6 +146,21 @@ __device__ inline unsigned long long pack_pair(uint32_t lo, uint32_t hi) {
 
 constexpr int kDecTile = 32;
 
+// Workgroups are dealt to the 8 XCDs in turn.  For a grid of nx x (heads)
+// workgroups with the heads (instance, KV head) a multiple of 8, the i-th
+// workgroup of XCD x takes item i % nx of head 8 (i / nx) + x: the table,
+// decode and combine workgroups of one head then all run on one XCD, and the
+// QK table and partial records they pass on stay in that XCD's L2.
+// `lin` is the workgroup's linear index, `nx` the items per head.
+struct XcdItem {
+  int64_t head;
+  int item;
+};
+__device__ inline XcdItem xcd_item(int64_t lin, int64_t nx) {
+  const int64_t i = lin >> 3;
+  return XcdItem{8 * (i / nx) + (lin & 7), (int)(i % nx)};
+}
+
 // Partial record per (instance, query head, split): m, l, 2 pad, O[128], W[nrp].
 __host__ __device__ inline int64_t part_rec_floats(int64_t n_refs) {
   return 132 + ((n_refs + 3) / 4) * 4;
@@ -166,8 +181,16 @@ __global__ __launch_bounds__(256) void k_qk_table(const T* __restrict__ q,
                                                   int64_t n_refs, int64_t n_valid) {
   // q rows as [head][part][33]: the four parts of a quad read different banks
   __shared__ float qs[16 * 4 * 33];
-  const int kvh = blockIdx.y;
-  const int64_t inst = blockIdx.z;
+  int kvh = blockIdx.y;
+  int64_t inst = blockIdx.z;
+  int bx = (int)blockIdx.x;
+  if ((((int64_t)gridDim.y * gridDim.z) & 7) == 0) {
+    const XcdItem it = xcd_item(blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z),
+                                gridDim.x);
+    kvh = (int)(it.head % H);
+    inst = it.head / H;
+    bx = it.item;
+  }
   const int Hq = H * G;
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
   const T* qh = q + (inst * Hq + kvh * G) * 128;
@@ -175,7 +198,7 @@ __global__ __launch_bounds__(256) void k_qk_table(const T* __restrict__ q,
     qs[(e >> 5) * 33 + (e & 31)] = (float)qh[e];
   __syncthreads();
   const int part = threadIdx.x & 3;  // dims 32*part .. +31
-  const int64_t j = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+  const int64_t j = (int64_t)bx * 64 + (threadIdx.x >> 2);
   if (j >= nrp) return;  // whole quads leave together
   float* out = qk + (inst * Hq + kvh * G) * nrp + j;
   const bool live = j < n_valid;
@@ -301,9 +324,16 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
   const int w = tid >> 6;
   const int n = lane & 15;
   const int quad = lane >> 4;
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int64_t inst = blockIdx.z;
+  int split = blockIdx.x;
+  int kvh = blockIdx.y;
+  int64_t inst = blockIdx.z;
+  if ((((int64_t)gridDim.y * gridDim.z) & 7) == 0) {
+    const XcdItem it = xcd_item(blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z),
+                                gridDim.x);
+    kvh = (int)(it.head % H);
+    inst = it.head / H;
+    split = it.item;
+  }
   const int64_t ih = inst * H + kvh;
   const int Hq = H * G;
   const int32_t tiles = (int32_t)((N + kDecTile - 1) / kDecTile);       // layout
@@ -910,9 +940,18 @@ __global__ __launch_bounds__(CT) void k_combine(const float* __restrict__ part,
   float* fs = wt + nrp;         // [n_split] split factors
   float* sm = fs + n_split;     // [2]: l, and [128] merged P.V at sm + 4
   float* red = sm + 132;        // [kCombRG][128] partial W . Vref
-  const int kvh = blockIdx.x;
-  const int64_t inst = blockIdx.y;
-  const int hq = kvh * G + (int)blockIdx.z;
+  // grid (H, n_inst, G): the G query heads of a KV head are its items
+  int kvh = blockIdx.x;
+  int64_t inst = blockIdx.y;
+  int g = blockIdx.z;
+  if ((((int64_t)gridDim.x * gridDim.y) & 7) == 0) {
+    const XcdItem it = xcd_item(blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z),
+                                gridDim.z);
+    kvh = (int)(it.head % H);
+    inst = it.head / H;
+    g = it.item;
+  }
+  const int hq = kvh * G + g;
   const int Hq = H * G;
   const int tid = threadIdx.x;
   const int64_t rec = part_rec_floats(n_refs);
