@@ -433,6 +433,11 @@ __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
     if constexpr (KM == 4) {
       const uint2 v = ld8(ib, r * 8u);
       p.sl[0] = u32x4{v.x, v.y, 0u, 0u};
+    } else if constexpr (KM == 8) {
+      // one word per lane (lanes 0-3 of the position's 16 hold words 0-3);
+      // the step spreads them over the 16 lanes before the gathers
+      p.sl[0].x = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(ib) + r * 16u +
+                                                     4u * (dl & 3));
     } else {
 #pragma unroll
       for (int c = 0; c < KM / 8; ++c) p.sl[c] = ld16(ib, r * (2u * KM) + 16u * c);
@@ -446,6 +451,14 @@ __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
     issue(clamp_pos(t + kQTokens), nxt);
     const bool mine = (uint32_t)(t - v0) < vspan;
     const uint32_t r = (uint32_t)(t - c0);
+    if constexpr (KM == 8) {
+      const uint32_t w0 = cur.sl[0].x;
+      // DPP row_newbcast:c gives every lane of a 16-lane row the word of lane c
+      cur.sl[0] = u32x4{(uint32_t)__builtin_amdgcn_mov_dpp((int)w0, 0x150, 0xF, 0xF, false),
+                        (uint32_t)__builtin_amdgcn_mov_dpp((int)w0, 0x151, 0xF, 0xF, false),
+                        (uint32_t)__builtin_amdgcn_mov_dpp((int)w0, 0x152, 0xF, 0xF, false),
+                        (uint32_t)__builtin_amdgcn_mov_dpp((int)w0, 0x153, 0xF, 0xF, false)};
+    }
     // fixed ascending-slot fp32 sum of the KM rows (all loads first)
     float acc[8];
     if constexpr (RQ) {
