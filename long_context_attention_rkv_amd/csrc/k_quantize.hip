@@ -23,6 +23,8 @@
 // reconstruction kernel keeps 32 lanes per token (16 for K, 16 for V).
 #include <type_traits>
 
+#include <utility>
+
 #include "rkv_common.h"
 #include "rkv_quant.h"
 
@@ -308,6 +310,23 @@ RKV_INLINE __device__ inline uint32_t slot_word(const PosLoads<T, KM>& p, int j)
   return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
 }
 
+// Slot words of a position: lane c (c < KM/2) of its 16 lanes loaded word c;
+// DPP row_newbcast:c gives every lane of the 16-lane row the word of lane c.
+template <int... C>
+RKV_INLINE __device__ inline void row_bcast_words(int w0, uint32_t* wd,
+                                                  std::integer_sequence<int, C...>) {
+  ((wd[C] = (uint32_t)__builtin_amdgcn_mov_dpp(w0, 0x150 + C, 0xF, 0xF, false)), ...);
+}
+template <typename T, int KM>
+RKV_INLINE __device__ inline void spread_slot_words(PosLoads<T, KM>& p) {
+  uint32_t wd[KM / 2];
+  row_bcast_words((int)p.sl[0].x, wd, std::make_integer_sequence<int, KM / 2>{});
+#pragma unroll
+  for (int c = 0; c < (KM + 7) / 8; ++c)
+    p.sl[c] = u32x4{wd[4 * c], wd[4 * c + 1], 4 * c + 2 < KM / 2 ? wd[4 * c + 2] : 0u,
+                    4 * c + 3 < KM / 2 ? wd[4 * c + 3] : 0u};
+}
+
 // Byte offset of this lane's piece of the raw reference row whose slot is
 // the low (half = 0) or high half of w: slot * 128 * sizeof(T) + 8 * dl *
 // sizeof(T), from lane16 = 16 * dl < 256.  The bf16 offset is one byte
@@ -430,18 +449,11 @@ __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
 #pragma unroll
     for (int c = 0; c < (int)(sizeof(T) / 2); ++c)
       p.x[c] = ld16(xb, r * kRowBytes + lane_off + 16u * c);
-    if constexpr (KM == 4) {
-      const uint2 v = ld8(ib, r * 8u);
-      p.sl[0] = u32x4{v.x, v.y, 0u, 0u};
-    } else if constexpr (KM == 8) {
-      // one word per lane (lanes 0-3 of the position's 16 hold words 0-3);
-      // the step spreads them over the 16 lanes before the gathers
-      p.sl[0].x = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(ib) + r * 16u +
-                                                     4u * (dl & 3));
-    } else {
-#pragma unroll
-      for (int c = 0; c < KM / 8; ++c) p.sl[c] = ld16(ib, r * (2u * KM) + 16u * c);
-    }
+    // one slot word per lane (lanes 0 .. KM/2-1 of the position's 16 hold
+    // words 0 .. KM/2-1); the step spreads them over the 16 lanes before the
+    // gathers
+    p.sl[0].x = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(ib) +
+                                                   r * (2u * KM) + 4u * (dl & (KM / 2 - 1)));
   };
   auto clamp_pos = [&](int t) RKV_INLINE { return min(max(t, v0), c1 - 1); };
   // One step of the fast path: request the loads of position t + 16 into
@@ -451,14 +463,7 @@ __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
     issue(clamp_pos(t + kQTokens), nxt);
     const bool mine = (uint32_t)(t - v0) < vspan;
     const uint32_t r = (uint32_t)(t - c0);
-    if constexpr (KM == 8) {
-      const uint32_t w0 = cur.sl[0].x;
-      // DPP row_newbcast:c gives every lane of a 16-lane row the word of lane c
-      cur.sl[0] = u32x4{(uint32_t)__builtin_amdgcn_mov_dpp((int)w0, 0x150, 0xF, 0xF, false),
-                        (uint32_t)__builtin_amdgcn_mov_dpp((int)w0, 0x151, 0xF, 0xF, false),
-                        (uint32_t)__builtin_amdgcn_mov_dpp((int)w0, 0x152, 0xF, 0xF, false),
-                        (uint32_t)__builtin_amdgcn_mov_dpp((int)w0, 0x153, 0xF, 0xF, false)};
-    }
+    spread_slot_words<T, KM>(cur);
     // fixed ascending-slot fp32 sum of the KM rows (all loads first)
     float acc[8];
     if constexpr (RQ) {
