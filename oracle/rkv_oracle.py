@@ -6,12 +6,11 @@ CPU-baseline leg use it.  It shares no code with the HIP library and does
 not import it.
 
 It is a plain, slow, step-by-step statement of what the path computes, for
-one (instance, KV head) at a time, on NumPy arrays.  Floating point is fp64
-except where a quantised code or scale is decided: there both this oracle and
-the kernels take the decision from the same fp32 residual (see
-``ref_mean_f32`` and ``residual_f32``), and the decision itself is the exact
-round-to-nearest-even of that fp32 value (fp64 here is provably enough to get
-the exact answer).
+one (instance, KV head) at a time, on NumPy arrays, in fp64 throughout:
+the reference mean KV_R and the residual KV - KV_R are formed in fp64 from
+the original-precision rows, and every quantised scale and code is the
+round-to-nearest-even of that fp64 value.  Distances are taken on keys
+rounded to bf16 (the one place the method's own precision enters), exactly.
 
 Sources (the method's pages):
   [P1] "ResidualKV: Residual-Based KV Cache Compression for Efficient
@@ -38,7 +37,7 @@ supports):
   * ties in distance go to the lower position;
   * the compressor/decompressor pair is the identity; the residual is stored
     as symmetric absmax group-quantised codes with an fp16 scale;
-  * bits == 0 means no quantisation: the residual is kept exactly (fp64).
+  * bits == 0 means no quantisation: the residual is kept as is.
 """
 
 import numpy as np
@@ -122,27 +121,23 @@ def select_topk(dist: np.ndarray, k: int) -> np.ndarray:
     return np.sort(order)
 
 
-def ref_mean_f32(ref_rows: np.ndarray) -> np.ndarray:
-    """KV_R: mean of the selected reference rows, in fp32.
-
-    The rows (ascending slot order) are added one after another in fp32
-    arithmetic, then the sum is divided by k_eff in fp32 -- the precision in
-    which the residual, and so every code, is decided.
-    """
-    rows = np.asarray(ref_rows, dtype=np.float32)
+def ref_mean(ref_rows: np.ndarray) -> np.ndarray:
+    """KV_R: the mean of the selected reference rows (the rows in ascending
+    slot order), in fp64 on the rows' original values."""
+    rows = np.asarray(ref_rows, dtype=np.float64)
     s = rows[0].copy()
     for m in range(1, rows.shape[0]):
-        s = (s + rows[m]).astype(np.float32)
-    return (s / np.float32(rows.shape[0])).astype(np.float32)
+        s = s + rows[m]
+    return s / rows.shape[0]
 
 
-def residual_f32(x: np.ndarray, mean32: np.ndarray) -> np.ndarray:
-    """z = KV_i - KV_R in fp32 (compressor = identity)."""
-    return (np.asarray(x, dtype=np.float32) - mean32).astype(np.float32)
+def residual(x: np.ndarray, mean64: np.ndarray) -> np.ndarray:
+    """z = KV_i - KV_R in fp64 (compressor = identity)."""
+    return np.asarray(x, dtype=np.float64) - np.asarray(mean64, dtype=np.float64)
 
 
-def quantize_residual(delta32: np.ndarray, bits: int, group: int):
-    """Symmetric absmax group quantisation of one fp32 residual row.
+def quantize_residual(z: np.ndarray, bits: int, group: int):
+    """Symmetric absmax group quantisation of one residual row (fp64).
 
     For each run of ``group`` contiguous elements: a = max |z|, the scale is
     the fp16 nearest to a / qmax (qmax = 2^(bits-1) - 1), and each code is
@@ -151,8 +146,7 @@ def quantize_residual(delta32: np.ndarray, bits: int, group: int):
     codes int64 [d]).
     """
     qmax = (1 << (bits - 1)) - 1
-    z = np.asarray(delta32, dtype=np.float32).astype(np.float64)
-    zg = z.reshape(-1, group)
+    zg = np.asarray(z, dtype=np.float64).reshape(-1, group)
     a = np.abs(zg).max(axis=1)
     scale = fp16_scale(a / qmax)
     s64 = scale.astype(np.float64)
@@ -177,7 +171,7 @@ def quantize_refs(K, V, T, group, bits=4):
     for X in (K, V):
         sc_p, c_p, d_p = [], [], []
         for pos in T:
-            sc, c = quantize_residual(np.asarray(X[pos], dtype=np.float32), bits, group)
+            sc, c = quantize_residual(np.asarray(X[pos], dtype=np.float64), bits, group)
             deq = c.astype(np.float64) * np.repeat(sc.astype(np.float64), group)
             sc_p.append(sc)
             c_p.append(c)
@@ -196,7 +190,8 @@ def quantize_refs(K, V, T, group, bits=4):
 # followed by the Walsh-Hadamard transform H (H[i][t] = (-1)^popcount(i&t)):
 #     f_c(x) = H D x / 16,     f_d(y) = D H y / 8,     f_d(f_c(x)) = x
 # (H H = 128 I, D D = I; both scalings are powers of two).  f_c is linear, so
-# z = f_c(KV - KV_R) is the rotated residual; it is quantised as usual.
+# z = f_c(KV - KV_R) is the rotated residual; it is quantised as usual.  Both
+# maps are taken here as fp64 matrix products.
 # ---------------------------------------------------------------------------
 
 _M64 = (1 << 64) - 1
@@ -222,26 +217,10 @@ def latent_signs(seed: int, d: int = 128) -> np.ndarray:
     return np.array([-1.0 if (x >> 63) else 1.0 for x in splitmix64(seed, d)], dtype=np.float32)
 
 
-def fwht_f32(x) -> np.ndarray:
-    """Unnormalised Walsh-Hadamard transform of a length-2^m vector in fp32:
-    butterflies (a, b) -> (a + b, a - b) on index bit 0, then bit 1, ..., each
-    result rounded to fp32."""
-    y = np.asarray(x, dtype=np.float32).copy()
-    n = y.shape[0]
-    h = 1
-    while h < n:
-        y = y.reshape(-1, 2, h)
-        a, b = y[:, 0, :].copy(), y[:, 1, :].copy()
-        y[:, 0, :] = (a + b).astype(np.float32)
-        y[:, 1, :] = (a - b).astype(np.float32)
-        y = y.reshape(n)
-        h *= 2
-    return y
-
-
-def latent_fc(z32, signs) -> np.ndarray:
-    """f_c of an fp32 row: sign flips (exact), the fp32 transform, / 16 (exact)."""
-    return (fwht_f32(np.asarray(z32, np.float32) * signs) * np.float32(1.0 / 16)).astype(np.float32)
+def latent_fc64(z, signs) -> np.ndarray:
+    """f_c in fp64: H D z / 16 (a matrix product with the Hadamard matrix)."""
+    z = np.asarray(z, dtype=np.float64)
+    return (hadamard(z.shape[-1]) @ (z * signs.astype(np.float64))) / 16.0
 
 
 def latent_fd64(y, signs) -> np.ndarray:
@@ -268,16 +247,17 @@ def encode(K, V, base, double_after, k, bits, group, rows=None, ref_bits=0, late
       rows      int64 [R]
       idx       uint16 [R, k]   ascending reference slots, 0xFFFF padding
       k_eff     int64 [R]
-      mean      fp32 [R, 2, d]  KV_R for K and V
-      delta     fp32 [R, 2, d]  residual (fp32)
-      scales    fp16 [R, 2, d/group]        (bits > 0)
-      codes     int64 [R, 2, d]             (bits > 0)
-      resid64   fp64 [R, 2, d]  exact residual (bits == 0)
+      mean      fp64 [R, 2, d]  KV_R for K and V
+      delta     fp64 [R, 2, d]  residual KV_i - KV_R
+      z         fp64 [R, 2, d]  the quantised quantity: delta, or
+                                f_c(delta) in latent mode     (bits > 0)
+      scales    fp16 [R, 2, d/group]                          (bits > 0)
+      codes     int64 [R, 2, d]                               (bits > 0)
     plus ``T`` (reference positions), and with ref_bits = 4 ``ref_q`` (the
     quantised reference store of quantize_refs), whose dequantised rows
     then stand in for the references in the means.  With latent_seed set
-    (bits > 0) the stored codes are those of f_c(residual), and ``signs``
-    holds D.
+    (bits > 0) ``signs`` holds D.  With bits == 0 the residual itself is
+    the stored record.
     """
     K = np.asarray(K, dtype=np.float32)
     V = np.asarray(V, dtype=np.float32)
@@ -291,8 +271,8 @@ def encode(K, V, base, double_after, k, bits, group, rows=None, ref_bits=0, late
         "T": T, "rows": rows,
         "idx": np.full((R, k), IDX_PAD, dtype=np.uint16),
         "k_eff": np.zeros(R, dtype=np.int64),
-        "mean": np.zeros((R, 2, d), dtype=np.float32),
-        "delta": np.zeros((R, 2, d), dtype=np.float32),
+        "mean": np.zeros((R, 2, d), dtype=np.float64),
+        "delta": np.zeros((R, 2, d), dtype=np.float64),
     }
     if ref_q is not None:
         out["ref_q"] = ref_q
@@ -302,10 +282,9 @@ def encode(K, V, base, double_after, k, bits, group, rows=None, ref_bits=0, late
         signs = latent_signs(latent_seed, d)
         out["signs"] = signs
     if bits > 0:
+        out["z"] = np.zeros((R, 2, d), dtype=np.float64)
         out["scales"] = np.zeros((R, 2, d // group), dtype=np.float16)
         out["codes"] = np.zeros((R, 2, d), dtype=np.int64)
-    else:
-        out["resid64"] = np.zeros((R, 2, d), dtype=np.float64)
     for r, i in enumerate(rows):
         c = candidate_count(int(i), T)
         dist = distances(keys[i], keys[T[:c]])
@@ -314,17 +293,16 @@ def encode(K, V, base, double_after, k, bits, group, rows=None, ref_bits=0, late
         out["k_eff"][r] = sel.shape[0]
         pos = T[sel]
         for p, X in enumerate((K, V)):
-            m32 = ref_mean_f32(ref_q["deq"][p][sel] if ref_q is not None else X[pos])
-            z32 = residual_f32(X[i], m32)
-            out["mean"][r, p] = m32
-            out["delta"][r, p] = z32
+            m = ref_mean(ref_q["deq"][p][sel] if ref_q is not None else X[pos])
+            z = residual(X[i], m)
+            out["mean"][r, p] = m
+            out["delta"][r, p] = z
             if bits > 0:
-                zq = latent_fc(z32, signs) if signs is not None else z32
+                zq = latent_fc64(z, signs) if signs is not None else z
                 s, q = quantize_residual(zq, bits, group)
+                out["z"][r, p] = zq
                 out["scales"][r, p] = s
                 out["codes"][r, p] = q
-            else:
-                out["resid64"][r, p] = X[i].astype(np.float64) - m32.astype(np.float64)
     return out
 
 
@@ -369,20 +347,20 @@ def reconstruct(enc, K, V, bits):
     """KV^_i for the encoded rows, fp64 [R, 2, d].
 
     Reference positions come back as stored: raw, or dequantised when the
-    reference store is quantised (enc has ``ref_q``).  Every other position is KV_R (the fp32 mean the residual was taken
-    against) plus the dequantised residual scale * code (bits > 0) or the
-    exact residual (bits == 0).
+    reference store is quantised (enc has ``ref_q``).  Every other position
+    is KV_R plus the dequantised residual: scale * code (through f_d in
+    latent mode) for bits > 0, the residual itself for bits == 0.
     """
     T = enc["T"]
     is_ref = np.isin(enc["rows"], T)
-    out = enc["mean"].astype(np.float64).copy()
+    out = enc["mean"].copy()
     if bits > 0:
         g = enc["codes"].shape[-1] // enc["scales"].shape[-1]
         sc = np.repeat(enc["scales"].astype(np.float64), g, axis=-1)
         y = sc * enc["codes"].astype(np.float64)
         out += latent_fd64(y, enc["signs"]) if "signs" in enc else y
     else:
-        out += enc["resid64"]
+        out += enc["delta"]
     if "ref_q" in enc:
         slot = np.searchsorted(T, enc["rows"])
         deq = enc["ref_q"]["deq"].astype(np.float64)

@@ -72,9 +72,10 @@ def _drifted(cfg: Config, base: torch.Tensor, layer: int, head: int,
 
 
 def gen_head_kv(cfg: Config, layer: int, seq: int, head: int, device="cpu",
-                seq_len: int = None):
+                seq_len: int = None, return_ids: bool = False):
     """K, V of one (layer, sequence, KV head): two [seq_len, head_dim] tensors
-    in the workload dtype."""
+    in the workload dtype (and the positions' prototype ids when
+    ``return_ids``)."""
     n = cfg.seq_len if seq_len is None else seq_len
     d = cfg.head_dim
     pk, pv = _prototypes(cfg, layer, head, device)
@@ -103,6 +104,8 @@ def gen_head_kv(cfg: Config, layer: int, seq: int, head: int, device="cpu",
     k = base_k + cfg.sigma * nk
     v = base_v + cfg.sigma * nv
     dt = torch_dtype(cfg)
+    if return_ids:
+        return k.to(dt), v.to(dt), ids
     return k.to(dt), v.to(dt)
 
 

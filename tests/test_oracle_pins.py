@@ -172,11 +172,30 @@ def test_topk_uses_bf16_rounded_keys():
 
 # ---------------------------------------------------------------- mean
 
-def test_mean_fp32_golden():
-    for c in _golden("mean_f32.json")["cases"]:
+def test_mean_fp64_golden():
+    for c in _golden("mean_f64.json")["cases"]:
         rows = np.array(c["rows"], dtype=np.float32).reshape(-1, 1)
-        m = oracle.ref_mean_f32(rows)
-        assert hex(int(m.view(np.uint32)[0])) == c["mean_hex"], c
+        m = oracle.ref_mean(rows)
+        assert m.dtype == np.float64
+        assert hex(int(m.view(np.uint64)[0])) == c["mean_hex"], c
+
+
+def test_mean_and_residual_are_exact_rationals_on_short_inputs():
+    # fp64 holds the sum of a few fp32 values exactly when their exponents
+    # are close; then the mean is the correctly rounded rational and the
+    # residual's error is below 2^-52 relative (checked with Fractions).
+    rng = np.random.default_rng(21)
+    for k in (1, 2, 3, 5, 7, 8):
+        rows = rng.standard_normal((k, 64)).astype(np.float32)
+        x = rng.standard_normal(64).astype(np.float32)
+        m = oracle.ref_mean(rows)
+        z = oracle.residual(x, m)
+        for t in (0, 17, 63):
+            want_m = sum(Fraction(float(r)) for r in rows[:, t]) / k
+            assert m[t] == float(want_m)
+            want_z = Fraction(float(x[t])) - want_m
+            assert abs(Fraction(float(z[t])) - want_z) <= \
+                (abs(want_z) + abs(want_m)) * Fraction(1, 2 ** 52)
 
 
 # ---------------------------------------------------------------- quantiser
@@ -287,9 +306,11 @@ def test_invariant_no_quantisation_reconstructs_exactly(dtype, s, k):
     K, V = _mixture(300, 64, 16, 0.2, 11, dtype)
     enc = oracle.encode(K, V, s, 0, k, 0, 32)
     kv = oracle.reconstruct(enc, K, V, 0)
+    # KV_R + (KV - KV_R) = KV: exact after rounding to the input precision,
+    # and within fp64 round-off before it
     assert np.array_equal(kv[:, 0].astype(np.float32), K)
     assert np.array_equal(kv[:, 1].astype(np.float32), V)
-    assert np.array_equal(kv[:, 0], K.astype(np.float64))
+    assert np.all(np.abs(kv[:, 0] - K) <= 2.0 ** -52 * (np.abs(K) + np.abs(enc["mean"][:, 0])))
 
 
 def test_invariant_no_quantisation_decode_is_full_attention():
@@ -319,8 +340,8 @@ def test_reconstruction_error_within_half_scale():
         for p, X in enumerate((K, V)):
             sc = np.repeat(enc["scales"][r, p].astype(np.float64), 32)
             err = np.abs(kv[r, p] - X[i].astype(np.float64))
-            # |z - s c| <= s/2 plus the fp32 rounding of the residual itself
-            assert np.all(err <= sc / 2 + 4e-7 * (np.abs(X[i]) + 1))
+            # |z - s c| <= s/2, up to fp64 round-off
+            assert np.all(err <= sc / 2 * (1 + 1e-12) + 1e-15 * (np.abs(X[i]) + 1))
 
 
 def test_reconstruction_mean_is_reference_average():
@@ -334,7 +355,7 @@ def test_reconstruction_mean_is_reference_average():
     # row 3: candidates slots 0 (pos 0, dist 1), 1 (pos 2, dist 1) -> both
     assert list(enc["idx"][3]) == [0, 1]
     np.testing.assert_array_equal(enc["mean"][3, 0], [1, 0, 0, 0])
-    np.testing.assert_array_equal(enc["mean"][3, 1], (V[0] + V[2]) / 2)
+    np.testing.assert_array_equal(enc["mean"][3, 1], (V[0].astype(np.float64) + V[2]) / 2)
     np.testing.assert_array_equal(enc["delta"][3, 0], K[3] - [1, 0, 0, 0])
     # row 1: candidates slot 0 only -> k_eff = 1, KV_R is that reference
     assert list(enc["idx"][1]) == [0, oracle.IDX_PAD]
@@ -398,7 +419,11 @@ def test_encode_with_quantized_refs_uses_the_dequantised_rows():
     deq = enc["ref_q"]["deq"]
     for r in (5, 40, 95):
         sel = enc["idx"][r][enc["idx"][r] != oracle.IDX_PAD].astype(np.int64)
-        np.testing.assert_array_equal(enc["mean"][r, 0], oracle.ref_mean_f32(deq[0][sel]))
+        # the library mean of the dequantised (not the raw) rows
+        np.testing.assert_allclose(enc["mean"][r, 0], deq[0][sel].astype(np.float64).mean(0),
+                                   rtol=0, atol=1e-15)
+        assert not np.allclose(enc["mean"][r, 0], K[enc["T"][sel]].astype(np.float64).mean(0),
+                               rtol=0, atol=1e-6)
     kv = oracle.reconstruct(enc, K, V, 4)
     T = enc["T"]
     np.testing.assert_array_equal(kv[T, 0], deq[0].astype(np.float64))
@@ -412,29 +437,39 @@ def test_splitmix64_published_vectors():
     assert sg[0] == -1.0 and sg[1] == 1.0 and sg[2] == 1.0   # top bits of the vector above
 
 
-def test_hadamard_and_fwht():
+def test_hadamard_and_latent_fc():
+    import scipy.linalg
     Hm = oracle.hadamard(128)
+    # the Sylvester construction of the library routine
+    np.testing.assert_array_equal(Hm, scipy.linalg.hadamard(128).astype(np.float64))
     np.testing.assert_array_equal(Hm @ Hm, 128 * np.eye(128))
-    e0 = np.zeros(128, np.float32)
-    e0[0] = 1
-    np.testing.assert_array_equal(oracle.fwht_f32(e0), np.ones(128))
+    sg = oracle.latent_signs(5)
+    # f_c of a unit vector e_t is column t of H times the sign of dim t, / 16
+    for t in (0, 1, 77, 127):
+        e = np.zeros(128)
+        e[t] = 1.0
+        np.testing.assert_array_equal(oracle.latent_fc64(e, sg),
+                                      sg[t] * scipy.linalg.hadamard(128)[:, t] / 16.0)
+    # linear: f_c(a x + y) = a f_c(x) + f_c(y) (non-integer data)
     rng = np.random.default_rng(3)
-    # small integers: every butterfly is exact, so the fast transform equals
-    # the matrix product exactly
-    x = rng.integers(-50, 50, 128).astype(np.float32)
-    np.testing.assert_array_equal(oracle.fwht_f32(x), (Hm @ x.astype(np.float64)).astype(np.float32))
+    x, y = rng.standard_normal((2, 128))
+    np.testing.assert_allclose(oracle.latent_fc64(2.5 * x + y, sg),
+                               2.5 * oracle.latent_fc64(x, sg) + oracle.latent_fc64(y, sg),
+                               rtol=0, atol=1e-13)
+    # the norm shrinks by sqrt(128) / 16 = 1/sqrt(2)
+    assert abs(np.linalg.norm(oracle.latent_fc64(x, sg)) - np.linalg.norm(x) / np.sqrt(2)) <= \
+        1e-13 * np.linalg.norm(x)
 
 
 def test_latent_pair_inverts():
     rng = np.random.default_rng(4)
     sg = oracle.latent_signs(99)
-    x = rng.standard_normal(128).astype(np.float32)
-    y = oracle.latent_fc(x, sg)
-    back = oracle.latent_fd64(y.astype(np.float64), sg)
-    assert np.max(np.abs(back - x)) <= 1e-5 * np.max(np.abs(x))
+    x = rng.standard_normal(128)
+    back = oracle.latent_fd64(oracle.latent_fc64(x, sg), sg)
+    assert np.max(np.abs(back - x)) <= 1e-13 * np.max(np.abs(x))
     # exact on integer data (no rounding anywhere)
-    xi = rng.integers(-8, 8, 128).astype(np.float32)
-    np.testing.assert_array_equal(oracle.latent_fd64(oracle.latent_fc(xi, sg).astype(np.float64), sg), xi)
+    xi = rng.integers(-8, 8, 128).astype(np.float64)
+    np.testing.assert_array_equal(oracle.latent_fd64(oracle.latent_fc64(xi, sg), sg), xi)
 
 
 def test_latent_encode_reconstruct_within_bound():
