@@ -259,6 +259,24 @@ rkv_status rkv_decode_attn_tiles(const void *q, int32_t n_q_heads, const rkv_cac
                                  float *out, int32_t n_split, void *ws, size_t ws_bytes,
                                  void *stream);
 
+/* Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): rkv_decode_attn with its workspace taken from a fixed device
+ * array of RKV_SCRATCH_BYTES inside the library instead of a caller buffer.
+ * Each GPU the library runs on holds its own copy of that array until the
+ * process ends; the first call on a device looks up its address there (a
+ * host-side query).  The call allocates nothing and launches the same
+ * kernels as rkv_decode_attn, so the results are the same bits.
+ * RKV_ERR_WORKSPACE when rkv_decode_workspace(c, n_q_heads, n_split) exceeds
+ * RKV_SCRATCH_BYTES (checked before any device work); other errors as for
+ * rkv_decode_attn.  All calls on one GPU share the array and nothing in it
+ * is kept between calls: calls that overlap on one GPU (other streams, other
+ * host threads) race and must be serialised by the caller. */
+#define RKV_SCRATCH_BYTES (32u << 20)
+rkv_status rkv_decode_attn_noalloc(const void *q, int32_t n_q_heads, const rkv_cache *c,
+                                   float softmax_scale, float *out, int32_t n_split,
+                                   void *stream);
+
 const char *rkv_status_string(rkv_status s);
 int32_t rkv_last_hip_error(void);
 int32_t rkv_version(void);

@@ -292,3 +292,22 @@ def rkv_decode_attn_tiles(q, n_q_heads: int, cache: Cache, softmax_scale: float,
                                         _ptr(out), int(n_split), _ptr(ws), ws.numel(),
                                         _stream(stream)), "rkv_decode_attn_tiles")
     return out
+
+
+def rkv_decode_attn_noalloc(q, n_q_heads: int, cache: Cache, softmax_scale: float, out,
+                            n_split: int = 1, stream=None):
+    """rkv_decode_attn with the library's fixed device scratch as workspace
+    (no workspace argument; `out` is the caller's [n_inst, n_q_heads,
+    head_dim] float32 tensor)."""
+    c = cache.c
+    if q.dtype != cache.torch_dtype or not q.is_cuda or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous {cache.torch_dtype} device tensor")
+    if q.numel() != c.n_inst * n_q_heads * c.head_dim:
+        raise ValueError("q must hold n_inst * n_q_heads * head_dim elements")
+    if (out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous()
+            or out.numel() != c.n_inst * n_q_heads * c.head_dim):
+        raise ValueError("out must be a contiguous float32 device tensor of the output shape")
+    _check(_load().rkv_decode_attn_noalloc(_ptr(q), int(n_q_heads), C.byref(c),
+                                          float(softmax_scale), _ptr(out), int(n_split),
+                                          _stream(stream)), "rkv_decode_attn_noalloc")
+    return out

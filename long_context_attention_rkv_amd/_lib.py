@@ -13,6 +13,8 @@ RKV_ERR_WORKSPACE = 3
 RKV_ERR_HIP = 4
 RKV_ERR_RANGE = 5
 
+RKV_SCRATCH_BYTES = 32 << 20   # the fixed scratch of rkv_decode_attn_noalloc
+
 RKV_F32 = 0
 RKV_BF16 = 1
 
@@ -72,6 +74,8 @@ SIGNATURES = {
     "rkv_decode_attn_len": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(RkvCache), C.c_int64,
                                       C.c_float, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
                                       C.c_void_p]),
+    "rkv_decode_attn_noalloc": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(RkvCache), C.c_float,
+                                          C.c_void_p, C.c_int32, C.c_void_p]),
     "rkv_status_string": (C.c_char_p, [C.c_int]),
     "rkv_last_hip_error": (C.c_int32, []),
     "rkv_version": (C.c_int32, []),

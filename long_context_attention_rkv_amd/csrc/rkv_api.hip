@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/rkv.h"
 #include "rkv_common.h"
 
@@ -360,6 +362,60 @@ rkv_status rkv_decode_attn_tiles(const void* q, int32_t n_q_heads, const rkv_cac
   if (!c) return RKV_ERR_INVALID_ARG;
   return decode_common(q, n_q_heads, c, c->seq_len, softmax_scale, out, tiles, n_tiles, n_split,
                        ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// Fixed device scratch of rkv_decode_attn_noalloc (each GPU the library runs
+// on holds its own copy until the process ends).  In host code this name is
+// only a stand-in: the kernels get the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[RKV_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, resolved once per device.
+rkv_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return RKV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return RKV_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rkv_status rkv_decode_attn_noalloc(const void* q, int32_t n_q_heads, const rkv_cache* c,
+                                   float softmax_scale, float* out, int32_t n_split,
+                                   void* stream) {
+  size_t need = 0;
+  rkv_status s = rkv_decode_workspace(c, n_q_heads, n_split, &need);
+  if (s != RKV_OK) return s;
+  if (need > (size_t)RKV_SCRATCH_BYTES) return RKV_ERR_WORKSPACE;
+  s = check_ready(c);
+  if (s != RKV_OK) return s;
+  void* ws = nullptr;
+  s = scratch_address(&ws);
+  if (s != RKV_OK) return s;
+  // Every kernel of the decode writes the parts of the scratch it later
+  // reads (QK table, partial records, rotated rows): nothing needs clearing.
+  return decode_common(q, n_q_heads, c, c->seq_len, softmax_scale, out, nullptr, 0, n_split, ws,
+                       (size_t)RKV_SCRATCH_BYTES, stream);
 }
 
 const char* rkv_status_string(rkv_status s) {

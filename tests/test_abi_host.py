@@ -257,3 +257,27 @@ def test_decode_split_hint(lib):
     two = _cache(n_inst=1, H=2, N=100, base=16)
     assert lib.rkv_cache_init(C.byref(two)) == L.RKV_OK
     assert lib.rkv_decode_split_hint(C.byref(two), 3, C.byref(ns)) == L.RKV_ERR_INVALID_ARG
+
+
+def test_noalloc_decode_checks_the_scratch_limit_before_the_device(lib):
+    null = C.c_void_p(0)
+    q, out = C.c_void_p(0x6000), C.c_void_p(0x5000)
+    ws = C.c_size_t()
+    # a whole 32-layer batch of 8 x 32K sequences needs more than the fixed
+    # scratch: refused before any device call
+    big = _cache(n_inst=256, H=8, N=32768, base=64)
+    assert lib.rkv_cache_init(C.byref(big)) == L.RKV_OK
+    assert lib.rkv_decode_workspace(C.byref(big), 32, 12, C.byref(ws)) == L.RKV_OK
+    assert ws.value > L.RKV_SCRATCH_BYTES
+    assert lib.rkv_decode_attn_noalloc(q, 32, C.byref(big), 0.1, out, 12, null) == \
+        L.RKV_ERR_WORKSPACE
+    # one layer of it fits; with the cache buffers unset the call fails
+    # validation, still before the device
+    layer = _cache(n_inst=8, H=8, N=32768, base=64)
+    assert lib.rkv_cache_init(C.byref(layer)) == L.RKV_OK
+    assert lib.rkv_decode_workspace(C.byref(layer), 32, 12, C.byref(ws)) == L.RKV_OK
+    assert ws.value <= L.RKV_SCRATCH_BYTES
+    assert lib.rkv_decode_attn_noalloc(q, 32, C.byref(layer), 0.1, out, 12, null) == \
+        L.RKV_ERR_INVALID_ARG
+    assert lib.rkv_decode_attn_noalloc(q, 30, C.byref(layer), 0.1, out, 12, null) == \
+        L.RKV_ERR_INVALID_ARG
