@@ -163,7 +163,10 @@ rkv_status rkv_cache_sizes(const rkv_cache *c, size_t sizes[6]);
 /* Workspace bytes for rkv_encode / rkv_select_refs / rkv_quantize. */
 rkv_status rkv_encode_workspace(const rkv_cache *c, size_t *bytes);
 
-/* Encode: K, V dtype [inst][H][N][D] -> the compressed cache in *c.
+/* Encode (paper page, section "DeltaKV Framework Architecture": strided
+ * references, the k nearest by L2 distance, their mean KV_R and the
+ * residual; news page, section "How ResidualKV Works": residuals kept as
+ * quantised codes): K, V dtype [inst][H][N][D] -> the compressed cache in *c.
  * = rkv_select_refs followed by rkv_quantize on the same stream. */
 rkv_status rkv_encode(const void *K, const void *V, const rkv_cache *c,
                       void *ws, size_t ws_bytes, void *stream);
@@ -193,25 +196,35 @@ rkv_status rkv_append(const void *K_new, const void *V_new, int64_t n_new, const
 rkv_status rkv_select_refs(const void *K, const void *V, const rkv_cache *c,
                            void *ws, size_t ws_bytes, void *stream);
 
-/* Residual quantisation with the indices already in c->ref_idx and the
- * references in c->ref_kv (as rkv_select_refs leaves them): for each
- * position and each of K and V, KV_R = the fp32 mean of its selected
- * references (added in ascending slot order), residual = x - KV_R in fp32,
- * and per group of `group` dims an fp16 scale nearest to max|residual|/qmax
- * (qmax = 2^(bits-1)-1) and codes nearest to residual/scale (ties to even),
- * clamped to +-qmax.  bits == 0 stores the exact residual in double.
- * Writes codes_k, codes_v, scales.  ws is unused. */
+/* Residual quantisation (paper page, sections "DeltaKV Framework
+ * Architecture" -- KV_R is the mean of the selected references and the
+ * residual is KV - KV_R -- and "Practical Deployment via Sparse-vLLM" -- the
+ * gather, mean and residual are one fused kernel; news page, section "How
+ * ResidualKV Works": compact quantised residual codes) with the indices
+ * already in c->ref_idx and the references in c->ref_kv (as rkv_select_refs
+ * leaves them): for each position and each of K and V, KV_R = the mean of
+ * its selected references and residual = x - KV_R, both formed in fp32 (an
+ * fp32 sum of the selected rows, divided by k_eff; the result is within
+ * 2^-21 (sum of |selected rows| + |x|) of the exact residual), and per group
+ * of `group` dims an fp16 scale nearest to max|residual|/qmax (qmax =
+ * 2^(bits-1)-1, saturating at 65504) and codes nearest to residual/scale
+ * (ties to even), clamped to +-qmax; both roundings are exact for that fp32
+ * residual.  bits == 0 stores x - KV_R exactly, in double.  Writes codes_k,
+ * codes_v, scales.  ws is unused. */
 rkv_status rkv_quantize(const void *K, const void *V, const rkv_cache *c,
                         void *ws, size_t ws_bytes, void *stream);
 
-/* Rebuild the cache: K_hat, V_hat float [inst][H][N][D].  Reference
+/* Rebuild the cache (paper page, section "DeltaKV Framework Architecture":
+ * KV^ = KV^_delta + KV_R): K_hat, V_hat float [inst][H][N][D].  Reference
  * positions come back from ref_kv; others as KV_R + scale*code (or + the
- * exact residual when bits == 0). */
+ * exact residual when bits == 0, which gives the input rows back bit for
+ * bit).  For parity checks and debugging; decode never materialises it. */
 rkv_status rkv_reconstruct(const rkv_cache *c, float *K_hat, float *V_hat,
                            void *stream);
 
-/* Workspace bytes for rkv_decode_attn with n_q_heads query heads and
- * n_split partitions of the sequence per (instance, KV head). */
+/* Workspace bytes for rkv_decode_attn* with n_q_heads query heads and
+ * n_split partitions of the sequence per (instance, KV head): a QK table
+ * and one partial record per (instance, query head, split). */
 rkv_status rkv_decode_workspace(const rkv_cache *c, int32_t n_q_heads,
                                 int32_t n_split, size_t *bytes);
 
@@ -221,14 +234,36 @@ rkv_status rkv_decode_workspace(const rkv_cache *c, int32_t n_q_heads,
  * device's CU count); the result is a hint, any n_split >= 1 is valid. */
 rkv_status rkv_decode_split_hint(const rkv_cache *c, int32_t n_q_heads, int32_t *n_split);
 
-/* Decode attention straight from the compressed cache: one query per
+/* Decode attention straight from the compressed cache (news page, section
+ * "How ResidualKV Works": tokens are rebuilt on the fly when attention needs
+ * them; paper page, section "Practical Deployment via Sparse-vLLM": the
+ * reconstruction is fused to save memory bandwidth): one query per
  * instance, q dtype [inst][n_q_heads][D]; query head h reads KV head
  * h / (n_q_heads / H).  out float [inst][n_q_heads][D] =
  * softmax(softmax_scale * q . K^) . V^ over all N positions, where K^, V^
  * are the reconstructed cache.  The reference mean is folded into the dot
  * products (q . KV_R is the mean of q . K_ref over the selected slots), so
  * no K^/V^ is materialised.  n_split >= 1 partitions each sequence; the
- * result does not depend on it beyond rounding.  bits must be 2, 4 or 8. */
+ * result does not depend on it beyond rounding.
+ *
+ * Arithmetic: q enters fp16 matrix products with a power-of-two pre-scale
+ * (the largest |q| of a KV head's query heads moved to [2^8, 2^9)) and the
+ * products p * scale_V with a power-of-two exponent per 1024 positions of a
+ * split (the largest V scale there moved below 1), so no magnitude of q or
+ * V overflows or flushes them; each keeps fp16's 11 bits for values within
+ * 2^14 of that largest one, and degrades gradually below (fp16 subnormals).
+ * Softmax, scales and merges run in fp32.
+ *
+ * Limits (RKV_ERR_UNSUPPORTED, checked before any device work): with
+ * bits > 0 the query heads of one KV head times the scale groups per row,
+ * G * (D / group), must not exceed 16 (e.g. GQA 4 with 32-dim groups, GQA
+ * 16 with 128-dim groups); the QK table and the reference weights of every
+ * reference are held on chip, (2G + 2 ceil(G/2)) (n_refs + 8) + 1040 G
+ * floats of LDS, which must fit 160 KiB (GQA 4: about 3000 references).
+ * bits == 0 (exact residuals) rebuilds every attended position from KV_R
+ * plus its stored residual and runs plain softmax attention: G <= 16, no
+ * per-reference LDS.  A query head whose KV head attends no position (an
+ * empty tile selection) gets a zero row. */
 rkv_status rkv_decode_attn(const void *q, int32_t n_q_heads,
                            const rkv_cache *c, float softmax_scale,
                            float *out, int32_t n_split, void *ws,

@@ -55,6 +55,19 @@ __host__ __device__ constexpr int invperm_of(int o) {
 
 __device__ inline f16x2 as_h2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
 
+// A float that is the same in every lane, moved to a scalar register (the
+// bits are passed through: the builtin takes an int).
+__device__ inline float uniform_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// Unsigned maximum of the two 16-bit halves of a and b (one packed op).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
 // Offset of a code decoded without the final subtract: 1024 + 2^(BITS-1).
 template <int BITS>
 constexpr float code_bias() { return 1024.f + (float)(1 << (BITS - 1)); }
@@ -297,6 +310,7 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
     const float* __restrict__ qrot) {
   // N: positions the cache holds (layout); Nlen <= N: positions attended
   constexpr int HPL = 4 / NG;  // query heads per lane in the score layout
+  constexpr int VW = (NG + 1) / 2;  // scale words holding the V scales
   constexpr int GS = 128 / NG;  // dims per scale group
   constexpr int CT = kChunkTiles * kDecTile;  // tokens per chunk
   // logit rows padded by 16 floats: the 4 heads of one position (lane quads)
@@ -316,7 +330,15 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
   float* m_s = lg_s + G * CTP;                                    // [16] block max per head
   float* wm_s = m_s + 16;                                         // [4][16] wave maxima
   float* sc_s = wm_s + 64;                                        // [16] rescale factors
-  _Float16* pst_all = reinterpret_cast<_Float16*>(sc_s + 16);     // [4][16][32]
+  // P.V operand scaling: the fp16 operand is p * scale_V * 2^-E, with 2^E
+  // (vp_s[0]) above every V scale seen so far in this split, so the product
+  // stays below 1 whatever the magnitude of V; the accumulators hold
+  // P.V / 2^E.  vp_s[1]: the factor the accumulators take when E grows;
+  // vp_s[2]: 2^-E (0 while every V scale is 0); vw_s[4]: the waves' chunk
+  // maxima of the V scale bits.
+  float* vp_s = sc_s + 16;                                        // [4]
+  uint32_t* vw_s = reinterpret_cast<uint32_t*>(vp_s + 4);         // [4]
+  _Float16* pst_all = reinterpret_cast<_Float16*>(vw_s + 4);      // [4][16][32]
   _Float16* sst_all = pst_all + 4 * 16 * kDecTile;                // [4][NG][32]
 
   const int tid = threadIdx.x;
@@ -366,6 +388,7 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
     for (int64_t e = tid; e < G * ls; e += 256) wt_s[e] = 0.f;
     for (int e = tid; e < 4 * 16 * kDecTile; e += 256) pst_all[e] = (_Float16)0.f;
     if (tid < 16) m_s[tid] = -INFINITY;
+    if (tid < 4) vp_s[tid] = 0.f;
   }
 
   // ---- A operand of the score MFMA: rows (h, g); lane quad covers dims
@@ -373,6 +396,11 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
   //      are scored against the rotated query qrot = H D q / 8 instead
   //      (q . f_d(y) = (H D q / 8) . y).
   f16x8 aq[4];
+  // The query enters the f16 MFMA scaled by a power of two, 2^s, that puts
+  // the largest |q| of the KV head's query heads in [2^8, 2^9): no fp16
+  // overflow or underflow for any magnitude of q.  qinv = 2^-s (the same in
+  // every lane) undoes it on the logit.
+  float qinv;
   {
     // the lane's 32 query values are 4 runs of 8 dims (32*quad + 8*s): load
     // them whole (one branch for the source), then permute and mask to the
@@ -390,12 +418,25 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
 #pragma unroll
       for (int s = 0; s < 4; ++s) load8(qq + 8 * s, qv[s]);
     }
+    float qm = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qm = fmaxf(qm, fabsf(qv[s][e]));
+    if (!live) qm = 0.f;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) qm = fmaxf(qm, __shfl_xor(qm, off));
+    qm = uniform_f32(qm);  // largest |q| of the G heads (all 128 dims)
+    int qe = 0;
+    (void)frexpf(qm, &qe);                   // qm in [2^(qe-1), 2^qe), or qe = 0 for 0
+    const float qs = (qm > 0.f && qm <= FLT_MAX) ? ldexpf(1.f, 9 - qe) : 1.f;
+    qinv = uniform_f32(1.f / qs);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int dim = 32 * quad + 8 * s + perm_of<BITS>(e);
-        aq[s][e] = (_Float16)((live && dim / GS == g) ? qv[s][perm_of<BITS>(e)] : 0.f);
+        aq[s][e] = (_Float16)((live && dim / GS == g) ? qv[s][perm_of<BITS>(e)] * qs : 0.f);
       }
     }
   }
@@ -432,6 +473,7 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
   f32x4 o[8];
 #pragma unroll
   for (int b = 0; b < 8; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float vinv = 0.f;  // 2^-E of the current chunk (the same in every lane)
 
   auto load_slots_of = [&](int32_t tok, uint32_t (&iw)[KM / 2]) RKV_INLINE {
     if constexpr (EX) {
@@ -475,12 +517,18 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
   // references) is chosen per tile, wave-uniformly, so each variant is
   // straight-line code.
   auto computeA_t = [&](auto ft_c, int32_t tb, int32_t t, int32_t c0, const TileRefs& tr,
-                        const ARegs& r, float (&wmax)[HPL]) RKV_INLINE {
+                        const ARegs& r, float (&wmax)[HPL], uint32_t& vmx) RKV_INLINE {
     constexpr bool FT = decltype(ft_c)::value;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int32_t tok = tb + 16 * b + n;
       const bool valid = tok < N32;
+      // largest V scale of the chunk, on the packed scale words (fp16 bits
+      // of non-negative values order like the values; with one group the
+      // low half is the K scale and is ignored); rows past the length
+      // reread a row inside it
+#pragma unroll
+      for (int m = 0; m < VW; ++m) vmx = pk_max_u16(vmx, r.sw[b][(NG >> 1) + m]);
       f32x4 acc = qbias;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -531,7 +579,7 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
             const float sk = half_bits_to_f32((uint16_t)(r.sw[b][g >> 1] >> (16 * (g & 1))));
             res = __builtin_fmaf(sk, acc[hh * NG + g], res);
           }
-          const float sc_ = slot >= 0 ? sref : res + rs * (1.0f / KM);
+          const float sc_ = slot >= 0 ? sref : __builtin_fmaf(res, qinv, rs * (1.0f / KM));
           const float lg = valid ? alpha * sc_ : -INFINITY;
           lg_s[h * CTP + u] = lg;
           wmax[hh] = fmaxf(wmax[hh], lg);
@@ -553,7 +601,7 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
                 const float sk = half_bits_to_f32((uint16_t)(r.sw[b][g >> 1] >> (16 * (g & 1))));
                 res = __builtin_fmaf(sk, acc[hh * NG + g], res);
               }
-              sc_ = res + rs * inv_keff;
+              sc_ = __builtin_fmaf(res, qinv, rs * inv_keff);
             }
             lg = alpha * sc_;
           }
@@ -563,13 +611,14 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
       }
     }
   };
-  auto computeA = [&](int32_t t, int32_t c0, const ARegs& r, float (&wmax)[HPL]) RKV_INLINE {
+  auto computeA = [&](int32_t t, int32_t c0, const ARegs& r, float (&wmax)[HPL],
+                      uint32_t& vmx) RKV_INLINE {
     const int32_t tb = tile_of(t) * kDecTile;
     const TileRefs tr = tile_refs(tb, N32, sc);
     if (EX && tr.cb >= KM)
-      computeA_t(std::true_type{}, tb, t, c0, tr, r, wmax);
+      computeA_t(std::true_type{}, tb, t, c0, tr, r, wmax, vmx);
     else
-      computeA_t(std::false_type{}, tb, t, c0, tr, r, wmax);
+      computeA_t(std::false_type{}, tb, t, c0, tr, r, wmax, vmx);
   };
   auto loadB = [&](int32_t t, BRegs& r) RKV_INLINE {
     const int32_t tb = tile_of(t) * kDecTile;
@@ -693,10 +742,12 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
         }
       }
       if (quad == 0) {
+        // scale_V * 2^-E_g: below 2, so p * scale_V * 2^-E_g stays in range
 #pragma unroll
         for (int g = 0; g < NG; ++g)
-          sst[g * kDecTile + pos] =
-              __builtin_bit_cast(_Float16, (uint16_t)(r.sw[b][(NG + g) >> 1] >> (16 * ((NG + g) & 1))));
+          sst[g * kDecTile + pos] = (_Float16)(
+              half_bits_to_f32((uint16_t)(r.sw[b][(NG + g) >> 1] >> (16 * ((NG + g) & 1)))) *
+              vinv);
       }
     }
 #pragma unroll
@@ -745,6 +796,7 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
     float wmax[HPL];
 #pragma unroll
     for (int hh = 0; hh < HPL; ++hh) wmax[hh] = -INFINITY;
+    uint32_t vmx = 0u;
     {
       // two register sets alternate (unrolled by 2): no copies of loads in flight
       // entries past the chunk load its last entry (never computed)
@@ -753,11 +805,11 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
       loadA(min(t, c1 - 1), ra);
       while (t < c1) {
         loadA(min(t + 4, c1 - 1), rb);
-        computeA(t, c0, ra, wmax);
+        computeA(t, c0, ra, wmax, vmx);
         t += 4;
         if (t >= c1) break;
         loadA(min(t + 4, c1 - 1), ra);
-        computeA(t, c0, rb, wmax);
+        computeA(t, c0, rb, wmax, vmx);
         t += 4;
       }
     }
@@ -766,7 +818,30 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
       const float m = quad_max(wmax[hh]);
       if (n == 0 && h0 + hh < G) wm_s[w * 16 + h0 + hh] = m;
     }
+    {
+      uint32_t v = vmx;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v = pk_max_u16(v, (uint32_t)__shfl_xor((int)v, off));
+      if (lane == 0) vw_s[w] = v;
+    }
     __syncthreads();
+    if (tid == 32) {
+      // E: the smallest power of two above every V scale so far (never
+      // shrinks, so the accumulators are only ever scaled down)
+      uint32_t mw = pk_max_u16(pk_max_u16(vw_s[0], vw_s[1]), pk_max_u16(vw_s[2], vw_s[3]));
+      if (NG == 1) mw >>= 16;  // the V scale is the high half
+      const float mv = half_bits_to_f32((uint16_t)max(mw & 0xFFFFu, mw >> 16));
+      const float po = vp_s[0];
+      float pn = po;
+      if (mv > 0.f) {
+        int e = 0;
+        (void)frexpf(mv, &e);  // mv < 2^e
+        pn = fmaxf(po, ldexpf(1.f, e));
+      }
+      vp_s[1] = po > 0.f ? po / pn : 1.f;  // exact: powers of two
+      vp_s[0] = pn;
+      vp_s[2] = pn > 0.f ? 1.f / pn : 0.f;
+    }
     if (tid < 16) {
       float f = 1.f;
       if (tid < G) {
@@ -783,6 +858,7 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
       // rescale what was accumulated against the old maximum
       bool any = false;
       for (int h = 0; h < G; ++h) any |= sc_s[h] != 1.f;
+      any |= vp_s[1] != 1.f;
       if (any) {
         for (int h = 0; h < G; ++h) {
           const float f = sc_s[h];
@@ -796,7 +872,7 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
         for (int j = 0; j < 4; ++j) {
           const float f = (4 * quad + j < G) ? sc_s[4 * quad + j] : 1.f;
 #pragma unroll
-          for (int b = 0; b < 8; ++b) o[b][j] *= f;
+          for (int b = 0; b < 8; ++b) o[b][j] *= f * vp_s[1];
         }
       }
     }
@@ -805,6 +881,8 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
     float mh[HPL];
 #pragma unroll
     for (int hh = 0; hh < HPL; ++hh) mh[hh] = (h0 + hh < G) ? m_s[h0 + hh] : 0.f;
+    vinv = uniform_f32(vp_s[2]);
+
     {
       BRegs ra, rb;
       int32_t t = c0 + w;
@@ -861,8 +939,8 @@ __global__ __launch_bounds__(256, (kDecodeBlocksPerCU<T, BITS, NG, KM, EX>())) v
   }
   for (int e = tid; e < G * 128; e += 256) {
     const int h = e >> 7, d = e & 127;
-    pr0[h * hstride + 4 + d] = ((ow[h * 128 + d] + ow[(G + h) * 128 + d]) + ow[(2 * G + h) * 128 + d]) +
-                               ow[(3 * G + h) * 128 + d];
+    pr0[h * hstride + 4 + d] = (((ow[h * 128 + d] + ow[(G + h) * 128 + d]) + ow[(2 * G + h) * 128 + d]) +
+                                ow[(3 * G + h) * 128 + d]) * vp_s[0];
   }
 }
 
@@ -1091,13 +1169,16 @@ __global__ __launch_bounds__(CT) void k_combine(const float* __restrict__ part,
     const float l = sm[0];
     const float o = sm[4 + tid];
     const int64_t at = (inst * Hq + hq) * 128 + tid;
+    // a head that attended no position (l = 0: an empty tile selection)
+    // gets a zero row
+    const float il = l > 0.f ? 1.f / l : 0.f;
     if (ores) {
       // latent codes: the residual part is still rotated; f_d is applied
       // to the whole row afterwards
-      ores[at] = o / l;
-      out[at] = s / l;
+      ores[at] = o * il;
+      out[at] = s * il;
     } else {
-      out[at] = (o + s) / l;
+      out[at] = (o + s) * il;
     }
   }
 }
@@ -1152,6 +1233,146 @@ __global__ __launch_bounds__(256) void k_latent_out(const float* __restrict__ or
   out[r * 128 + 2 * l + 1] += b * 0.125f;
 }
 
+// ------------------------------------------------------- exact residuals
+// bits = 0 keeps every residual exactly (fp64), so attention runs on the
+// rebuilt cache itself: each attended position is KV_R + residual, with
+// KV_R the fp32 mean the encoder took (ascending-slot fp32 sum, divided by
+// k_eff), which gives back the input rows.  Plain softmax attention, one
+// block per (instance, KV head, split); wave w takes positions w, w+4, ...
+// of each tile, lane l dims 2l and 2l+1.  Writes the same partial records as
+// k_decode (W = 0: the reference mean is already inside every row), so
+// k_combine merges them unchanged.  G <= 16.
+template <typename T>
+__device__ inline float2 ld_pair(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    return make_float2(bf16_lo(w), bf16_hi(w));
+  } else {
+    return *reinterpret_cast<const float2*>(p);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_decode_exact(
+    const T* __restrict__ q, const T* __restrict__ ref_kv, const uint16_t* __restrict__ idx,
+    const double* __restrict__ rk, const double* __restrict__ rv, float* __restrict__ part,
+    float alpha, int64_t N, int64_t Nlen, int64_t n_refs, Sched sc, int k, int G, int H,
+    int n_split, const int32_t* __restrict__ tile_list, int32_t n_list) {
+  __shared__ float ms[4][16], ls[4][16];
+  __shared__ float os[4][16][128];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int64_t inst = blockIdx.z;
+  const int64_t ih = inst * H + kvh;
+  const int Hq = H * G;
+  const int32_t tiles_len = (int32_t)((Nlen + kDecTile - 1) / kDecTile);
+  const int32_t* tl = tile_list ? tile_list + ih * n_list : nullptr;
+  const int32_t n_ent = tl ? n_list : tiles_len;
+  const int32_t tps = (n_ent + n_split - 1) / n_split;
+  const int32_t t0 = split * tps;
+  const int32_t t1 = (t0 + tps < n_ent) ? t0 + tps : n_ent;
+  const int d0 = 2 * lane;
+  float qa[16], qb[16], m[16], l[16], o0[16], o1[16];
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    qa[h] = qb[h] = 0.f;
+    m[h] = -INFINITY;
+    l[h] = o0[h] = o1[h] = 0.f;
+    if (h < G) {
+      const float2 v = ld_pair(q + ((inst * Hq + kvh * G + h) * 128 + d0));
+      qa[h] = v.x;
+      qb[h] = v.y;
+    }
+  }
+  const T* rkb = ref_kv + ih * 2 * n_refs * 128;   // K plane; V plane at + n_refs * 128
+  for (int32_t e = t0; e < t1; ++e) {
+    int32_t tile = e;
+    if (tl) {
+      const int32_t x = tl[e];
+      tile = (x >= 0 && x < tiles_len) ? x : tiles_len;
+    }
+    for (int u = w; u < kDecTile; u += 4) {
+      const int64_t p = (int64_t)tile * kDecTile + u;
+      if (p >= Nlen) break;
+      float2 kk, vv;
+      const int32_t slot = sched_slot((int32_t)p, sc);
+      if (slot >= 0) {
+        kk = ld_pair(rkb + (int64_t)slot * 128 + d0);
+        vv = ld_pair(rkb + (n_refs + slot) * 128 + d0);
+      } else {
+        const int32_t cnt = sched_count_le((int32_t)p, sc);
+        const int keff = cnt < k ? cnt : k;
+        float sk0 = 0.f, sk1 = 0.f, sv0 = 0.f, sv1 = 0.f;
+        for (int j = 0; j < keff; ++j) {
+          const int64_t r = idx[(ih * N + p) * k + j];
+          const float2 a = ld_pair(rkb + r * 128 + d0);
+          const float2 b = ld_pair(rkb + (n_refs + r) * 128 + d0);
+          if (j == 0) {
+            sk0 = a.x; sk1 = a.y; sv0 = b.x; sv1 = b.y;
+          } else {
+            sk0 += a.x; sk1 += a.y; sv0 += b.x; sv1 += b.y;
+          }
+        }
+        const float kf = (float)keff;
+        const double2 dk = *reinterpret_cast<const double2*>(rk + (ih * N + p) * 128 + d0);
+        const double2 dv = *reinterpret_cast<const double2*>(rv + (ih * N + p) * 128 + d0);
+        kk = make_float2((float)((double)(sk0 / kf) + dk.x), (float)((double)(sk1 / kf) + dk.y));
+        vv = make_float2((float)((double)(sv0 / kf) + dv.x), (float)((double)(sv1 / kf) + dv.y));
+      }
+#pragma unroll
+      for (int h = 0; h < 16; ++h) {
+        if (h < G) {
+          float sdot = __builtin_fmaf(qa[h], kk.x, qb[h] * kk.y);
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) sdot += __shfl_xor(sdot, off);
+          const float lg = alpha * sdot;
+          const float mn = fmaxf(m[h], lg);
+          const float f = m[h] > -INFINITY ? __expf(m[h] - mn) : 0.f;
+          const float pe = __expf(lg - mn);
+          l[h] = l[h] * f + pe;
+          o0[h] = __builtin_fmaf(pe, vv.x, o0[h] * f);
+          o1[h] = __builtin_fmaf(pe, vv.y, o1[h] * f);
+          m[h] = mn;
+        }
+      }
+    }
+  }
+  // merge the four waves
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    if (h < G) {
+      if (lane == 0) {
+        ms[w][h] = m[h];
+        ls[w][h] = l[h];
+      }
+      os[w][h][d0] = o0[h];
+      os[w][h][d0 + 1] = o1[h];
+    }
+  }
+  __syncthreads();
+  const int64_t rec = part_rec_floats(n_refs);
+  const int64_t nrp = ((n_refs + 3) / 4) * 4;
+  for (int h = 0; h < G; ++h) {
+    float* pr = part + ((inst * Hq + kvh * G + h) * n_split + split) * rec;
+    const float M = fmaxf(fmaxf(ms[0][h], ms[1][h]), fmaxf(ms[2][h], ms[3][h]));
+    float fw[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) fw[x] = ms[x][h] > -INFINITY ? __expf(ms[x][h] - M) : 0.f;
+    if (threadIdx.x < 128) {
+      const int d = threadIdx.x;
+      pr[4 + d] = ((fw[0] * os[0][h][d] + fw[1] * os[1][h][d]) + fw[2] * os[2][h][d]) +
+                  fw[3] * os[3][h][d];
+    }
+    if (threadIdx.x == 0) {
+      pr[0] = M;
+      pr[1] = ((fw[0] * ls[0][h] + fw[1] * ls[1][h]) + fw[2] * ls[2][h]) + fw[3] * ls[3][h];
+    }
+    for (int64_t j = threadIdx.x; j < nrp; j += 256) pr[132 + j] = 0.f;
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 static size_t qk_bytes(int64_t n_inst, int n_q_heads, int64_t n_refs) {
   const size_t b = (size_t)n_inst * n_q_heads * (((n_refs + 3) / 4) * 4) * 4;
@@ -1179,7 +1400,7 @@ size_t decode_ws_bytes(int64_t n_inst, int H, int n_q_heads, int n_split, int64_
 size_t decode_lds_bytes(int G, int NG, int64_t n_refs) {
   const int64_t nrp = ((n_refs + 3) / 4) * 4;
   return (size_t)((2 * G + 2 * ((G + 1) / 2)) * (nrp + 8) + G * (kChunkTiles * kDecTile + kLgPad) +
-                  96) * 4 +
+                  96 + 4 + 4) * 4 +  // m_s, wm_s, sc_s; vp_s; vw_s
          (size_t)(4 * 16 + 4 * NG) * kDecTile * 2;
 }
 
@@ -1189,11 +1410,39 @@ size_t combine_lds_bytes(int G, int64_t n_refs, int n_split) {
   return (size_t)(nrp + n_split + 132 + (1024 / 16) * 128) * 4;  // the 1024-thread form
 }
 
-// Whether the decode kernels' LDS fits one CU (160 KiB).
-bool decode_fits(int G, int group, int64_t n_refs, int n_split) {
+// Whether the decode kernels' LDS fits one CU (160 KiB).  The exact-residual
+// decode keeps no per-reference state; only its combine does.
+bool decode_fits(int G, int group, int64_t n_refs, int n_split, bool exact) {
   const int NG = 128 / group;
-  return decode_lds_bytes(G, NG, n_refs) <= 160 * 1024 &&
+  return (exact || decode_lds_bytes(G, NG, n_refs) <= 160 * 1024) &&
          combine_lds_bytes(G, n_refs, n_split) <= 160 * 1024;
+}
+
+template <typename T>
+hipError_t launch_decode_exact(const void* q, int n_q_heads, const uint16_t* idx,
+                               const void* ref_kv, const uint8_t* ck, const uint8_t* cv,
+                               float alpha, float* out, int n_split, void* ws, int64_t n_inst,
+                               int H, int64_t N, int64_t len, int64_t n_refs, Sched sc, int k,
+                               const int32_t* tile_list, int32_t n_list, hipStream_t st) {
+  const int G = n_q_heads / H;
+  float* part = (float*)((char*)ws + qk_bytes(n_inst, n_q_heads, n_refs));
+  hipLaunchKernelGGL(k_decode_exact<T>, dim3(n_split, H, (unsigned)n_inst), dim3(256), 0, st,
+                     (const T*)q, (const T*)ref_kv, idx, (const double*)ck, (const double*)cv,
+                     part, alpha, N, len, n_refs, sc, k, G, H, n_split, tile_list, n_list);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n_valid = sched_count((int32_t)len, sc);
+  const bool wide = (int64_t)H * n_inst * G <= 512;
+  const size_t clds = combine_lds_bytes(G, n_refs, n_split);
+  auto comb = wide ? k_combine<T, 1024> : k_combine<T, 256>;
+  if (clds > 64 * 1024) {
+    e = hipFuncSetAttribute((const void*)comb, hipFuncAttributeMaxDynamicSharedMemorySize, (int)clds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(comb, dim3(H, (unsigned)n_inst, G), dim3(wide ? 1024 : 256), clds, st, part,
+                     (const T*)ref_kv, (const uint16_t*)nullptr, 0, 128, out, G, H, n_refs, n_valid,
+                     n_split, (float*)nullptr);
+  return hipGetLastError();
 }
 
 template <typename T, int BITS, int NG, int KM, bool EX>
@@ -1304,6 +1553,11 @@ hipError_t launch_decode(int dtype, int bits, const void* q, int n_q_heads, cons
                          void* ws, int64_t n_inst, int H, int64_t N, int64_t len, int64_t n_refs, Sched sc,
                          int k, int group, const int32_t* tile_list, int32_t n_list,
                          const LatMask* lm, hipStream_t st) {
+  if (bits == 0) {
+    if (dtype == 0)
+      return launch_decode_exact<float>(q, n_q_heads, idx, ref_kv, ck, cv, softmax_scale, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
+    return launch_decode_exact<__bf16>(q, n_q_heads, idx, ref_kv, ck, cv, softmax_scale, out, n_split, ws, n_inst, H, N, len, n_refs, sc, k, tile_list, n_list, st);
+  }
   if (dtype == 0)
     return launch_decode_b<float>(bits, group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, lm, st);
   return launch_decode_b<__bf16>(bits, group, k, q, n_q_heads, idx, ref_kv, ref_scales, ref_bits, group, ck, cv, sc16, softmax_scale, out, n_split, ws, n_inst, H, N, len, n_refs, sc, tile_list, n_list, lm, st);

@@ -39,7 +39,7 @@ hipError_t launch_decode(int dtype, int bits, const void* q, int n_q_heads, cons
                          int32_t n_list, const LatMask* lm, hipStream_t st);
 size_t decode_ws_bytes(int64_t n_inst, int H, int n_q_heads, int n_split, int64_t n_refs,
                        bool latent);
-bool decode_fits(int G, int group, int64_t n_refs, int n_split);
+bool decode_fits(int G, int group, int64_t n_refs, int n_split, bool exact);
 }  // namespace rkv
 
 using rkv::Sched;
@@ -316,10 +316,15 @@ static rkv_status decode_common(const void* q, int32_t n_q_heads, const rkv_cach
   if (s != RKV_OK) return s;
   if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0 || n_split < 1 || n_split > 4096)
     return RKV_ERR_INVALID_ARG;
-  if (c->bits == 0) return RKV_ERR_UNSUPPORTED;
   const int G = n_q_heads / c->n_kv_heads;
-  if (G * (c->head_dim / c->group) > 16) return RKV_ERR_UNSUPPORTED;
-  if (!rkv::decode_fits(G, c->group, c->n_refs, n_split)) return RKV_ERR_UNSUPPORTED;
+  // The quantised decode holds one MFMA row per (query head, scale group) of
+  // a KV head: at most 16.  Exact residuals (bits = 0) take one row per
+  // query head.
+  const int rows = c->bits == 0 ? G : G * (c->head_dim / c->group);
+  if (rows > 16) return RKV_ERR_UNSUPPORTED;
+  // LDS holds the QK table and reference weights of every reference
+  if (!rkv::decode_fits(G, c->bits == 0 ? 128 : c->group, c->n_refs, n_split, c->bits == 0))
+    return RKV_ERR_UNSUPPORTED;
   if (c->n_inst == 0) return RKV_OK;
   if (!q || !out || !al16(q) || !al16(out)) return RKV_ERR_INVALID_ARG;
   if (c->seq_len == 0) return RKV_ERR_INVALID_ARG;

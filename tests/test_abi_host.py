@@ -172,9 +172,11 @@ def test_entry_points_validate_before_touching_the_device(lib):
     assert lib.rkv_decode_attn_tiles(C.c_void_p(0x6000), 32, C.byref(c), 0.1,
                                      C.c_void_p(0x8000), 4, out, 4, C.c_void_p(0x7000),
                                      ws.value - 1, null) == L.RKV_ERR_WORKSPACE
+    # exact residuals (bits = 0) decode too; the workspace is still checked
     c.bits = 0
+    assert lib.rkv_decode_workspace(C.byref(c), 32, 4, C.byref(ws)) == L.RKV_OK
     assert lib.rkv_decode_attn(C.c_void_p(0x6000), 32, C.byref(c), 0.1, out, 4,
-                               C.c_void_p(0x7000), ws.value, null) == L.RKV_ERR_UNSUPPORTED
+                               C.c_void_p(0x7000), ws.value - 1, null) == L.RKV_ERR_WORKSPACE
     # n_refs not initialised for this shape
     c2 = _cache()
     assert lib.rkv_encode(C.c_void_p(1), C.c_void_p(1), C.byref(c2), null, 0, null) == \
@@ -281,3 +283,39 @@ def test_noalloc_decode_checks_the_scratch_limit_before_the_device(lib):
         L.RKV_ERR_INVALID_ARG
     assert lib.rkv_decode_attn_noalloc(q, 30, C.byref(layer), 0.1, out, 12, null) == \
         L.RKV_ERR_INVALID_ARG
+
+
+def test_decode_refuses_what_its_layout_cannot_hold(lib):
+    """Decode holds one MFMA row per (query head, scale group) of a KV head
+    (at most 16), and keeps the QK table and reference weights of every
+    reference in LDS; both limits come back as RKV_ERR_UNSUPPORTED before
+    any device work."""
+    null = C.c_void_p(0)
+    q, out, ws = C.c_void_p(0x6000), C.c_void_p(0x5000), C.c_void_p(0x7000)
+    big = 1 << 40
+
+    def ready(c):
+        assert lib.rkv_cache_init(C.byref(c)) == L.RKV_OK
+        for name in ("ref_idx", "codes_k", "codes_v", "scales", "ref_kv"):
+            setattr(c, name, 0x10000)
+        return c
+
+    # GQA 8 with 32-dim groups: 8 x 4 = 32 rows
+    c = ready(_cache(n_inst=1, H=1, N=4096, base=64))
+    assert lib.rkv_decode_attn(q, 8, C.byref(c), 0.1, out, 2, ws, big, null) == L.RKV_ERR_UNSUPPORTED
+    # the same with 128-dim groups fits (8 rows) up to the workspace check
+    c.group = 128
+    assert lib.rkv_decode_attn(q, 8, C.byref(c), 0.1, out, 2, ws, 16, null) == L.RKV_ERR_WORKSPACE
+    # exact residuals: one row per query head, 17 heads are too many
+    c0 = ready(_cache(n_inst=1, H=1, N=4096, base=64))
+    c0.bits = 0
+    assert lib.rkv_decode_attn(q, 17, C.byref(c0), 0.1, out, 2, ws, big, null) == L.RKV_ERR_UNSUPPORTED
+    assert lib.rkv_decode_attn(q, 16, C.byref(c0), 0.1, out, 2, ws, 16, null) == L.RKV_ERR_WORKSPACE
+    # 4096 references with GQA 4: the per-reference LDS state does not fit
+    many = ready(_cache(n_inst=1, H=1, N=16384, base=4))
+    assert many.n_refs == 4096
+    assert lib.rkv_decode_attn(q, 4, C.byref(many), 0.1, out, 2, ws, big, null) == \
+        L.RKV_ERR_UNSUPPORTED
+    # 2048 references fit
+    fits = ready(_cache(n_inst=1, H=1, N=8192, base=4))
+    assert lib.rkv_decode_attn(q, 4, C.byref(fits), 0.1, out, 2, ws, 16, null) == L.RKV_ERR_WORKSPACE

@@ -270,6 +270,102 @@ def test_decode_parity(case):
         assert err <= 2e-3
 
 
+# (log2 of the q scaling, log2 of the V scaling, code bits): the query enters
+# the f16 score MFMA with a power-of-two pre-scale and the P.V operand with a
+# power-of-two exponent per softmax chunk, so decode holds its bar whatever
+# the magnitudes (fp16 would otherwise overflow or flush these).
+SCALED = [(8, 0, 4), (-8, 0, 4), (16, 0, 4), (-20, 0, 4), (0, -8, 4), (0, -12, 4), (0, -20, 4),
+          (0, 12, 4), (-8, -20, 8), (0, -20, 2)]
+
+
+@pytest.mark.parametrize("case", SCALED, ids=[f"q2^{a}_v2^{b}_int{c}" for a, b, c in SCALED])
+def test_decode_parity_scaled_inputs(case):
+    _need_gpu()
+    eq, ev, bits = case
+    cfg = _cfg(1, n_kv_heads=2, n_q_heads=8)
+    N = 1000
+    say(f"[decode parity, q x 2^{eq}, V x 2^{ev}] int{bits}")
+    K, V = make_kv(cfg, 1, N)
+    V.mul_(2.0 ** ev)
+    q = make_q(cfg, 1)
+    q.mul_(2.0 ** eq)
+    cache = encode(cfg, K, V, bits, 1, N)
+    Kn, Vn, qn = to_np_f32(K), to_np_f32(V), to_np_f32(q)
+    for scale in (1.0 / math.sqrt(cfg.head_dim), 1.0):
+        got = rkv.rkv_decode_attn(q, cfg.n_q_heads, cache, scale, n_split=3).cpu().numpy()
+        want = _oracle_decode(cfg, Kn, Vn, qn, bits, scale)
+        err = attn_err(got, want)
+        say(f"  scale={scale:.4f} worst per-head rel L2 = {err:.2e}")
+        assert err <= 2e-3
+
+
+EXACT = [("tiny_f32", get_config(0), 1, 1024, 1e-5), ("llama_bf16_gqa4", _cfg(1, n_kv_heads=2, n_q_heads=8), 2, 700, 1e-5),
+         ("stress_bf16_k16", _cfg(4, n_kv_heads=2, n_q_heads=14, batch=1), 1, 600, 1e-5)]
+
+
+@pytest.mark.parametrize("case", EXACT, ids=[c[0] for c in EXACT])
+def test_decode_without_quantisation_is_full_attention(case):
+    """bits = 0 keeps exact residuals: decode over the rebuilt cache is
+    textbook softmax attention over the raw K, V (dense, over a prefix, and
+    over listed tiles)."""
+    _need_gpu()
+    name, cfg, n_inst, N, tol = case
+    say(f"[exact decode] {name}: N={N}")
+    K, V = make_kv(cfg, n_inst, N)
+    q = make_q(cfg, n_inst)
+    cache = encode(cfg, K, V, 0, n_inst, N)
+    Kn, Vn, qn = to_np_f32(K), to_np_f32(V), to_np_f32(q)
+    G = cfg.n_q_heads // cfg.n_kv_heads
+    L = N - 77
+    lists = _tile_lists(n_inst, cfg.n_kv_heads, N, 0.4, seed=5)
+    tiles = torch.from_numpy(lists).cuda()
+    for scale in (1.0 / math.sqrt(cfg.head_dim), 1.0):
+        want = np.stack([oracle.decode_attn(qn[i], Kn[i].astype(np.float64), Vn[i].astype(np.float64), scale)
+                         for i in range(n_inst)])
+        got = rkv.rkv_decode_attn(q, cfg.n_q_heads, cache, scale, n_split=3).cpu().numpy()
+        err = attn_err(got, want)
+        want_l = np.stack([oracle.decode_attn(qn[i], Kn[i, :, :L].astype(np.float64),
+                                              Vn[i, :, :L].astype(np.float64), scale)
+                           for i in range(n_inst)])
+        got_l = rkv.rkv_decode_attn_len(q, cfg.n_q_heads, cache, L, scale, n_split=2).cpu().numpy()
+        err_l = attn_err(got_l, want_l)
+        want_t = np.zeros_like(want)
+        for i in range(n_inst):
+            for h in range(cfg.n_kv_heads):
+                pos = oracle.tile_positions(lists[i, h], N)
+                want_t[i, h * G:(h + 1) * G] = oracle.decode_attn(
+                    qn[i, h * G:(h + 1) * G], Kn[i, h][None, pos].astype(np.float64),
+                    Vn[i, h][None, pos].astype(np.float64), scale)
+        got_t = rkv.rkv_decode_attn_tiles(q, cfg.n_q_heads, cache, scale, tiles, n_split=3).cpu().numpy()
+        err_t = attn_err(got_t, want_t)
+        say(f"  scale={scale:.4f} worst per-head rel L2: dense {err:.2e}, prefix {err_l:.2e}, "
+            f"tiles {err_t:.2e}")
+        assert max(err, err_l, err_t) <= tol
+
+
+def test_decode_tiles_empty_selection_gives_zero_rows():
+    """A KV head whose list selects no position attends nothing: its query
+    heads get zero rows, the other heads are unaffected."""
+    _need_gpu()
+    cfg = _cfg(1, n_kv_heads=2, n_q_heads=8)
+    N = 640
+    say("[decode tiles] empty selection")
+    K, V = make_kv(cfg, 1, N)
+    q = make_q(cfg, 1)
+    cache = encode(cfg, K, V, 4, 1, N)
+    n_tiles = N // 32
+    lists = np.array([[[3, 7, 11], [-1, n_tiles, n_tiles + 5]]], dtype=np.int32)
+    got = rkv.rkv_decode_attn_tiles(q, 8, cache, 1.0, torch.from_numpy(lists).cuda(),
+                                    n_split=2).cpu().numpy()
+    assert np.all(got[0, 4:] == 0)
+    Kn, Vn, qn = to_np_f32(K), to_np_f32(V), to_np_f32(q)
+    enc = oracle.encode(Kn[0, 0], Vn[0, 0], cfg.stride_base, 0, cfg.k, 4, cfg.group)
+    kv = oracle.reconstruct(enc, Kn[0, 0], Vn[0, 0], 4)
+    pos = oracle.tile_positions(lists[0, 0], N)
+    want = oracle.decode_attn(qn[0, :4], kv[None, pos, 0], kv[None, pos, 1], 1.0)
+    assert attn_err(got[0, :4], want) <= 2e-3
+
+
 def test_decode_split_invariance():
     _need_gpu()
     cfg = _cfg(1, n_kv_heads=2, n_q_heads=8)
