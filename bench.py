@@ -113,27 +113,97 @@ def cpu_info():
             "affinity": aff}
 
 
-def cpu_baseline(cfg, bits, K_head, V_head, seconds):
-    """Time the oracle's encode on rows sampled uniformly over one (layer,
-    sequence, KV head) of the workload until about `seconds` of CPU work."""
+def _oracle_encode_rows(args):
+    """Worker: time oracle.encode on sampled rows until `seconds` of work."""
+    K_head, V_head, cfg_fields, bits, seconds, seed = args
     import numpy as np
     import oracle
-    rng = np.random.default_rng(0)
-    N = cfg.seq_len
+    try:  # one thread per worker: the cores are counted by processes
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+    base, double_after, k, group, N = cfg_fields
+    rng = np.random.default_rng(seed)
     done, t_used, batch = 0, 0.0, 64
     while t_used < seconds:
         rows = np.sort(rng.integers(0, N, batch))
         t0 = time.perf_counter()
-        oracle.encode(K_head, V_head, cfg.stride_base, cfg.double_after, cfg.k, bits,
-                      cfg.group, rows=rows)
+        oracle.encode(K_head, V_head, base, double_after, k, bits, group, rows=rows)
         t_used += time.perf_counter() - t0
         done += batch
         batch = min(batch * 2, 4096)
-    return {"value": done / t_used, "unit": "head-tokens/s", "cores": 1, "kind": "oracle",
-            "sample": (f"oracle encode of {done} token rows drawn uniformly over one "
-                       f"(layer, sequence, KV head) of {cfg.name} (N={N}), "
-                       f"{t_used:.1f} s on one host core; NumPy fp64/fp32, single-threaded"),
-            "host": cpu_info()}
+    return done, t_used
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return [{"api": d.get("internal_api"), "threads": d.get("num_threads")}
+                for d in threadpool_info()]
+    except Exception:
+        return None
+
+
+def cpu_baseline(cfg, bits, K_head, V_head, seconds, q_head=None):
+    """The oracle on the host cores, on bounded samples of the workload:
+    encode of rows sampled uniformly over one (layer, sequence, KV head) on
+    one core and on every core of the process's affinity (one worker process
+    per core, each on its own sample), and decode of one (sequence, KV head)
+    over a prefix of its positions, reported as the decode stream's
+    algorithmic bytes per second."""
+    import multiprocessing as mp
+
+    import numpy as np
+    import oracle
+    info = cpu_info()
+    fields = (cfg.stride_base, cfg.double_after, cfg.k, cfg.group, cfg.seq_len)
+    ncores = max(1, info["affinity"])
+    blas = blas_threads()
+    ctx = mp.get_context("fork")
+    with ctx.Pool(1) as pool:  # in a child, so the one-thread limit stays there
+        one_done, one_t = pool.map(_oracle_encode_rows,
+                                   [(K_head, V_head, fields, bits, seconds, 0)])[0]
+    t0 = time.perf_counter()
+    with ctx.Pool(ncores) as pool:
+        res = pool.map(_oracle_encode_rows,
+                       [(K_head, V_head, fields, bits, seconds / 2, 1 + i) for i in range(ncores)])
+    wall = time.perf_counter() - t0
+    all_done = sum(r[0] for r in res)
+    out = {"value": all_done / wall, "unit": "head-tokens/s", "cores": ncores, "kind": "oracle",
+           "sample": (f"oracle encode (fp64 NumPy) of token rows drawn uniformly over one "
+                      f"(layer, sequence, KV head) of {cfg.name} (N={cfg.seq_len}): "
+                      f"{ncores} worker processes, {all_done} rows in {wall:.1f} s wall; "
+                      f"throughput extrapolates linearly to the whole workload"),
+           "one_core": {"value": one_done / one_t, "unit": "head-tokens/s", "cores": 1,
+                        "sample": f"{one_done} rows in {one_t:.1f} s on one core"},
+           "host": info, "blas_threads": blas,
+           "note": "every worker limits its BLAS/OpenMP pools to one thread"}
+    if q_head is not None and cfg.decode:
+        # decode of one (sequence, KV head) over its first L positions: the
+        # oracle rebuilds the rows and runs softmax attention for the KV
+        # head's query heads (encoding them is not timed)
+        L = min(cfg.seq_len, 4096)
+        enc = oracle.encode(K_head[:L], V_head[:L], cfg.stride_base, cfg.double_after, cfg.k,
+                            bits, cfg.group)
+        G = cfg.n_q_heads // cfg.n_kv_heads
+        reps, t_dec = 0, 0.0
+        while t_dec < min(5.0, seconds):
+            t1 = time.perf_counter()
+            kv = oracle.reconstruct(enc, K_head[:L], V_head[:L], bits)
+            oracle.decode_attn(q_head[:G], kv[None, :, 0], kv[None, :, 1], 1.0 / math.sqrt(128))
+            t_dec += time.perf_counter() - t1
+            reps += 1
+        nref = enc["T"].shape[0]
+        rec = _record_bytes(cfg, bits)
+        elt = 2 if cfg.dtype == "bf16" else 4
+        nbytes = (L - nref) * rec + nref * 2 * cfg.head_dim * elt
+        out["decode"] = {"value": nbytes * reps / t_dec / 1e9, "unit": "GB/s",
+                         "cores": "BLAS pools as listed",
+                         "sample": (f"oracle reconstruct + attention of one (sequence, KV head), "
+                                    f"its first {L} positions and {G} query heads, {reps} reps in "
+                                    f"{t_dec:.1f} s; bytes = the decode stream of those positions")}
+    return out
 
 
 def main():
@@ -145,7 +215,7 @@ def main():
     ap.add_argument("--bits", type=int, default=None)
     ap.add_argument("--kernel-reps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="also run a plain copy of this many MiB (counter calibration)")
     a = ap.parse_args()
@@ -415,7 +485,8 @@ def main():
     }
     if not a.no_cpu:
         h0 = (K[0, 0].float().cpu().numpy(), V[0, 0].float().cpu().numpy())
-        rec["cpu_baseline"] = cpu_baseline(cfg, bits, h0[0], h0[1], a.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(cfg, bits, h0[0], h0[1], a.cpu_seconds,
+                                           q_head=q[0].float().cpu().numpy())
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec))

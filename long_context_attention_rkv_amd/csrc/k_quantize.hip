@@ -597,6 +597,309 @@ __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
   }
 }
 
+// ------------------------------------------------- quantise, LDS gathers
+// The same computation with the reference rows gathered from LDS instead of
+// the L1/L2 path (bf16 caches whose reference rows of one plane fit in
+// 128 KB, i.e. up to 512 references): one block of 16 waves takes one plane (K or V) of one
+// (instance, head) over a chunk of 32-position tiles and first copies that
+// plane's reference rows (the ones positions below the range end can
+// select) into LDS, so every gather of the chunk is an LDS read.  Each wave
+// owns whole tiles: at step s (0..7) its four 16-lane rows take positions
+// 8 r + s of the tile (r = lane / 16), so after the 8 steps a lane holds,
+// for each of its 8 dims, the codes of 8 consecutive positions -- one word
+// of the transposed V layout -- and writes it directly (no LDS staging, no
+// block barrier after the copy).
+//
+// Arithmetic: the selected rows are summed with v_dot2_f32_bf16 (one
+// element times 1 plus the running fp32 sum: no unpacking), z = fl(x -
+// sum / k_eff); scales and codes are the exact round-half-even of
+// max|z| / qmax and z / scale, as in k_quantize (bf16 data puts many z /
+// scale exactly on a half-integer, so the tie must be decided exactly).
+//
+// Loads: a wave keeps RD steps' rows and slot words in flight (a whole
+// tile, 8 steps, in the common forms; 4 where registers are short): each
+// step's registers are refilled with the step RD later -- of this tile or of
+// the wave's next one -- as soon as the step is done.
+constexpr int kLdsQWaves = 16;             // waves per block
+constexpr int kLdsRefBytes = 128 * 1024;   // reference rows of one plane held in LDS
+constexpr int kLdsChunkTiles = 256;        // tiles per block
+
+// bf16 pair selectors (the low or the high element of a word, times 1),
+// held in registers: as a compile-time operand the compiler encodes the low
+// selector 0x00003F80 as the inline constant 1.0, which v_dot2c_f32_bf16
+// does not read as that pattern (sums measured wrong on the device), so the
+// patterns are moved into VGPRs by hand once per kernel.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+struct Bf16Sel {
+  bf16x2_t lo, hi;
+};
+RKV_INLINE __device__ inline Bf16Sel make_bf16_sel() {
+  uint32_t lo, hi;
+  asm volatile("v_mov_b32 %0, 0x3f80" : "=v"(lo));
+  asm volatile("v_mov_b32 %0, 0x3f800000" : "=v"(hi));
+  return Bf16Sel{__builtin_bit_cast(bf16x2_t, lo), __builtin_bit_cast(bf16x2_t, hi)};
+}
+
+// acc += the 8 elements of a raw row piece (bf16: 16 bytes, fp32: 32 bytes).
+RKV_INLINE __device__ inline void acc_add8(const u32x4 (&r)[1], float (&acc)[8], const Bf16Sel& sl) {
+  const uint32_t wd[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bf16x2_t v = __builtin_bit_cast(bf16x2_t, wd[q]);
+    acc[2 * q] = __builtin_amdgcn_fdot2_f32_bf16(v, sl.lo, acc[2 * q], false);
+    acc[2 * q + 1] = __builtin_amdgcn_fdot2_f32_bf16(v, sl.hi, acc[2 * q + 1], false);
+  }
+}
+RKV_INLINE __device__ inline void acc_add8(const u32x4 (&r)[2], float (&acc)[8], const Bf16Sel&) {
+  float x[8];
+  widen(r, x);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] += x[e];
+}
+
+// LDS row piece of `slot` for this lane (byte offset from ref_piece_off).
+template <typename T>
+RKV_INLINE __device__ inline void lds_piece(const char* base, uint32_t off, u32x4 (&r)[sizeof(T) / 2]) {
+#pragma unroll
+  for (int c = 0; c < (int)(sizeof(T) / 2); ++c)
+    r[c] = *reinterpret_cast<const u32x4*>(base + off + 16u * c);
+}
+
+// This lane's 8 codes of the V plane at step s (position 8 r + s of the
+// tile), packed into the per-dim words (BITS = 2, 4: one word holds the 8
+// positions; BITS = 8: two).
+template <int BITS>
+RKV_INLINE __device__ inline void v_accumulate(const uint32_t (&u)[8], int s, uint32_t (&vw)[8][BITS == 8 ? 2 : 1]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if constexpr (BITS == 8) {
+      vw[e][s >> 2] |= (u[e] & 0xFFu) << (8 * (s & 3));
+    } else {
+      vw[e][0] |= (u[e] & ((1u << BITS) - 1)) << (BITS * s);
+    }
+  }
+}
+
+template <typename T, int BITS, int KM, bool LAT>
+__global__ __launch_bounds__(1024) void k_quantize_lds(
+    const T* __restrict__ K, const T* __restrict__ V, const uint16_t* __restrict__ idx,
+    const T* __restrict__ ref_kv, uint8_t* __restrict__ codes_k, uint8_t* __restrict__ codes_v,
+    uint16_t* __restrict__ scales, int64_t N, int64_t n_refs, Sched sc, int k, int group, int H,
+    int p0, int n_in, int chunk_tiles, LatMask lm) {
+  static_assert(BITS == 2 || BITS == 4 || BITS == 8, "quantised codes only");
+  extern __shared__ u32x4 rl[];  // the plane's reference rows, 128 elements each
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int rr = lane >> 4;        // 16-lane row of the wave: positions 8 rr + s
+  const int dl = lane & 15;        // dims [8 dl, 8 dl + 8)
+  // grid (2 * chunks, H, inst); the chunks and planes of one head run on one
+  // XCD when the heads split evenly over the 8 XCDs
+  int64_t ih = (int64_t)blockIdx.z * H + blockIdx.y;
+  int item = (int)blockIdx.x;
+  if (((gridDim.y * gridDim.z) & 7u) == 0) {
+    const int64_t nc = gridDim.x;
+    const int64_t L = blockIdx.x + nc * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+    const int64_t i = L >> 3;
+    ih = 8 * (i / nc) + (L & 7);
+    item = (int)(i % nc);
+  }
+  const int plane = item & 1;
+  const int p1 = p0 + n_in;
+  const int t_first = (p0 >> 5) + (item >> 1) * chunk_tiles;
+  const int t_last = (p1 + kVTile - 1) >> 5;
+  const int t_end = t_first + chunk_tiles < t_last ? t_first + chunk_tiles : t_last;
+  if (t_first >= t_end) return;  // whole block
+
+  // copy the reference rows positions below p1 can select
+  {
+    const int nr = sched_count(p1, sc);
+    const u32x4* src = reinterpret_cast<const u32x4*>(ref_kv + (ih * 2 + plane) * n_refs * 128);
+    const int n16 = nr * (int)(128 * sizeof(T) / 16);
+    for (int i = tid; i < n16; i += 1024) rl[i] = src[i];
+  }
+  __syncthreads();
+
+  const char* lb = reinterpret_cast<const char*>(rl);
+  const Bf16Sel bsel = make_bf16_sel();
+  const uint32_t lane16 = 16u * dl;
+  const int n_groups = 128 / group;
+  const int lanes_per_group = group >> 3;
+  const bool scale_lane = (dl & (lanes_per_group - 1)) == 0;
+  const int sgrp = dl / lanes_per_group;
+  const T* xin = (plane ? V : K) + ih * n_in * 128 + 8 * dl;  // + (position - p0) * 128
+  const uint16_t* ib = idx + ih * N * k;
+  // K codes and scales of this head through bounded buffer descriptors: a
+  // store that must not happen gets an offset past the range and is dropped
+  // by the hardware, so no store sits behind a branch (a branch around a
+  // store would make the compiler wait for every load in flight before it)
+  // (bases at the chunk's first position: offsets stay 32-bit)
+  const int64_t cpos0 = (int64_t)t_first * kVTile;
+  const int64_t cpos1 = (int64_t)t_end * kVTile < N ? (int64_t)t_end * kVTile : N;
+  const uint32_t ck_bytes = (uint32_t)(cpos1 - cpos0) * (16u * BITS);
+  const __amdgpu_buffer_rsrc_t kb = __builtin_amdgcn_make_buffer_rsrc(
+      codes_k + (ih * N + cpos0) * (16 * BITS), 0, (int)ck_bytes, 0x00020000);
+  const uint32_t sc_bytes = (uint32_t)(cpos1 - cpos0) * 4u * n_groups;
+  const __amdgpu_buffer_rsrc_t sb = __builtin_amdgcn_make_buffer_rsrc(
+      scales + (ih * N + cpos0) * 2 * n_groups, 0, (int)sc_bytes, 0x00020000);
+  const uint32_t k_lane = (uint32_t)dl * BITS;
+  const uint32_t s_lane = 2u * (uint32_t)(plane * n_groups + sgrp);
+  constexpr uint32_t kDrop = 0x80000000u;  // past every range: the store is dropped
+  constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
+  constexpr float inv_qmax = 1.0f / qmax;
+  constexpr float tol = (qmax + 1.f) * 0x1p-21f;
+
+  // residual of this lane's 8 dims at position `pos` -> scale and codes (u);
+  // stores the scale and (K plane) the codes when `mine`
+  auto finish = [&](int pos, bool mine, float (&z)[8], uint32_t (&u)[8]) RKV_INLINE {
+    if constexpr (LAT) {
+      lat_signs8(z, lm, dl);
+      fwht128_8(z, dl);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[e] *= 0.0625f;
+    }
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(z[e]));
+    a = group_max_nonneg(a, lanes_per_group);
+    bool plain;
+    const uint16_t sbits = exact_scale_bits_plain(a, qmax, inv_qmax, plain);
+    const float sv = half_bits_to_f32(sbits);
+    const float rs = sv > 0.f ? __builtin_amdgcn_rcpf(sv) : 0.f;  // within 1 ulp of 1/s
+    // a scale that is not plain (rare) has every code decided exactly and clamped
+    codes8<false>(z, sv, rs, qmax, tol, u, !plain);
+    const uint32_t rp = (uint32_t)(pos - cpos0);
+    const uint32_t soff = (mine && scale_lane) ? rp * (4u * n_groups) + s_lane : kDrop;
+    __builtin_amdgcn_raw_buffer_store_b16(sbits, sb, (int)soff, 0, 0);
+    if (plane == 0) {
+      const uint32_t koff = mine ? rp * (16u * BITS) + k_lane : kDrop;
+      buffer_store_word<BITS>(kb, koff, pack8<BITS>(u));
+    }
+  };
+
+  // row piece and slot word of step s of the tile at tb (positions clamped
+  // into [lo, hi))
+  auto issue = [&](int tbx, int lo, int hi, int s, PosLoads<T, KM>& pl) RKV_INLINE {
+    const int pos = min(max(tbx + 8 * rr + s, lo), hi - 1);
+#pragma unroll
+    for (int c = 0; c < (int)(sizeof(T) / 2); ++c)
+      pl.x[c] = *reinterpret_cast<const u32x4*>(xin + (int64_t)(pos - p0) * 128 + (16 / sizeof(T)) * c);
+    pl.sl[0].x = *reinterpret_cast<const uint32_t*>(ib + (int64_t)pos * KM + 2 * (dl & (KM / 2 - 1)));
+  };
+  // steps in flight per wave: a whole tile where the registers allow
+  constexpr int RD = (KM <= 8 && BITS <= 4 && !LAT && sizeof(T) == 2) ? 8 : 4;
+  PosLoads<T, KM> ring[RD];
+  bool ring_ok = false;  // the ring holds the current tile's first RD steps
+  for (int t = t_first + w; t < t_end; t += kLdsQWaves) {
+    const int tb = t * kVTile;
+    const int v0 = tb > p0 ? tb : p0;
+    const int v1 = tb + kVTile < p1 ? tb + kVTile : p1;
+    const bool fast = k == KM && sched_count_le(tb, sc) >= KM;
+    uint32_t vw[8][BITS == 8 ? 2 : 1];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int c = 0; c < (BITS == 8 ? 2 : 1); ++c) vw[e][c] = 0u;
+    if (fast) {
+      // every position has KM candidates: unconditional loads (positions
+      // outside the range reread one inside it and store nothing)
+      auto step = [&](int s, PosLoads<T, KM>& cur) RKV_INLINE {
+        const int pos = tb + 8 * rr + s;
+        const bool mine = pos >= v0 && pos < v1;
+        spread_slot_words<T, KM>(cur);
+        u32x4 g[KM][sizeof(T) / 2];
+#pragma unroll
+        for (int j = 0; j < KM; ++j) lds_piece<T>(lb, ref_piece_off<T>(slot_word(cur, j), j & 1, lane16), g[j]);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KM; ++j) acc_add8(g[j], acc, bsel);
+        float x[8], z[8];
+        widen(cur.x, x);
+        constexpr float inv = 1.0f / KM;  // KM is 4, 8 or 16: exact
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = __builtin_fmaf(acc[e], -inv, x[e]);
+        uint32_t u[8];
+        finish(pos, mine, z, u);
+        if (plane == 1) v_accumulate<BITS>(u, s, vw);
+      };
+      if (!ring_ok) {
+#pragma unroll
+        for (int s = 0; s < RD; ++s) issue(tb, v0, v1, s, ring[s]);
+      }
+      // step s + RD is requested as soon as step s is done: later steps of
+      // this tile, then the first steps of the wave's next tile if that one
+      // is a fast tile too
+      const int tn = t + kLdsQWaves;
+      const bool next = tn < t_end && k == KM && sched_count_le(tn * kVTile, sc) >= KM;
+      const int nb = tn * kVTile;
+      const int nv0 = nb > p0 ? nb : p0;
+      const int nv1 = nb + kVTile < p1 ? nb + kVTile : p1;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        step(s, ring[s % RD]);
+        if (s + RD < 8) issue(tb, v0, v1, s + RD, ring[s % RD]);
+        else if (next) issue(nb, nv0, nv1, s + RD - 8, ring[s % RD]);
+      }
+      ring_ok = next;
+    } else {
+      // first tiles of a sequence (fewer than k candidates) or k < KM
+#pragma unroll 1
+      for (int s = 0; s < 8; ++s) {
+        const int pos = tb + 8 * rr + s;
+        const bool mine = pos >= v0 && pos < v1;
+        uint32_t u[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        if (mine) {
+          u32x4 xr[sizeof(T) / 2];
+#pragma unroll
+          for (int c = 0; c < (int)(sizeof(T) / 2); ++c)
+            xr[c] = *reinterpret_cast<const u32x4*>(xin + (int64_t)(pos - p0) * 128 + (16 / sizeof(T)) * c);
+          const int cnt = sched_count_le(pos, sc);
+          const int keff = cnt < k ? cnt : k;
+          const uint16_t* irow = ib + (int64_t)pos * k;
+          float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          for (int j = 0; j < keff; ++j) {
+            const uint32_t slot = irow[j];
+            u32x4 g[sizeof(T) / 2];
+            lds_piece<T>(lb, (slot * 128u + 8u * dl) * (uint32_t)sizeof(T), g);
+            acc_add8(g, acc, bsel);
+          }
+          float x[8], z[8];
+          widen(xr, x);
+          if (is_pow2(keff)) {
+            const float inv = __uint_as_float((uint32_t)(127 - __builtin_ctz(keff)) << 23);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[e] = x[e] - acc[e] * inv;
+          } else {
+            const float kf = (float)keff;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[e] = x[e] - acc[e] / kf;
+          }
+          finish(pos, true, z, u);
+        }
+        if (plane == 1) v_accumulate<BITS>(u, s, vw);
+      }
+      ring_ok = false;
+    }
+    if (plane == 1) {
+      // the words of positions 8 rr .. 8 rr + 7 of the tile, for the lane's 8
+      // dims; a tile cut by the range keeps the other positions' bits
+      const int g0 = tb + 8 * rr;
+      const int lo = v0 - g0 < 0 ? 0 : v0 - g0;
+      const int hi = v1 - g0 > 8 ? 8 : v1 - g0;
+      uint8_t* dst = codes_v + ((ih * ((N + kVTile - 1) / kVTile) + t) * 128 + 8 * dl) *
+                                   (kVTile * BITS / 8) + rr * BITS;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint64_t wv = BITS == 8 ? ((uint64_t)vw[e][BITS == 8 ? 1 : 0] << 32 | vw[e][0])
+                                      : (uint64_t)vw[e][0];
+        uint8_t* d = dst + e * (kVTile * BITS / 8);
+        if (lo == 0 && hi == 8) store_word<BITS>(d, wv);
+        else if (lo < hi) store_word_range<BITS>(d, wv, lo, hi);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------ reconstruct
 template <int BITS>
 __device__ inline int code_at(const uint8_t* row, int t) {
@@ -696,8 +999,33 @@ hipError_t launch_quantize_t(const void* K, const void* V, const uint16_t* idx,
   auto pick_r = [&](auto lat) {
     return ref_bits == 4 ? pick(std::true_type{}, lat) : pick(std::false_type{}, lat);
   };
-  auto kern = lm ? pick_r(std::true_type{}) : pick_r(std::false_type{});
   const LatMask m = lm ? *lm : LatMask{{0u, 0u, 0u, 0u}};
+  // Reference rows of one plane that fit in LDS: gathers from LDS
+  const size_t ref_lds = (size_t)sched_count((int32_t)(p0 + n_in), sc) * 128 * sizeof(T);
+  if constexpr (BITS != 0 && sizeof(T) == 2) {
+    if (ref_bits == 0 && ref_lds <= (size_t)kLdsRefBytes) {
+      const int64_t ntiles = (p0 + n_in + kVTile - 1) / kVTile - p0 / kVTile;
+      const int64_t nch = (ntiles + kLdsChunkTiles - 1) / kLdsChunkTiles;
+      auto pick_l = [&](auto lat) {
+        constexpr bool L = decltype(lat)::value;
+        return k <= 4 ? k_quantize_lds<T, BITS, 4, L>
+                      : (k <= 8 ? k_quantize_lds<T, BITS, 8, L> : k_quantize_lds<T, BITS, 16, L>);
+      };
+      auto kl = lm ? pick_l(std::true_type{}) : pick_l(std::false_type{});
+      if (ref_lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute((const void*)kl,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)ref_lds);
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL(kl, dim3((unsigned)(2 * nch), H, (unsigned)n_inst), dim3(1024),
+                         ref_lds, st, (const T*)K, (const T*)V, idx, (const T*)ref_kv, ck, cv,
+                         sc16, N, n_refs, sc, k, group, H, (int)p0, (int)n_in,
+                         (int)kLdsChunkTiles, m);
+      return hipGetLastError();
+    }
+  }
+  auto kern = lm ? pick_r(std::true_type{}) : pick_r(std::false_type{});
   hipLaunchKernelGGL(kern, dim3((unsigned)nchunks, H, (unsigned)n_inst),
                      dim3(512), 0, st, (const T*)K, (const T*)V, idx, (const T*)ref_kv, ref_scales, ck,
                      cv, sc16, N, n_refs, sc, k, group, chunk, H, (int)p0, (int)n_in, m);

@@ -18,7 +18,8 @@ add still fit):
     S the sum of |row| over the selected rows;
   * z32 = fl(x - KV_R32): a further u (|x| + S);
 so |z32 - z| <= 4u (S + |x|) = 2^-22 (S + |x|); the bound used, 2^-21 (S + |x|),
-doubles it.  In latent mode z = H D (x - KV_R) / 16 is formed by seven fp32
+doubles it.  Scales and codes are then the exact roundings of the GPU's own
+z32 (ties to even decided exactly).  In latent mode z = H D (x - KV_R) / 16 is formed by seven fp32
 butterfly stages on z32; each output is a signed sum of all 128 inputs, so
 the bound is (sum_t e_t + 14u sum_t (|z_t| + e_t)) / 16 for every element.
 """
