@@ -319,7 +319,7 @@ def main():
     stream_append = {"us_per_call": ap_mean * 1e6, "head_tokens_per_call": n_inst * H,
                      "head_tokens_per_s": n_inst * H / ap_mean,
                      "note": "rkv_append of one position for all layers x sequences x KV heads "
-                             "(distance/top-k against the 512 references + quantise)"}
+                             f"(distance/top-k against the {n_refs} references + quantise)"}
 
     # full-pipeline quantisation: the same layer with the reference store in
     # int4 (storage per head-token, and the layer's encode + decode)
@@ -428,16 +428,23 @@ def main():
     }
     # dominant kernel of the step by time; `traffic` = measured HBM bytes per
     # launch (profiles/), null unless taken on the current kernel sources
+    # the quantiser gathers reference rows from LDS when one plane's rows fit
+    # in 128 KB (bf16, up to 512 references), else through the L1/L2
+    qz_kernel = "k_quantize_lds" if cfg.dtype == "bf16" and n_refs * 256 <= 128 * 1024 \
+        and N >= 4 * n_refs else "k_quantize"
+    # profiles/ summaries are named per workload, and per code width where the
+    # workload is run at several
+    wl_tag = cfg.name if len(cfg.bits) == 1 else f"{cfg.name}_int{bits}"
     if qz_mean >= sel_mean:
-        roof = {"bound": "hbm", "kernel": "k_quantize", "achieved": qz_gbps,
+        roof = {"bound": "hbm", "kernel": qz_kernel, "achieved": qz_gbps,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": qz_gbps / HBM_PEAK_GBPS,
-                "traffic": measured_traffic("k_quantize", cfg.name),
+                "traffic": measured_traffic(qz_kernel, wl_tag),
                 "algorithmic_bytes": alg["quantize_bytes"]}
     else:
         roof = {"bound": "mfma", "kernel": "k_dist_topk", "achieved": sel_tflops,
                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": sel_tflops / BF16_MFMA_PEAK_TFLOPS,
-                "traffic": measured_traffic("k_dist_topk", cfg.name),
+                "traffic": measured_traffic("k_dist_topk", wl_tag),
                 "algorithmic_flops": alg["select_flops"],
                 "note": "timed as rkv_select_refs = k_refstore (about 1 % of it) + k_dist_topk"}
 

@@ -1000,10 +1000,14 @@ hipError_t launch_quantize_t(const void* K, const void* V, const uint16_t* idx,
     return ref_bits == 4 ? pick(std::true_type{}, lat) : pick(std::false_type{}, lat);
   };
   const LatMask m = lm ? *lm : LatMask{{0u, 0u, 0u, 0u}};
-  // Reference rows of one plane that fit in LDS: gathers from LDS
-  const size_t ref_lds = (size_t)sched_count((int32_t)(p0 + n_in), sc) * 128 * sizeof(T);
+  // Reference rows of one plane that fit in LDS: gathers from LDS, when the
+  // range is long enough to repay copying the rows into every block (at
+  // least four positions per reference; a streaming append of a few
+  // positions gathers through the L1/L2 instead)
+  const int64_t nr_range = sched_count((int32_t)(p0 + n_in), sc);
+  const size_t ref_lds = (size_t)nr_range * 128 * sizeof(T);
   if constexpr (BITS != 0 && sizeof(T) == 2) {
-    if (ref_bits == 0 && ref_lds <= (size_t)kLdsRefBytes) {
+    if (ref_bits == 0 && ref_lds <= (size_t)kLdsRefBytes && n_in >= 4 * nr_range) {
       const int64_t ntiles = (p0 + n_in + kVTile - 1) / kVTile - p0 / kVTile;
       const int64_t nch = (ntiles + kLdsChunkTiles - 1) / kLdsChunkTiles;
       auto pick_l = [&](auto lat) {

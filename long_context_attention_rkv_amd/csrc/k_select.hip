@@ -118,24 +118,48 @@ __device__ inline float topk_get(const float (&top)[KM], int k) {
 // Row of accumulator register r of a 32x32 MFMA tile for lane half `half`.
 __device__ inline int acc_row(int r, int half) { return (r & 3) + 8 * (r >> 2) + 4 * half; }
 
-// Survivor lists: per (lane, token set) entries of two words, the distance
-// (fp32 bits) and the slot, laid out [entry][word][64 lanes] so that one
-// entry is a single two-address LDS store.  Capacity: the lane's k best, 3
-// more (a lane holds about k/2 + 1 survivors on average, rarely more than
-// k + 3, so a list seldom needs cutting), plus the kCheckRows accumulator
-// rows appended between two fullness checks.
+// Survivor lists: per (lane, token set) entries of a distance (fp32 bits)
+// and a slot.  For k <= 8 an entry is two words, laid out [entry][word][64
+// lanes] so that one entry is a single two-address LDS store; capacity: the
+// lane's k best, 3 more (a lane holds about k/2 + 1 survivors on average,
+// rarely more than k + 3, so a list seldom needs cutting), plus the
+// kCheckRows accumulator rows appended between two fullness checks.  For
+// k > 8 the distances ([entry][64 lanes] words) and the slots ([entry][64
+// lanes] halves) are separate arrays and the capacity has no slack (k +
+// kCheckRows): 6 bytes per entry, so that two blocks fit in LDS.
 constexpr int kCheckRows = 4;
 template <int KM>
-constexpr int surv_cap() { return KM + 3 + kCheckRows; }
-constexpr int kEntryWords = 128;  // stride of one list entry, in 32-bit words
+constexpr bool split_lists() { return KM > 8; }
+template <int KM>
+constexpr int surv_cap() { return split_lists<KM>() ? KM + kCheckRows : KM + 3 + kCheckRows; }
+constexpr int kEntryWords = 128;  // stride of one two-word entry, in 32-bit words
+
+// One lane's list: d = its distance of entry 0, s (split layout) its slot of
+// entry 0.
+template <bool SPLIT>
+struct LaneList {
+  uint32_t* d;
+  uint16_t* s;
+  static constexpr int kD = SPLIT ? 64 : kEntryWords;  // distance stride, in words
+  __device__ uint32_t dist(int c) const { return d[c * kD]; }
+  __device__ uint32_t slot(int c) const {
+    if constexpr (SPLIT) return s[c * 64];
+    else return d[c * kEntryWords + 64];
+  }
+  __device__ void put(int c, uint32_t dv, uint32_t sv) const {
+    d[c * kD] = dv;
+    if constexpr (SPLIT) s[c * 64] = (uint16_t)sv;
+    else d[c * kEntryWords + 64] = sv;
+  }
+};
 
 // Loads a lane's survivor list into registers; entries past cnt read as +inf.
-template <int CAP>
-__device__ inline void load_list(const uint32_t* bl, int cnt, float (&e)[CAP], float (&js)[CAP]) {
+template <int CAP, bool SPLIT>
+__device__ inline void load_list(const LaneList<SPLIT>& bl, int cnt, float (&e)[CAP], float (&js)[CAP]) {
 #pragma unroll
   for (int c = 0; c < CAP; ++c) {
-    const float v = __uint_as_float(bl[c * kEntryWords]);
-    const uint32_t j = bl[c * kEntryWords + 64];
+    const float v = __uint_as_float(bl.dist(c));
+    const uint32_t j = bl.slot(c);
     e[c] = c < cnt ? v : INFINITY;
     js[c] = (float)j;
   }
@@ -145,8 +169,8 @@ __device__ inline void load_list(const uint32_t* bl, int cnt, float (&e)[CAP], f
 // equal to the k-th value the earlier (lower) slots stay.  Lowers tau to the
 // k-th value: an entry dropped here is beaten by k kept ones, and every later
 // entry has a higher slot.
-template <int KM, int CAP>
-__device__ __forceinline__ void lane_compact(uint32_t* bl, int& cnt, float& tau, int k) {
+template <int KM, int CAP, bool SPLIT>
+__device__ __forceinline__ void lane_compact(const LaneList<SPLIT>& bl, int& cnt, float& tau, int k) {
   if (cnt <= k) return;
   float e[CAP], js[CAP];
   load_list<CAP>(bl, cnt, e, js);
@@ -167,8 +191,7 @@ __device__ __forceinline__ void lane_compact(uint32_t* bl, int& cnt, float& tau,
     const bool take = e[c] < t || (tie && ties < quota);
     ties += tie;
     if (take) {
-      bl[out * kEntryWords] = __float_as_uint(e[c]);
-      bl[out * kEntryWords + 64] = (uint32_t)js[c];
+      bl.put(out, __float_as_uint(e[c]), (uint32_t)js[c]);
       ++out;
     }
   }
@@ -179,9 +202,10 @@ __device__ __forceinline__ void lane_compact(uint32_t* bl, int& cnt, float& tau,
 // The keff nearest references of one token from its two survivor lists
 // (la: cnt_a entries, lb: cnt_b entries), lowest slot first among equal
 // distances; returns them in ascending slot order, 65535 past keff.
-template <int KM, int CAP>
-__device__ __forceinline__ void token_select(const uint32_t* la, int cnt_a, const uint32_t* lb,
-                                             int cnt_b, int keff, float (&sel)[KM]) {
+template <int KM, int CAP, bool SPLIT>
+__device__ __forceinline__ void token_select(const LaneList<SPLIT>& la, int cnt_a,
+                                             const LaneList<SPLIT>& lb, int cnt_b, int keff,
+                                             float (&sel)[KM]) {
   float ea[CAP], ja[CAP], eb[CAP], jb[CAP];
   load_list<CAP>(la, cnt_a, ea, ja);
   load_list<CAP>(lb, cnt_b, eb, jb);
@@ -285,16 +309,21 @@ constexpr int kRowPad = 136;  // bf16 per staged key row: 128 + 8 (bank spread)
 constexpr int kSets = 2;      // 32-token sets per wave
 constexpr int kBlockRows = 4 * 32 * kSets;
 
-// Two blocks per CU while the survivor lists fit (k <= 8), else one.
+// Two blocks per CU (79 KB of LDS each).
 template <typename T, int KM>
-__global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
+__global__ __launch_bounds__(256, 2) void k_dist_topk(
     const T* __restrict__ K, const __bf16* __restrict__ refkey,
     const float* __restrict__ refnorm, uint16_t* __restrict__ idx_out, int64_t N,
     int64_t n_refs, Sched sc, int k, int H, int n_blocks, int64_t p0, int64_t n_in) {
   // positions [p0, p1) from input rows [ih][n_in][128]; idx rows at ih * N + position
   const int64_t p1 = p0 + n_in;
   constexpr int CAP = surv_cap<KM>();
-  __shared__ uint32_t sbl[4][kSets][CAP][2][64];
+  constexpr bool SPLIT = split_lists<KM>();
+  __shared__ uint32_t sbd[4][kSets][CAP][SPLIT ? 64 : kEntryWords];
+  __shared__ uint16_t sbs[SPLIT ? 4 : 1][kSets][SPLIT ? CAP : 1][64];
+  auto list_of = [&](int w_, int c_, int l_) RKV_INLINE {
+    return LaneList<SPLIT>{&sbd[w_][c_][0][l_], &sbs[SPLIT ? w_ : 0][c_][0][l_]};
+  };
   __shared__ __attribute__((aligned(16))) __bf16 kbuf[2][32][kRowPad];
   __shared__ __attribute__((aligned(16))) float nbuf[2][32];
   const int tid = threadIdx.x;
@@ -467,44 +496,45 @@ __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
   }
 
   // ---- pass 2: collect candidates <= tau
-  // ends[c]: word offset of the end of list c (count * kEntryWords); a
-  // survivor moves it by one entry (compare, select, add per candidate)
-  uint32_t ends[kSets];
+  // ends[c]: the end of list c; a survivor moves it by one entry (compare,
+  // select, add per candidate)
+  LaneList<SPLIT> ends[kSets];
 #pragma unroll
-  for (int c = 0; c < kSets; ++c) ends[c] = 0;
+  for (int c = 0; c < kSets; ++c) ends[c] = list_of(w, c, lane);
   stream([&](int rt, const f32x16 (&acc)[kSets]) RKV_INLINE {
     const uint32_t r0 = (uint32_t)rt * 32 + 4 * half;
 #pragma unroll
     for (int h = 0; h < 16 / kCheckRows; ++h) {
 #pragma unroll
       for (int c = 0; c < kSets; ++c) {
-        uint32_t* bl = &sbl[w][c][0][0][lane];
 #pragma unroll
         for (int r = kCheckRows * h; r < kCheckRows * h + kCheckRows; ++r) {
           // at most CAP - 1 entries here: at most kCheckRows - 1 appends
           // since the last check left at most CAP - kCheckRows
-          uint32_t* at = bl + ends[c];
-          at[0] = __float_as_uint(acc[c][r]);
-          at[64] = r0 + (uint32_t)acc_row(r, 0);
-          ends[c] += acc[c][r] <= tau[c] ? (uint32_t)kEntryWords : 0u;
+          ends[c].put(0, __float_as_uint(acc[c][r]), r0 + (uint32_t)acc_row(r, 0));
+          const int inc = acc[c][r] <= tau[c] ? 1 : 0;
+          ends[c].d += inc * LaneList<SPLIT>::kD;
+          if constexpr (SPLIT) ends[c].s += inc * 64;
         }
       }
       bool full = false;
 #pragma unroll
-      for (int c = 0; c < kSets; ++c) full |= ends[c] > (uint32_t)((CAP - kCheckRows) * kEntryWords);
+      for (int c = 0; c < kSets; ++c) full |= ends[c].d > &sbd[w][c][CAP - kCheckRows][lane];
       if (__any(full)) {
 #pragma unroll
         for (int c = 0; c < kSets; ++c) {
-          int cnt = (int)(ends[c] / kEntryWords);
-          lane_compact<KM, CAP>(&sbl[w][c][0][0][lane], cnt, tau[c], k);
-          ends[c] = (uint32_t)cnt * kEntryWords;
+          const LaneList<SPLIT> bl = list_of(w, c, lane);
+          int cnt = (int)(ends[c].d - bl.d) / LaneList<SPLIT>::kD;
+          lane_compact<KM, CAP>(bl, cnt, tau[c], k);
+          ends[c].d = bl.d + cnt * LaneList<SPLIT>::kD;
+          if constexpr (SPLIT) ends[c].s = bl.s + cnt * 64;
         }
       }
     }
   });
   int cnt[kSets];
 #pragma unroll
-  for (int c = 0; c < kSets; ++c) cnt[c] = (int)(ends[c] / kEntryWords);
+  for (int c = 0; c < kSets; ++c) cnt[c] = (int)(ends[c].d - &sbd[w][c][0][lane]) / LaneList<SPLIT>::kD;
   if (!active) return;
 
   // ---- final: one token per lane (set `half`, column n) from the lists of
@@ -515,7 +545,7 @@ __global__ __launch_bounds__(256, KM <= 8 ? 2 : 1) void k_dist_topk(
     const int last = c ? my_last[1] : my_last[0];
     const int keff = (last + 1 < k) ? last + 1 : k;
     float sel[KM];
-    token_select<KM, CAP>(&sbl[w][c][0][0][n], (int)cp.a, &sbl[w][c][0][0][n + 32], (int)cp.b,
+    token_select<KM, CAP>(list_of(w, c, n), (int)cp.a, list_of(w, c, n + 32), (int)cp.b,
                           keff < 1 ? 1 : keff, sel);
     if (c ? valid_row[1] : valid_row[0]) {
       uint16_t* orow = idx_out + (ih * N + row0 + 32 * c + n) * k;
