@@ -687,7 +687,10 @@ __global__ __launch_bounds__(1024) void k_quantize_lds(
     uint16_t* __restrict__ scales, int64_t N, int64_t n_refs, Sched sc, int k, int group, int H,
     int p0, int n_in, int chunk_tiles, LatMask lm) {
   static_assert(BITS == 2 || BITS == 4 || BITS == 8, "quantised codes only");
-  extern __shared__ u32x4 rl[];  // the plane's reference rows, 128 elements each
+  static_assert(sizeof(T) == 2, "bf16 rows: 256 bytes each");
+  // the plane's reference rows, 128 elements each (a static array: its LDS
+  // address is known when the kernel is compiled, so gathers need no base add)
+  __shared__ u32x4 rl[kLdsRefBytes / 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -777,14 +780,23 @@ __global__ __launch_bounds__(1024) void k_quantize_lds(
     }
   };
 
-  // row piece and slot word of step s of the tile at tb (positions clamped
-  // into [lo, hi))
-  auto issue = [&](int tbx, int lo, int hi, int s, PosLoads<T, KM>& pl) RKV_INLINE {
-    const int pos = min(max(tbx + 8 * rr + s, lo), hi - 1);
-#pragma unroll
-    for (int c = 0; c < (int)(sizeof(T) / 2); ++c)
-      pl.x[c] = *reinterpret_cast<const u32x4*>(xin + (int64_t)(pos - p0) * 128 + (16 / sizeof(T)) * c);
-    pl.sl[0].x = *reinterpret_cast<const uint32_t*>(ib + (int64_t)pos * KM + 2 * (dl & (KM / 2 - 1)));
+  // Row piece and slot word of step s of the tile at tbx, through bounded
+  // buffer descriptors over the range's rows and slot rows: a position
+  // outside [p0, p1) reads zeros or a row of the range (its results are
+  // never stored), so no clamp is needed, and the step's offset is an
+  // instruction immediate.
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>((plane ? V : K) + ih * n_in * 128), 0, n_in * 256, 0x00020000);
+  const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(ib + (int64_t)p0 * KM), 0, n_in * KM * 2, 0x00020000);
+  const uint32_t x_lane = 16u * dl;
+  const uint32_t i_lane = 4u * (dl & (KM / 2 - 1));
+  auto issue = [&](int tbx, int s, PosLoads<T, KM>& pl) RKV_INLINE {
+    const uint32_t r0 = (uint32_t)(tbx + 8 * rr - p0);
+    pl.x[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            xrs, (int)(r0 * 256u + x_lane + 256u * s), 0, 0));
+    pl.sl[0].x = __builtin_amdgcn_raw_buffer_load_b32(
+        irs, (int)(r0 * (2u * KM) + i_lane + 2u * KM * s), 0, 0);
   };
   // steps in flight per wave: a whole tile where the registers allow
   constexpr int RD = (KM <= 8 && BITS <= 4 && !LAT && sizeof(T) == 2) ? 8 : 4;
@@ -810,9 +822,11 @@ __global__ __launch_bounds__(1024) void k_quantize_lds(
         u32x4 g[KM][sizeof(T) / 2];
 #pragma unroll
         for (int j = 0; j < KM; ++j) lds_piece<T>(lb, ref_piece_off<T>(slot_word(cur, j), j & 1, lane16), g[j]);
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        // the sum starts at the first row itself (exact), then adds the others
+        float acc[8];
+        widen(g[0], acc);
 #pragma unroll
-        for (int j = 0; j < KM; ++j) acc_add8(g[j], acc, bsel);
+        for (int j = 1; j < KM; ++j) acc_add8(g[j], acc, bsel);
         float x[8], z[8];
         widen(cur.x, x);
         constexpr float inv = 1.0f / KM;  // KM is 4, 8 or 16: exact
@@ -824,7 +838,7 @@ __global__ __launch_bounds__(1024) void k_quantize_lds(
       };
       if (!ring_ok) {
 #pragma unroll
-        for (int s = 0; s < RD; ++s) issue(tb, v0, v1, s, ring[s]);
+        for (int s = 0; s < RD; ++s) issue(tb, s, ring[s]);
       }
       // step s + RD is requested as soon as step s is done: later steps of
       // this tile, then the first steps of the wave's next tile if that one
@@ -832,13 +846,11 @@ __global__ __launch_bounds__(1024) void k_quantize_lds(
       const int tn = t + kLdsQWaves;
       const bool next = tn < t_end && k == KM && sched_count_le(tn * kVTile, sc) >= KM;
       const int nb = tn * kVTile;
-      const int nv0 = nb > p0 ? nb : p0;
-      const int nv1 = nb + kVTile < p1 ? nb + kVTile : p1;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         step(s, ring[s % RD]);
-        if (s + RD < 8) issue(tb, v0, v1, s + RD, ring[s % RD]);
-        else if (next) issue(nb, nv0, nv1, s + RD - 8, ring[s % RD]);
+        if (s + RD < 8) issue(tb, s + RD, ring[s % RD]);
+        else if (next) issue(nb, s + RD - 8, ring[s % RD]);
       }
       ring_ok = next;
     } else {
@@ -1007,7 +1019,8 @@ hipError_t launch_quantize_t(const void* K, const void* V, const uint16_t* idx,
   const int64_t nr_range = sched_count((int32_t)(p0 + n_in), sc);
   const size_t ref_lds = (size_t)nr_range * 128 * sizeof(T);
   if constexpr (BITS != 0 && sizeof(T) == 2) {
-    if (ref_bits == 0 && ref_lds <= (size_t)kLdsRefBytes && n_in >= 4 * nr_range) {
+    if (ref_bits == 0 && ref_lds <= (size_t)kLdsRefBytes && n_in >= 4 * nr_range &&
+        n_in < (int64_t{1} << 23)) {  // byte offsets of the range's rows fit 31 bits
       const int64_t ntiles = (p0 + n_in + kVTile - 1) / kVTile - p0 / kVTile;
       const int64_t nch = (ntiles + kLdsChunkTiles - 1) / kLdsChunkTiles;
       auto pick_l = [&](auto lat) {
@@ -1016,14 +1029,8 @@ hipError_t launch_quantize_t(const void* K, const void* V, const uint16_t* idx,
                       : (k <= 8 ? k_quantize_lds<T, BITS, 8, L> : k_quantize_lds<T, BITS, 16, L>);
       };
       auto kl = lm ? pick_l(std::true_type{}) : pick_l(std::false_type{});
-      if (ref_lds > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute((const void*)kl,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)ref_lds);
-        if (e != hipSuccess) return e;
-      }
       hipLaunchKernelGGL(kl, dim3((unsigned)(2 * nch), H, (unsigned)n_inst), dim3(1024),
-                         ref_lds, st, (const T*)K, (const T*)V, idx, (const T*)ref_kv, ck, cv,
+                         0, st, (const T*)K, (const T*)V, idx, (const T*)ref_kv, ck, cv,
                          sc16, N, n_refs, sc, k, group, H, (int)p0, (int)n_in,
                          (int)kLdsChunkTiles, m);
       return hipGetLastError();
