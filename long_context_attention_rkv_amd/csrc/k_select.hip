@@ -309,9 +309,12 @@ constexpr int kRowPad = 136;  // bf16 per staged key row: 128 + 8 (bank spread)
 constexpr int kSets = 2;      // 32-token sets per wave
 constexpr int kBlockRows = 4 * 32 * kSets;
 
-// Two blocks per CU (79 KB of LDS each).
-template <typename T, int KM>
-__global__ __launch_bounds__(256, 2) void k_dist_topk(
+// Two blocks per CU (79 KB of LDS each).  DIRECT: the form for short ranges
+// (a streaming append): one wave per block, no staging, no barriers -- each
+// wave loads its A operands and norms straight from L2, one tile ahead, and
+// runs the same MFMA chain (so its indices equal the staged form's).
+template <typename T, int KM, bool DIRECT>
+__global__ __launch_bounds__(DIRECT ? 64 : 256, 2) void k_dist_topk(
     const T* __restrict__ K, const __bf16* __restrict__ refkey,
     const float* __restrict__ refnorm, uint16_t* __restrict__ idx_out, int64_t N,
     int64_t n_refs, Sched sc, int k, int H, int n_blocks, int64_t p0, int64_t n_in) {
@@ -319,13 +322,15 @@ __global__ __launch_bounds__(256, 2) void k_dist_topk(
   const int64_t p1 = p0 + n_in;
   constexpr int CAP = surv_cap<KM>();
   constexpr bool SPLIT = split_lists<KM>();
-  __shared__ uint32_t sbd[4][kSets][CAP][SPLIT ? 64 : kEntryWords];
-  __shared__ uint16_t sbs[SPLIT ? 4 : 1][kSets][SPLIT ? CAP : 1][64];
+  constexpr int NWV = DIRECT ? 1 : 4;           // waves per block
+  constexpr int BROWS = NWV * 32 * kSets;       // tokens per block
+  __shared__ uint32_t sbd[NWV][kSets][CAP][SPLIT ? 64 : kEntryWords];
+  __shared__ uint16_t sbs[SPLIT ? NWV : 1][kSets][SPLIT ? CAP : 1][64];
   auto list_of = [&](int w_, int c_, int l_) RKV_INLINE {
     return LaneList<SPLIT>{&sbd[w_][c_][0][l_], &sbs[SPLIT ? w_ : 0][c_][0][l_]};
   };
-  __shared__ __attribute__((aligned(16))) __bf16 kbuf[2][32][kRowPad];
-  __shared__ __attribute__((aligned(16))) float nbuf[2][32];
+  __shared__ __attribute__((aligned(16))) __bf16 kbuf[DIRECT ? 1 : 2][32][kRowPad];
+  __shared__ __attribute__((aligned(16))) float nbuf[DIRECT ? 1 : 2][32];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -344,12 +349,12 @@ __global__ __launch_bounds__(256, 2) void k_dist_topk(
     bx = (int)(i % nb);
   }
   const int blk = n_blocks - 1 - bx;
-  const int64_t blk0 = p0 + (int64_t)blk * kBlockRows;
+  const int64_t blk0 = p0 + (int64_t)blk * BROWS;
   const int64_t row0 = blk0 + w * 32 * kSets;
   const bool active = row0 < p1;
   const int n = lane & 31;
   const int half = lane >> 5;
-  const int64_t blk_last = (blk0 + kBlockRows - 1 < p1) ? blk0 + kBlockRows - 1 : p1 - 1;
+  const int64_t blk_last = (blk0 + BROWS - 1 < p1) ? blk0 + BROWS - 1 : p1 - 1;
   const int ntile_blk = (int)((sched_count_le((int32_t)blk_last, sc) + 31) / 32);
   const int64_t last_row = (row0 + 32 * kSets - 1 < p1) ? row0 + 32 * kSets - 1 : p1 - 1;
   const int ntile = active ? (int)((sched_count_le((int32_t)last_row, sc) + 31) / 32) : 0;
@@ -394,25 +399,16 @@ __global__ __launch_bounds__(256, 2) void k_dist_topk(
   };
   // acc[c][r]: e = |ref|^2 - 2 k.ref of candidate slot rt*32 + acc_row(r, half)
   // for token row0 + 32c + n; +inf past the token's last candidate.
-  auto tile_scores = [&](int rt, int b, f32x16 (&acc)[kSets]) RKV_INLINE {
-    f32x16 init;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 nn = *reinterpret_cast<const float4*>(&nbuf[b][8 * q4 + 4 * half]);
-      init[4 * q4 + 0] = nn.x;
-      init[4 * q4 + 1] = nn.y;
-      init[4 * q4 + 2] = nn.z;
-      init[4 * q4 + 3] = nn.w;
-    }
+  auto tile_scores = [&](int rt, auto&& get_a, const f32x16& init, f32x16 (&acc)[kSets]) RKV_INLINE {
     {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kbuf[b][n][8 * half]);
+      const bf16x8 a = get_a(0);
 #pragma unroll
       for (int c = 0; c < kSets; ++c)
         acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[c][0], init, 0, 0, 0);
     }
 #pragma unroll
     for (int s = 1; s < 8; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kbuf[b][n][16 * s + 8 * half]);
+      const bf16x8 a = get_a(s);
 #pragma unroll
       for (int c = 0; c < kSets; ++c)
         acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[c][s], acc[c], 0, 0, 0);
@@ -429,6 +425,33 @@ __global__ __launch_bounds__(256, 2) void k_dist_topk(
       }
     }
   };
+  // scores of the tile staged in LDS buffer b
+  auto lds_scores = [&](int rt, int b, f32x16 (&acc)[kSets]) RKV_INLINE {
+    f32x16 init;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 nn = *reinterpret_cast<const float4*>(&nbuf[b][8 * q4 + 4 * half]);
+      init[4 * q4 + 0] = nn.x;
+      init[4 * q4 + 1] = nn.y;
+      init[4 * q4 + 2] = nn.z;
+      init[4 * q4 + 3] = nn.w;
+    }
+    tile_scores(rt, [&](int s_) RKV_INLINE {
+      return *reinterpret_cast<const bf16x8*>(&kbuf[b][n][16 * s_ + 8 * half]);
+    }, init, acc);
+  };
+  // DIRECT: a tile's A operands (slot rt*32 + n, dims 16s + 8*half + [0,8))
+  // and norms (rows acc_row(r, half)) straight from memory, slots past the
+  // last reference clamped to it (their scores are masked)
+  auto dload = [&](int rt, bf16x8 (&a)[8], f32x16& init) RKV_INLINE {
+    const uint32_t slot = min((uint32_t)rt * 32 + (uint32_t)n, last_slot);
+#pragma unroll
+    for (int s_ = 0; s_ < 8; ++s_)
+      a[s_] = *reinterpret_cast<const bf16x8*>(rk + slot * 128 + 16 * s_ + 8 * half);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      init[r] = rn[min((uint32_t)rt * 32 + (uint32_t)acc_row(r, half), last_slot)];
+  };
   // Streams every candidate tile of the block through LDS; `epi(rt, acc)`
   // consumes this wave's scores of tile rt.  Global loads run two tiles
   // ahead: tile rt + 2 is requested while tile rt is scored, and tile rt + 1
@@ -439,25 +462,48 @@ __global__ __launch_bounds__(256, 2) void k_dist_topk(
   // with no branch around them the load counter waits only for the older
   // tile, and the newer load stays in flight across the scoring.
   auto stream = [&](auto&& epi) RKV_INLINE {
-    u32x4 pa[2], pb[2];
-    float na, nb;
-    gload(0, pa, na);
-    lstore(0, pa, na);
-    gload(1, pb, nb);
-    __syncthreads();
-    auto step = [&](int rt, u32x4 (&st)[2], float& sn, u32x4 (&ld)[2], float& ln) RKV_INLINE {
-      gload(rt + 2, ld, ln);
-      if (rt < ntile) {
-        f32x16 acc[kSets];
-        tile_scores(rt, rt & 1, acc);
-        epi(rt, acc);
+    if constexpr (DIRECT) {
+      // one wave: its own tiles, the next one's operands in flight (two
+      // register sets alternate)
+      bf16x8 a0[8], a1[8];
+      f32x16 i0, i1;
+      dload(0, a0, i0);
+      for (int rt = 0; rt < ntile; rt += 2) {
+        dload(rt + 1, a1, i1);
+        {
+          f32x16 acc[kSets];
+          tile_scores(rt, [&](int s_) RKV_INLINE { return a0[s_]; }, i0, acc);
+          epi(rt, acc);
+        }
+        if (rt + 1 >= ntile) break;
+        dload(rt + 2, a0, i0);
+        {
+          f32x16 acc[kSets];
+          tile_scores(rt + 1, [&](int s_) RKV_INLINE { return a1[s_]; }, i1, acc);
+          epi(rt + 1, acc);
+        }
       }
-      lstore((rt + 1) & 1, st, sn);
+    } else {
+      u32x4 pa[2], pb[2];
+      float na, nb;
+      gload(0, pa, na);
+      lstore(0, pa, na);
+      gload(1, pb, nb);
       __syncthreads();
-    };
-    for (int rt = 0; rt < ntile_blk; rt += 2) {
-      step(rt, pb, nb, pa, na);
-      step(rt + 1, pa, na, pb, nb);
+      auto step = [&](int rt, u32x4 (&st)[2], float& sn, u32x4 (&ld)[2], float& ln) RKV_INLINE {
+        gload(rt + 2, ld, ln);
+        if (rt < ntile) {
+          f32x16 acc[kSets];
+          lds_scores(rt, rt & 1, acc);
+          epi(rt, acc);
+        }
+        lstore((rt + 1) & 1, st, sn);
+        __syncthreads();
+      };
+      for (int rt = 0; rt < ntile_blk; rt += 2) {
+        step(rt, pb, nb, pa, na);
+        step(rt + 1, pa, na, pb, nb);
+      }
     }
   };
 
@@ -601,13 +647,23 @@ hipError_t launch_refstore(int dtype, const void* K, const void* V, void* ref_kv
                                    n_inst, H, p0, n_in, n_refs, sc, st);
 }
 
+// Ranges up to this many positions per head take the one-wave form.
+constexpr int64_t kDirectMaxRows = 256;
+
 template <typename T, int KM>
 hipError_t launch_topk_t(const void* K, const void* refkey, const float* refnorm,
                          uint16_t* idx, int64_t n_inst, int H, int64_t N, int64_t n_refs,
                          Sched sc, int k, int64_t p0, int64_t n_in, hipStream_t st) {
+  if (n_in <= kDirectMaxRows) {
+    const int n_blocks = (int)((n_in + 32 * kSets - 1) / (32 * kSets));
+    hipLaunchKernelGGL((k_dist_topk<T, KM, true>), dim3(n_blocks, H, (unsigned)n_inst),
+                       dim3(64), 0, st, (const T*)K, (const __bf16*)refkey, refnorm, idx, N,
+                       n_refs, sc, k, H, n_blocks, p0, n_in);
+    return hipGetLastError();
+  }
   const int n_blocks = (int)((n_in + kBlockRows - 1) / kBlockRows);
-  hipLaunchKernelGGL((k_dist_topk<T, KM>), dim3(n_blocks, H, (unsigned)n_inst), dim3(256), 0,
-                     st, (const T*)K, (const __bf16*)refkey, refnorm, idx, N, n_refs, sc, k,
+  hipLaunchKernelGGL((k_dist_topk<T, KM, false>), dim3(n_blocks, H, (unsigned)n_inst), dim3(256),
+                     0, st, (const T*)K, (const __bf16*)refkey, refnorm, idx, N, n_refs, sc, k,
                      H, n_blocks, p0, n_in);
   return hipGetLastError();
 }
