@@ -51,12 +51,12 @@ def pytest_terminal_summary(terminalreporter):
 def pytest_sessionfinish(session):
     """Write the accepted near-ties and rounding-boundary cases of every
     encode comparison to a JSON record ($RKV_PARITY_REPORT, by default
-    gpurun_out/parity_counts.json under the repository root)."""
+    reports/parity_counts.json under the repository root)."""
     rep = _parity_report()
     if not rep:
         return
     path = os.environ.get("RKV_PARITY_REPORT",
-                          os.path.join(ROOT, "gpurun_out", "parity_counts.json"))
+                          os.path.join(ROOT, "reports", "parity_counts.json"))
     try:
         os.makedirs(os.path.dirname(path), exist_ok=True)
         with open(path, "w") as f:
