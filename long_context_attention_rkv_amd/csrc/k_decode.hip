@@ -1100,6 +1100,19 @@ __global__ __launch_bounds__(CT) void k_combine(const float* __restrict__ part,
       }
       s = kCombSplits;
     }
+    // further splits in batches, each batch's loads first (the sum keeps
+    // split order)
+    for (; s + kCombSplits <= n_split; s += kCombSplits) {
+      float4 v[kCombSplits];
+#pragma unroll
+      for (int u = 0; u < kCombSplits; ++u)
+        v[u] = *reinterpret_cast<const float4*>(base + (s + u) * rec + 132 + 4 * c);
+#pragma unroll
+      for (int u = 0; u < kCombSplits; ++u) {
+        const float f = fs[s + u];
+        acc.x += f * v[u].x; acc.y += f * v[u].y; acc.z += f * v[u].z; acc.w += f * v[u].w;
+      }
+    }
     for (; s < n_split; ++s) {
       const float f = fs[s];
       const float4 v = *reinterpret_cast<const float4*>(base + s * rec + 132 + 4 * c);
@@ -1116,7 +1129,19 @@ __global__ __launch_bounds__(CT) void k_combine(const float* __restrict__ part,
         acc.y += fs[u] * ov[u].y;
       }
     }
-    for (int s = kCombSplits; s < n_split; ++s) {
+    int s = kCombSplits;
+    for (; s + kCombSplits <= n_split; s += kCombSplits) {
+      float2 v[kCombSplits];
+#pragma unroll
+      for (int u = 0; u < kCombSplits; ++u)
+        v[u] = *reinterpret_cast<const float2*>(base + (s + u) * rec + 4 + od);
+#pragma unroll
+      for (int u = 0; u < kCombSplits; ++u) {
+        acc.x += fs[s + u] * v[u].x;
+        acc.y += fs[s + u] * v[u].y;
+      }
+    }
+    for (; s < n_split; ++s) {
       const float2 v = *reinterpret_cast<const float2*>(base + s * rec + 4 + od);
       acc.x += fs[s] * v.x;
       acc.y += fs[s] * v.y;
