@@ -624,11 +624,14 @@ constexpr int kLdsQWaves = 16;             // waves per block
 constexpr int kLdsRefBytes = 128 * 1024;   // reference rows of one plane held in LDS
 constexpr int kLdsChunkTiles = 256;        // tiles per block
 
-// bf16 pair selectors (the low or the high element of a word, times 1),
-// held in registers: as a compile-time operand the compiler encodes the low
-// selector 0x00003F80 as the inline constant 1.0, which v_dot2c_f32_bf16
-// does not read as that pattern (sums measured wrong on the device), so the
-// patterns are moved into VGPRs by hand once per kernel.
+// bf16 pair selectors (the low or the high element of a word times a power
+// of two), held in registers: as a compile-time operand the compiler encodes
+// the low selector 0x00003F80 as the inline constant 1.0, which
+// v_dot2c_f32_bf16 does not read as that pattern (sums measured wrong on the
+// device), so the patterns are moved into VGPRs by hand once per kernel.
+// make_bf16_sel gives the factor 1; make_bf16_nsel<KM> the factor -1/KM
+// (KM = 4, 8, 16: bf16 0xBE80, 0xBE00, 0xBD80), exact for every bf16 value
+// that is not below 2^-122 in magnitude.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 struct Bf16Sel {
   bf16x2_t lo, hi;
@@ -639,8 +642,43 @@ RKV_INLINE __device__ inline Bf16Sel make_bf16_sel() {
   asm volatile("v_mov_b32 %0, 0x3f800000" : "=v"(hi));
   return Bf16Sel{__builtin_bit_cast(bf16x2_t, lo), __builtin_bit_cast(bf16x2_t, hi)};
 }
+template <int KM>
+RKV_INLINE __device__ inline Bf16Sel make_bf16_nsel() {
+  static_assert(KM == 4 || KM == 8 || KM == 16, "power-of-two slot counts");
+  uint32_t lo, hi;
+  if constexpr (KM == 4) {
+    asm volatile("v_mov_b32 %0, 0xbe80" : "=v"(lo));
+    asm volatile("v_mov_b32 %0, 0xbe800000" : "=v"(hi));
+  } else if constexpr (KM == 8) {
+    asm volatile("v_mov_b32 %0, 0xbe00" : "=v"(lo));
+    asm volatile("v_mov_b32 %0, 0xbe000000" : "=v"(hi));
+  } else {
+    asm volatile("v_mov_b32 %0, 0xbd80" : "=v"(lo));
+    asm volatile("v_mov_b32 %0, 0xbd800000" : "=v"(hi));
+  }
+  return Bf16Sel{__builtin_bit_cast(bf16x2_t, lo), __builtin_bit_cast(bf16x2_t, hi)};
+}
 
-// acc += the 8 elements of a raw row piece (bf16: 16 bytes, fp32: 32 bytes).
+// acc = the 8 elements of a bf16 row piece times the selectors' factor: the
+// three-operand dot with a zero addend (the builtin becomes the two-operand
+// form, which needs the zero moved into acc first).  The product is exact,
+// so the result needs no rounding.
+RKV_INLINE __device__ inline float dot2_sel0(uint32_t w, bf16x2_t sel) {
+  float d;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(d) : "v"(w), "v"(sel));
+  return d;
+}
+RKV_INLINE __device__ inline void acc_set8(const u32x4 (&r)[1], float (&acc)[8], const Bf16Sel& sl) {
+  const uint32_t wd[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc[2 * q] = dot2_sel0(wd[q], sl.lo);
+    acc[2 * q + 1] = dot2_sel0(wd[q], sl.hi);
+  }
+}
+
+// acc += the 8 elements of a raw row piece times the selectors' factor
+// (bf16: 16 bytes; fp32: 32 bytes, factor 1).
 RKV_INLINE __device__ inline void acc_add8(const u32x4 (&r)[1], float (&acc)[8], const Bf16Sel& sl) {
   const uint32_t wd[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
 #pragma unroll
@@ -693,7 +731,7 @@ __global__ __launch_bounds__(1024) void k_quantize_lds(
   __shared__ u32x4 rl[kLdsRefBytes / 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: tile loop in scalars
   const int rr = lane >> 4;        // 16-lane row of the wave: positions 8 rr + s
   const int dl = lane & 15;        // dims [8 dl, 8 dl + 8)
   // grid (2 * chunks, H, inst); the chunks and planes of one head run on one
@@ -725,6 +763,7 @@ __global__ __launch_bounds__(1024) void k_quantize_lds(
 
   const char* lb = reinterpret_cast<const char*>(rl);
   const Bf16Sel bsel = make_bf16_sel();
+  const Bf16Sel nsel = make_bf16_nsel<KM>();
   const uint32_t lane16 = 16u * dl;
   const int n_groups = 128 / group;
   const int lanes_per_group = group >> 3;
@@ -732,29 +771,33 @@ __global__ __launch_bounds__(1024) void k_quantize_lds(
   const int sgrp = dl / lanes_per_group;
   const T* xin = (plane ? V : K) + ih * n_in * 128 + 8 * dl;  // + (position - p0) * 128
   const uint16_t* ib = idx + ih * N * k;
-  // K codes and scales of this head through bounded buffer descriptors: a
-  // store that must not happen gets an offset past the range and is dropped
-  // by the hardware, so no store sits behind a branch (a branch around a
-  // store would make the compiler wait for every load in flight before it)
-  // (bases at the chunk's first position: offsets stay 32-bit)
-  const int64_t cpos0 = (int64_t)t_first * kVTile;
-  const int64_t cpos1 = (int64_t)t_end * kVTile < N ? (int64_t)t_end * kVTile : N;
-  const uint32_t ck_bytes = (uint32_t)(cpos1 - cpos0) * (16u * BITS);
+  // K codes and scales of this head through bounded buffer descriptors over
+  // the positions [p0, p1): the hardware drops a store whose offset falls
+  // outside, which takes care of positions outside the range (below p0 the
+  // 32-bit offset wraps past the end), so no store sits behind a branch (a
+  // branch around a store would make the compiler wait for every load in
+  // flight before it).  Offset of position pos, lane piece: (pos - p0) times
+  // the bytes per position (wave-uniform) plus a lane constant; lanes that
+  // write no scale get a lane constant past every range.
+  constexpr uint32_t kDrop = 0x80000000u;
+  const uint32_t ck_bytes = (uint32_t)n_in * (16u * BITS);
   const __amdgpu_buffer_rsrc_t kb = __builtin_amdgcn_make_buffer_rsrc(
-      codes_k + (ih * N + cpos0) * (16 * BITS), 0, (int)ck_bytes, 0x00020000);
-  const uint32_t sc_bytes = (uint32_t)(cpos1 - cpos0) * 4u * n_groups;
+      codes_k + (ih * N + p0) * (16 * BITS), 0, (int)ck_bytes, 0x00020000);
+  const uint32_t sc_bytes = (uint32_t)n_in * 4u * n_groups;
   const __amdgpu_buffer_rsrc_t sb = __builtin_amdgcn_make_buffer_rsrc(
-      scales + (ih * N + cpos0) * 2 * n_groups, 0, (int)sc_bytes, 0x00020000);
-  const uint32_t k_lane = (uint32_t)dl * BITS;
-  const uint32_t s_lane = 2u * (uint32_t)(plane * n_groups + sgrp);
-  constexpr uint32_t kDrop = 0x80000000u;  // past every range: the store is dropped
+      scales + (ih * N + p0) * 2 * n_groups, 0, (int)sc_bytes, 0x00020000);
+  const uint32_t k_lane = (uint32_t)(8 * rr) * (16u * BITS) + (uint32_t)dl * BITS;
+  const uint32_t s_lane = scale_lane ? (uint32_t)(8 * rr) * (4u * n_groups) +
+                                           2u * (uint32_t)(plane * n_groups + sgrp)
+                                     : kDrop;
   constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
   constexpr float inv_qmax = 1.0f / qmax;
   constexpr float tol = (qmax + 1.f) * 0x1p-21f;
 
-  // residual of this lane's 8 dims at position `pos` -> scale and codes (u);
-  // stores the scale and (K plane) the codes when `mine`
-  auto finish = [&](int pos, bool mine, float (&z)[8], uint32_t (&u)[8]) RKV_INLINE {
+  // residual of this lane's 8 dims at position tb + 8 rr + s -> scale and
+  // codes (u); stores the scale and (K plane) the codes if that position is
+  // in [p0, p1)
+  auto finish = [&](int tb, int s, float (&z)[8], uint32_t (&u)[8]) RKV_INLINE {
     if constexpr (LAT) {
       lat_signs8(z, lm, dl);
       fwht128_8(z, dl);
@@ -771,13 +814,9 @@ __global__ __launch_bounds__(1024) void k_quantize_lds(
     const float rs = sv > 0.f ? __builtin_amdgcn_rcpf(sv) : 0.f;  // within 1 ulp of 1/s
     // a scale that is not plain (rare) has every code decided exactly and clamped
     codes8<false>(z, sv, rs, qmax, tol, u, !plain);
-    const uint32_t rp = (uint32_t)(pos - cpos0);
-    const uint32_t soff = (mine && scale_lane) ? rp * (4u * n_groups) + s_lane : kDrop;
-    __builtin_amdgcn_raw_buffer_store_b16(sbits, sb, (int)soff, 0, 0);
-    if (plane == 0) {
-      const uint32_t koff = mine ? rp * (16u * BITS) + k_lane : kDrop;
-      buffer_store_word<BITS>(kb, koff, pack8<BITS>(u));
-    }
+    const uint32_t ru = (uint32_t)(tb + s - p0);  // wave-uniform
+    __builtin_amdgcn_raw_buffer_store_b16(sbits, sb, (int)(ru * (4u * n_groups) + s_lane), 0, 0);
+    if (plane == 0) buffer_store_word<BITS>(kb, ru * (16u * BITS) + k_lane, pack8<BITS>(u));
   };
 
   // Row piece and slot word of step s of the tile at tbx, through bounded
@@ -816,24 +855,20 @@ __global__ __launch_bounds__(1024) void k_quantize_lds(
       // every position has KM candidates: unconditional loads (positions
       // outside the range reread one inside it and store nothing)
       auto step = [&](int s, PosLoads<T, KM>& cur) RKV_INLINE {
-        const int pos = tb + 8 * rr + s;
-        const bool mine = pos >= v0 && pos < v1;
         spread_slot_words<T, KM>(cur);
         u32x4 g[KM][sizeof(T) / 2];
 #pragma unroll
         for (int j = 0; j < KM; ++j) lds_piece<T>(lb, ref_piece_off<T>(slot_word(cur, j), j & 1, lane16), g[j]);
-        // the sum starts at the first row itself (exact), then adds the others
+        // acc = -(fp32 sum of the rows in slot order) / KM: the rows enter
+        // scaled by -1/KM (exact), so every partial sum is the unscaled one's
+        // exact image; then z = fl(x + acc) = fl(x - sum / KM)
         float acc[8];
-        widen(g[0], acc);
+        acc_set8(g[0], acc, nsel);
 #pragma unroll
-        for (int j = 1; j < KM; ++j) acc_add8(g[j], acc, bsel);
-        float x[8], z[8];
-        widen(cur.x, x);
-        constexpr float inv = 1.0f / KM;  // KM is 4, 8 or 16: exact
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = __builtin_fmaf(acc[e], -inv, x[e]);
+        for (int j = 1; j < KM; ++j) acc_add8(g[j], acc, nsel);
+        acc_add8(cur.x, acc, bsel);
         uint32_t u[8];
-        finish(pos, mine, z, u);
+        finish(tb, s, acc, u);
         if (plane == 1) v_accumulate<BITS>(u, s, vw);
       };
       if (!ring_ok) {
@@ -886,7 +921,7 @@ __global__ __launch_bounds__(1024) void k_quantize_lds(
 #pragma unroll
             for (int e = 0; e < 8; ++e) z[e] = x[e] - acc[e] / kf;
           }
-          finish(pos, true, z, u);
+          finish(tb, s, z, u);
         }
         if (plane == 1) v_accumulate<BITS>(u, s, vw);
       }

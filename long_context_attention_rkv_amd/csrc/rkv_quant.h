@@ -76,30 +76,43 @@ __device__ inline int exact_code(float z, float s, float rs, float qmax, float t
 
 // Codes of 8 residuals with scale s (rs ~ 1/s within 1 ulp; rs = 0 when
 // s = 0).  t = fl(z*rs + 1.5*2^23) holds the integer nearest to the exact
-// product z*rs (ties to even) in its low mantissa bits; fma(z, rs, M - t) is
-// that rounding's remainder.  When every remainder is clear of 1/2 by more
-// than the product's error, z*rs and z/s round alike; otherwise the lane
-// decides each code exactly.  Returned as M + code (so the low bits are the
-// two's complement code), clamped to [-qmax, qmax].  kClamp = false skips
-// the clamp of the estimated codes, for callers that pass exact = true
-// unless the scale keeps every code in range (exact_scale_bits_plain): the
-// exactly decided codes are always clamped.
+// product z*rs (ties to even) in its low mantissa bits; r = fma(z, rs, M - t)
+// is that rounding's remainder.  When a remainder is clear of 1/2 by more
+// than the product's error, z*rs and z/s round alike.  Otherwise the code is
+// one of the two integers either side of the half-integer b next to z*rs on
+// r's side, and the sign of fma(-b, s, z) = z - b*s (exact: b*s has at most
+// 19 significant bits and the difference is a multiple of 2^-149) decides it,
+// ties going to the even integer (the low bit of M + code).  Returned as
+// M + code (so the low bits are the two's complement code), clamped to
+// [-qmax, qmax].  kClamp = false skips the clamp of the estimated codes, for
+// callers that pass exact = true unless the scale keeps every code in range
+// (exact_scale_bits_plain): codes that took the exact path are always
+// clamped.
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 
 template <bool kClamp = true>
 __device__ inline void codes8(const float (&z)[8], float s, float rs, float qmax, float tol,
                               uint32_t (&u)[8], bool exact = false) {
-  float t[8];
+  float t[8], r[8];
   float emax = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     t[e] = __builtin_fmaf(z[e], rs, kMagic);
-    const float r = __builtin_fmaf(z[e], rs, kMagic - t[e]);
-    emax = fmaxf(emax, fabsf(r));
+    r[e] = __builtin_fmaf(z[e], rs, kMagic - t[e]);
+    emax = fmaxf(emax, fabsf(r[e]));
   }
   if (exact || emax > 0.5f - tol) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = kMagic + (float)exact_code(z[e], s, rs, qmax, tol);
+    for (int e = 0; e < 8; ++e) {
+      if (fabsf(r[e]) > 0.5f - tol) {
+        const float lo = r[e] < 0.f ? t[e] - 1.f : t[e];   // M + the lower candidate
+        const float b = (lo - kMagic) + 0.5f;              // the half-integer between them
+        const float h = __builtin_fmaf(-b, s, z[e]);
+        const bool odd = (__float_as_uint(lo) & 1u) != 0u;
+        t[e] = (h > 0.f || (h == 0.f && odd)) ? lo + 1.f : lo;
+      }
+      t[e] = __builtin_amdgcn_fmed3f(t[e], kMagic - qmax, kMagic + qmax);
+    }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e)
