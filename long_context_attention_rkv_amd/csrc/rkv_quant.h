@@ -48,13 +48,17 @@ __device__ inline uint16_t exact_scale_bits(float a, float qmax, float inv_qmax)
 // rounding of a normal-range estimate.  Then the scale is within a relative
 // 2^-11 of a/qmax, so |z/scale| < qmax + 1/2 for every element of the group
 // (qmax <= 127) and no code of the group needs clamping.
+// (The plain rounding is taken unconditionally and replaced in the rare other
+// case: one divergent branch instead of a branch per condition.)
 __device__ inline uint16_t exact_scale_bits_plain(float a, float qmax, float inv_qmax,
                                                   bool& plain) {
   const float y = a * inv_qmax;
-  const int low = (int)(__float_as_uint(y) & 0x1FFFu) - 0x1000;
-  plain = y >= 0x1p-14f && y < 65504.f && (low > 3 || low < -3);
-  if (plain) return f32_to_half_bits_rne(y);
-  return exact_scale_bits_slow(a, qmax, inv_qmax);
+  // low bits within 3 of the half-way pattern: (bits & 0x1FFF) - 0x0FFD in [0, 6]
+  const uint32_t near = (__float_as_uint(y) & 0x1FFFu) - 0x0FFDu;
+  plain = (y >= 0x1p-14f) & (y < 65504.f) & (near > 6u);
+  uint16_t b = f32_to_half_bits_rne(y);
+  if (!plain) b = exact_scale_bits_slow(a, qmax, inv_qmax);
+  return b;
 }
 
 // Integer nearest to z/s (ties to even), clamped to [-qmax, qmax].  s > 0.
