@@ -611,8 +611,12 @@ __global__ __launch_bounds__(512, KM <= 8 ? 6 : 4) void k_quantize(
 // block barrier after the copy).
 //
 // Arithmetic: the selected rows are summed with v_dot2_f32_bf16 (one
-// element times 1 plus the running fp32 sum: no unpacking), z = fl(x -
-// sum / k_eff); scales and codes are the exact round-half-even of
+// element times -1/k plus the running fp32 sum: no unpacking, and the
+// scaling is exact, so the partial sums are those of the plain sum scaled),
+// then the token row enters the same way times 1: z = fl(x - sum / k)
+// (positions with fewer than k candidates, in a sequence's first tiles,
+// sum the rows plainly and divide by k_eff); scales and codes are the
+// exact round-half-even of
 // max|z| / qmax and z / scale, as in k_quantize (bf16 data puts many z /
 // scale exactly on a half-integer, so the tie must be decided exactly).
 //
