@@ -704,10 +704,12 @@ def test_full_size_sampled_encode(case):
     say(f"  near-ties: {near}")
 
 
-@pytest.mark.parametrize("index", [1, 2])
+@pytest.mark.parametrize("index", [1, 2, 3])
 def test_full_size_decode_one_kv_head(index):
     """Decode at the full context of the workload for all query heads of KV
-    head 0 (the oracle rebuilds that head completely)."""
+    head 0 (the oracle rebuilds that head completely).  Index 3 is the
+    dynamic-stride 131072-position workload (896 references: the largest
+    oracle encode of the suite)."""
     _need_gpu()
     cfg = get_config(index)
     N = cfg.seq_len
@@ -719,12 +721,14 @@ def test_full_size_decode_one_kv_head(index):
     Kn, Vn = to_np_f32(K[0, 0]), to_np_f32(V[0, 0])
     enc = oracle.encode(Kn, Vn, cfg.stride_base, cfg.double_after, cfg.k, 4, cfg.group)
     kv = oracle.reconstruct(enc, Kn, Vn, 4)
-    # the flat 1/sqrt(d) query and the sharp alpha = 1 one; 16 splits, and one
-    # split that walks the whole context (N / 1024 softmax chunks, each
-    # folding its fixed-point reference weights into the totals)
+    # the flat 1/sqrt(d) query and the sharp alpha = 1 one; the split count
+    # the library suggests for this cache, 16 splits, and one split that walks the whole context
+    # (N / 1024 softmax chunks, each folding its fixed-point reference
+    # weights into the totals)
+    splits = sorted({rkv.rkv_decode_split_hint(cache, cfg.n_q_heads), 16, 1}, reverse=True)
     for scale in (1.0 / math.sqrt(cfg.head_dim), 1.0):
         want = oracle.decode_attn(to_np_f32(q[0, :G]), kv[None, :, 0], kv[None, :, 1], scale)
-        for n_split in (16, 1):
+        for n_split in splits:
             got = rkv.rkv_decode_attn(q, cfg.n_q_heads, cache, scale,
                                       n_split=n_split).cpu().numpy()
             err = attn_err(got[0, :G], want)
