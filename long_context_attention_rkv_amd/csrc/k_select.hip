@@ -333,7 +333,7 @@ __global__ __launch_bounds__(DIRECT ? 64 : 256, 2) void k_dist_topk(
   __shared__ __attribute__((aligned(16))) float nbuf[DIRECT ? 1 : 2][32];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Workgroups are dealt to the 8 XCDs in turn.  When the heads split evenly
   // over them, the i-th workgroup of XCD x takes block i % n_blocks of head
   // 8 (i / n_blocks) + x, so the blocks of one head run together on one XCD
@@ -363,15 +363,20 @@ __global__ __launch_bounds__(DIRECT ? 64 : 256, 2) void k_dist_topk(
   int my_last[kSets];
   // B operands: bf16(key) of token row0 + 32c + n, dims 16s + 8*half + [0,8);
   // the A operands (staged reference keys) carry the factor -2.
+  auto uniform_ptr = [](const void* p) RKV_INLINE {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  };
   bf16x8 bfrag[kSets][8];
+  const T* krow[kSets];
 #pragma unroll
   for (int c = 0; c < kSets; ++c) {
     const int64_t i = row0 + 32 * c + n;
     valid_row[c] = i < p1;
     my_last[c] = valid_row[c] ? sched_count_le((int32_t)i, sc) - 1 : -1;
-    const T* krow = K + (ih * n_in + (valid_row[c] ? i - p0 : 0)) * 128 + 8 * half;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) bfrag[c][s] = load_key_frag(krow + 16 * s, valid_row[c]);
+    krow[c] = K + (ih * n_in + (valid_row[c] ? i - p0 : 0)) * 128 + 8 * half;
   }
   const __bf16* rk = refkey + ih * n_refs * 128;
   const float* rn = refnorm + ih * n_refs;
@@ -380,14 +385,24 @@ __global__ __launch_bounds__(DIRECT ? 64 : 256, 2) void k_dist_topk(
   // past the last reference read the last one instead: every score of such
   // a slot is masked (it lies beyond every token's last candidate).
   const uint32_t last_slot = (uint32_t)(n_refs - 1);
+  // Staging loads through bounded buffer descriptors over this head's keys
+  // and norms: slots past the last reference read zeros (every score of such
+  // a slot is masked: it lies beyond every token's last candidate), the tile
+  // offset is a scalar and the lane offsets are fixed, so a tile's loads
+  // take no vector address arithmetic.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(rk), 0, __builtin_amdgcn_readfirstlane((int)(n_refs * 256)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t nrs = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(rn), 0, __builtin_amdgcn_readfirstlane((int)(n_refs * 4)), 0x00020000);
+  // thread t loads chunks t and t + 256 of the tile (16 bytes each); the
+  // whole offset is in the range-checked vector part
+  const int kvoff = tid * 16;
+  const int nvoff = (tid & 31) * 4;
   auto gload = [&](int rt, u32x4 (&v)[2], float& nv) RKV_INLINE {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int chunk = tid + 256 * c;
-      const uint32_t slot = min((uint32_t)rt * 32 + (uint32_t)(chunk >> 4), last_slot);
-      v[c] = *reinterpret_cast<const u32x4*>(rk + slot * 128 + (chunk & 15) * 8);
-    }
-    nv = rn[min((uint32_t)rt * 32 + (uint32_t)(tid & 31), last_slot)];
+    const int vo = kvoff + rt * 8192;
+    v[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, vo, 0, 0));
+    v[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, vo + 4096, 0, 0));
+    nv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(nrs, nvoff + rt * 128, 0, 0));
   };
   auto lstore = [&](int b, const u32x4 (&v)[2], float nv) RKV_INLINE {
 #pragma unroll
@@ -395,8 +410,49 @@ __global__ __launch_bounds__(DIRECT ? 64 : 256, 2) void k_dist_topk(
       const int chunk = tid + 256 * c;
       *reinterpret_cast<u32x4*>(&kbuf[b][chunk >> 4][(chunk & 15) * 8]) = v[c];
     }
-    if (tid < 32) nbuf[b][tid] = nv;
+    // (every thread stores: a branch here would let the compiler sink the
+    // norm load into it, past the key loads)
+    nbuf[b][tid & 31] = nv;
   };
+  // The first two tiles' staging loads go out before the token keys: the
+  // load counter completes in order, so the first staging store then waits
+  // only for them, and the first MFMAs wait only for the key fragments they
+  // use (requested in chain order: dims 16s .. 16s + 15 of both sets).
+  // pa/pb: the two register sets of staged tiles in flight; pass 1 starts
+  // with tiles 0 and 1 in them, and leaves pass 2's tile 0 in LDS buffer 0
+  // and its tile 1 in pb (see stream)
+  u32x4 pa[2], pb[2];
+  float na = 0.f, nb = 0.f;
+  if constexpr (!DIRECT) {
+    gload(0, pa, na);
+    gload(1, pb, nb);
+  }
+  if constexpr (sizeof(T) == 2) {
+    // bf16 keys through a bounded descriptor over the range's rows: rows
+    // past the range read zeros, with no branch around the loads (a branch
+    // would make every later wait count conservative)
+    // (the descriptor starts at the wave's first row and covers at most its
+    // 64 rows, so the offsets stay small for any range length)
+    const int64_t wrows = p1 - row0 < 32 * kSets ? p1 - row0 : 32 * kSets;
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(K + (ih * n_in + (active ? row0 - p0 : 0)) * 128), 0,
+        __builtin_amdgcn_readfirstlane(active ? (int)wrows * 256 : 0), 0x00020000);
+    int xo[kSets];
+#pragma unroll
+    for (int c = 0; c < kSets; ++c) xo[c] = (32 * c + n) * 256 + 16 * half;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int c = 0; c < kSets; ++c)
+        bfrag[c][s] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xrs, xo[c] + 32 * s, 0, 0));
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int c = 0; c < kSets; ++c) bfrag[c][s] = load_key_frag(krow[c] + 16 * s, valid_row[c]);
+  }
+
   // acc[c][r]: e = |ref|^2 - 2 k.ref of candidate slot rt*32 + acc_row(r, half)
   // for token row0 + 32c + n; +inf past the token's last candidate.
   auto tile_scores = [&](int rt, auto&& get_a, const f32x16& init, f32x16 (&acc)[kSets]) RKV_INLINE {
@@ -414,14 +470,13 @@ __global__ __launch_bounds__(DIRECT ? 64 : 256, 2) void k_dist_topk(
         acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[c][s], acc[c], 0, 0, 0);
     }
     if (rt >= full_tiles) {
-      const int r0 = rt * 32;
+      const int r0 = rt * 32 + 4 * half;
 #pragma unroll
       for (int c = 0; c < kSets; ++c) {
+        const int lim = my_last[c] - r0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int sl = r0 + acc_row(r, half);
-          if (sl > my_last[c]) acc[c][r] = INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (acc_row(r, 0) > lim) acc[c][r] = INFINITY;
       }
     }
   };
@@ -461,7 +516,7 @@ __global__ __launch_bounds__(DIRECT ? 64 : 256, 2) void k_dist_topk(
   // (tiles past the block's last read clamped slots and are never scored):
   // with no branch around them the load counter waits only for the older
   // tile, and the newer load stays in flight across the scoring.
-  auto stream = [&](auto&& epi) RKV_INLINE {
+  auto stream = [&](auto&& epi, bool pre) RKV_INLINE {
     if constexpr (DIRECT) {
       // one wave: its own tiles, the next one's operands in flight (two
       // register sets alternate)
@@ -484,14 +539,18 @@ __global__ __launch_bounds__(DIRECT ? 64 : 256, 2) void k_dist_topk(
         }
       }
     } else {
-      u32x4 pa[2], pb[2];
-      float na, nb;
-      gload(0, pa, na);
-      lstore(0, pa, na);
-      gload(1, pb, nb);
-      __syncthreads();
+      // Pass 1 (pre): tile 0 is in pa and tile 1 in flight in pb.  Its last
+      // two loads wrap to tiles 0 and 1 again, so that at its end LDS buffer
+      // 0 holds tile 0 and pb tile 1 for pass 2, which then starts at once.
+      const int nt_even = (ntile_blk + 1) & ~1;
+      if (pre) {
+        lstore(0, pa, na);
+        __syncthreads();
+      }
       auto step = [&](int rt, u32x4 (&st)[2], float& sn, u32x4 (&ld)[2], float& ln) RKV_INLINE {
-        gload(rt + 2, ld, ln);
+        int tgt = rt + 2;
+        if (pre && tgt >= nt_even) tgt -= nt_even;
+        gload(tgt, ld, ln);
         if (rt < ntile) {
           f32x16 acc[kSets];
           lds_scores(rt, rt & 1, acc);
@@ -518,7 +577,7 @@ __global__ __launch_bounds__(DIRECT ? 64 : 256, 2) void k_dist_topk(
     for (int c = 0; c < kSets; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) bk[c][r] = fminf(bk[c][r], acc[c][r]);
-  });
+  }, true);
   // one token per lane: lower lanes take set 0, upper lanes set 1, each with
   // the 16 bucket minima of both of its lanes
   static_assert(kSets == 2, "the half swap pairs two token sets");
@@ -577,7 +636,7 @@ __global__ __launch_bounds__(DIRECT ? 64 : 256, 2) void k_dist_topk(
         }
       }
     }
-  });
+  }, false);
   int cnt[kSets];
 #pragma unroll
   for (int c = 0; c < kSets; ++c) cnt[c] = (int)(ends[c].d - &sbd[w][c][0][lane]) / LaneList<SPLIT>::kD;
