@@ -134,21 +134,25 @@ template <int KM>
 constexpr int surv_cap() { return split_lists<KM>() ? KM + kCheckRows : KM + 3 + kCheckRows; }
 constexpr int kEntryWords = 128;  // stride of one two-word entry, in 32-bit words
 
-// One lane's list: d = its distance of entry 0, s (split layout) its slot of
-// entry 0.
+// One lane's list: d = its distance of entry 0.  Split layout: a wave's
+// lists are [set 0 distances][set 1 distances][slot words], each [entry][64
+// lanes] words; the slot word of (entry, lane) holds set 0's slot in its low
+// half and set 1's in its high half, so the slot of set c sits a fixed
+// `soff` halfwords from the distance (one pointer per list, and the 64 lanes
+// of a store touch 64 different words).
 template <bool SPLIT>
 struct LaneList {
   uint32_t* d;
-  uint16_t* s;
+  int soff;  // split layout: halfword offset of the slot from the distance
   static constexpr int kD = SPLIT ? 64 : kEntryWords;  // distance stride, in words
   __device__ uint32_t dist(int c) const { return d[c * kD]; }
   __device__ uint32_t slot(int c) const {
-    if constexpr (SPLIT) return s[c * 64];
+    if constexpr (SPLIT) return reinterpret_cast<const uint16_t*>(d)[soff + c * 128];
     else return d[c * kEntryWords + 64];
   }
   __device__ void put(int c, uint32_t dv, uint32_t sv) const {
     d[c * kD] = dv;
-    if constexpr (SPLIT) s[c * 64] = (uint16_t)sv;
+    if constexpr (SPLIT) reinterpret_cast<uint16_t*>(d)[soff + c * 128] = (uint16_t)sv;
     else d[c * kEntryWords + 64] = sv;
   }
 };
@@ -324,10 +328,11 @@ __global__ __launch_bounds__(DIRECT ? 64 : 256, 2) void k_dist_topk(
   constexpr bool SPLIT = split_lists<KM>();
   constexpr int NWV = DIRECT ? 1 : 4;           // waves per block
   constexpr int BROWS = NWV * 32 * kSets;       // tokens per block
-  __shared__ uint32_t sbd[NWV][kSets][CAP][SPLIT ? 64 : kEntryWords];
-  __shared__ uint16_t sbs[SPLIT ? NWV : 1][kSets][SPLIT ? CAP : 1][64];
+  __shared__ uint32_t sbd[NWV][SPLIT ? kSets + 1 : kSets][CAP][SPLIT ? 64 : kEntryWords];
+  // halfword offset from set c's distance to its slot (split layout)
+  auto soff_of = [](int c_) RKV_INLINE { return (kSets - c_) * CAP * 128 + c_; };
   auto list_of = [&](int w_, int c_, int l_) RKV_INLINE {
-    return LaneList<SPLIT>{&sbd[w_][c_][0][l_], &sbs[SPLIT ? w_ : 0][c_][0][l_]};
+    return LaneList<SPLIT>{&sbd[w_][c_][0][l_], soff_of(c_)};
   };
   __shared__ __attribute__((aligned(16))) __bf16 kbuf[DIRECT ? 1 : 2][32][kRowPad];
   __shared__ __attribute__((aligned(16))) float nbuf[DIRECT ? 1 : 2][32];
@@ -619,7 +624,6 @@ __global__ __launch_bounds__(DIRECT ? 64 : 256, 2) void k_dist_topk(
           ends[c].put(0, __float_as_uint(acc[c][r]), r0 + (uint32_t)acc_row(r, 0));
           const int inc = acc[c][r] <= tau[c] ? 1 : 0;
           ends[c].d += inc * LaneList<SPLIT>::kD;
-          if constexpr (SPLIT) ends[c].s += inc * 64;
         }
       }
       bool full = false;
@@ -632,7 +636,6 @@ __global__ __launch_bounds__(DIRECT ? 64 : 256, 2) void k_dist_topk(
           int cnt = (int)(ends[c].d - bl.d) / LaneList<SPLIT>::kD;
           lane_compact<KM, CAP>(bl, cnt, tau[c], k);
           ends[c].d = bl.d + cnt * LaneList<SPLIT>::kD;
-          if constexpr (SPLIT) ends[c].s = bl.s + cnt * 64;
         }
       }
     }
