@@ -386,15 +386,15 @@ __global__ __launch_bounds__(DIRECT ? 64 : 256, 2) void k_dist_topk(
   const __bf16* rk = refkey + ih * n_refs * 128;
   const float* rn = refnorm + ih * n_refs;
 
-  // cooperative staging: 512 chunks of 16 B per tile, 2 per thread.  Slots
-  // past the last reference read the last one instead: every score of such
-  // a slot is masked (it lies beyond every token's last candidate).
+  // (one-wave form) slots past the last reference read the last one
+  // instead: every score of such a slot is masked
   const uint32_t last_slot = (uint32_t)(n_refs - 1);
-  // Staging loads through bounded buffer descriptors over this head's keys
-  // and norms: slots past the last reference read zeros (every score of such
-  // a slot is masked: it lies beyond every token's last candidate), the tile
-  // offset is a scalar and the lane offsets are fixed, so a tile's loads
-  // take no vector address arithmetic.
+  // Cooperative staging, 512 chunks of 16 B per tile, 2 per thread, through
+  // bounded buffer descriptors over this head's keys and norms: slots past
+  // the last reference read zeros (every score of such a slot is masked: it
+  // lies beyond every token's last candidate), the tile offset is a scalar
+  // and the lane offsets are fixed, so a tile's loads take no vector address
+  // arithmetic.
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       uniform_ptr(rk), 0, __builtin_amdgcn_readfirstlane((int)(n_refs * 256)), 0x00020000);
   const __amdgpu_buffer_rsrc_t nrs = __builtin_amdgcn_make_buffer_rsrc(
