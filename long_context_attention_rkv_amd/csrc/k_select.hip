@@ -496,9 +496,12 @@ __global__ __launch_bounds__(DIRECT ? 64 : 256, 2) void k_dist_topk(
       init[4 * q4 + 2] = nn.z;
       init[4 * q4 + 3] = nn.w;
     }
-    tile_scores(rt, [&](int s_) RKV_INLINE {
-      return *reinterpret_cast<const bf16x8*>(&kbuf[b][n][16 * s_ + 8 * half]);
-    }, init, acc);
+    // all eight A fragments requested at once: one LDS round trip per tile
+    bf16x8 af[8];
+#pragma unroll
+    for (int s_ = 0; s_ < 8; ++s_) af[s_] = *reinterpret_cast<const bf16x8*>(&kbuf[b][n][16 * s_ + 8 * half]);
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads together, ahead of the chain
+    tile_scores(rt, [&](int s_) RKV_INLINE { return af[s_]; }, init, acc);
   };
   // DIRECT: a tile's A operands (slot rt*32 + n, dims 16s + 8*half + [0,8))
   // and norms (rows acc_row(r, half)) straight from memory, slots past the
