@@ -756,12 +756,24 @@ __global__ __launch_bounds__(1024) void k_quantize_lds(
   const int t_end = t_first + chunk_tiles < t_last ? t_first + chunk_tiles : t_last;
   if (t_first >= t_end) return;  // whole block
 
-  // copy the reference rows positions below p1 can select
+  // copy the reference rows positions below p1 can select: every thread
+  // requests all of its chunks before its first store (one memory round
+  // trip instead of one per chunk), through a descriptor bounded by those
+  // rows, so chunks past them read zeros (never gathered) and neither loop
+  // needs a branch
   {
     const int nr = sched_count(p1, sc);
-    const u32x4* src = reinterpret_cast<const u32x4*>(ref_kv + (ih * 2 + plane) * n_refs * 128);
-    const int n16 = nr * (int)(128 * sizeof(T) / 16);
-    for (int i = tid; i < n16; i += 1024) rl[i] = src[i];
+    constexpr int kPer = kLdsRefBytes / 16 / 1024;
+    const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(ref_kv + (ih * 2 + plane) * n_refs * 128), 0,
+        nr * (int)(128 * sizeof(T)), 0x00020000);
+    u32x4 tmp[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      tmp[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rrs, (tid + 1024 * j) * 16, 0, 0));
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) rl[tid + 1024 * j] = tmp[j];
   }
   __syncthreads();
 
