@@ -848,8 +848,10 @@ __global__ __launch_bounds__(1024) void k_quantize_lds(
   const uint32_t i_lane = 4u * (dl & (KM / 2 - 1));
   auto issue = [&](int tbx, int s, PosLoads<T, KM>& pl) RKV_INLINE {
     const uint32_t r0 = (uint32_t)(tbx + 8 * rr - p0);
+    // token rows are read once: non-temporal (nt), which measured about 1 %
+    // faster; the slot words stay cached (the other plane's blocks read them)
     pl.x[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            xrs, (int)(r0 * 256u + x_lane + 256u * s), 0, 0));
+                                            xrs, (int)(r0 * 256u + x_lane + 256u * s), 0, 2));
     pl.sl[0].x = __builtin_amdgcn_raw_buffer_load_b32(
         irs, (int)(r0 * (2u * KM) + i_lane + 2u * KM * s), 0, 0);
   };
