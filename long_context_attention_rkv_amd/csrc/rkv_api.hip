@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -75,9 +76,20 @@ size_t elt_bytes(rkv_dtype d) { return d == RKV_F32 ? 4 : 2; }
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 inline bool al16(const void* p) { return aligned(p, 16); }
 
+// The dtype field as the integer a C caller stored: C++ may not load a value
+// outside the enumerators' range through the enum type, so the field is
+// validated on its bytes before anything reads it as rkv_dtype.
+static_assert(sizeof(rkv_dtype) == sizeof(int32_t), "rkv_dtype is stored as a C int");
+inline int32_t dtype_code(const rkv_cache* c) {
+  int32_t v;
+  memcpy(&v, &c->dtype, sizeof v);
+  return v;
+}
+
 rkv_status check_shape(const rkv_cache* c) {
   if (!c) return RKV_ERR_INVALID_ARG;
-  if (c->dtype != RKV_F32 && c->dtype != RKV_BF16) return RKV_ERR_INVALID_ARG;
+  const int32_t dt = dtype_code(c);
+  if (dt != RKV_F32 && dt != RKV_BF16) return RKV_ERR_INVALID_ARG;
   if (c->n_inst < 0 || c->n_kv_heads < 1 || c->seq_len < 0) return RKV_ERR_INVALID_ARG;
   if (c->seq_len > kMaxPos) return RKV_ERR_INVALID_ARG;
   if (c->n_inst > 65535 || c->n_kv_heads > 65535) return RKV_ERR_INVALID_ARG;
