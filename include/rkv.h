@@ -100,7 +100,7 @@ typedef struct {
   rkv_dtype dtype;       /* K/V/q element type                                 */
   int64_t n_inst;        /* independent instances (batch x layers)             */
   int32_t n_kv_heads;    /* H                                                  */
-  int64_t seq_len;       /* N, positions per instance                          */
+  int64_t seq_len;       /* N, positions per instance, at most 2^22            */
   int32_t head_dim;      /* D; 128 is the supported value                      */
   rkv_stride stride;     /* reference schedule                                 */
   int32_t k;             /* nearest references averaged per token, 1..16       */

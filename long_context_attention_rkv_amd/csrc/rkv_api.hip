@@ -53,6 +53,10 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 constexpr int64_t kMaxPos = int64_t(1) << 30;  // positions must stay below 2^30
+// Positions per sequence in a cache: the kernels address one head's rows,
+// codes and slots with 32-bit byte offsets and buffer ranges (an fp32 row is
+// 512 bytes, so 2^22 rows are 2^31 bytes).
+constexpr int64_t kMaxSeqLen = int64_t(1) << 22;
 
 bool sched_ok(rkv_stride s) {
   if (s.base < 1 || s.base > (1 << 20)) return false;
@@ -91,7 +95,7 @@ rkv_status check_shape(const rkv_cache* c) {
   const int32_t dt = dtype_code(c);
   if (dt != RKV_F32 && dt != RKV_BF16) return RKV_ERR_INVALID_ARG;
   if (c->n_inst < 0 || c->n_kv_heads < 1 || c->seq_len < 0) return RKV_ERR_INVALID_ARG;
-  if (c->seq_len > kMaxPos) return RKV_ERR_INVALID_ARG;
+  if (c->seq_len > kMaxSeqLen) return RKV_ERR_INVALID_ARG;
   if (c->n_inst > 65535 || c->n_kv_heads > 65535) return RKV_ERR_INVALID_ARG;
   if (!sched_ok(c->stride)) return RKV_ERR_INVALID_ARG;
   if (c->k < 1 || c->k > 16) return RKV_ERR_INVALID_ARG;

@@ -162,6 +162,20 @@ static void check_cache_init_and_sizes(void) {
   lb.latent = 1;
   lb.bits = 0;
   CHECK(rkv_cache_init(&lb) == RKV_ERR_INVALID_ARG);
+  {
+    /* the longest sequence the kernels' 32-bit row offsets reach, and one
+     * tile more */
+    rkv_cache lg = make_cache(1, 1, (int64_t)1 << 22, 1 << 16);
+    CHECK(rkv_cache_init(&lg) == RKV_OK && lg.n_refs == 64);
+    lg.seq_len += 32;
+    CHECK(rkv_cache_init(&lg) == RKV_ERR_INVALID_ARG);
+    /* the largest instance and head counts at that length: sizes in range */
+    rkv_cache mx = make_cache(65535, 65535, (int64_t)1 << 22, 1 << 16);
+    CHECK(rkv_cache_init(&mx) == RKV_OK);
+    CHECK(rkv_cache_sizes(&mx, sz) == RKV_OK);
+    CHECK(sz[1] == (size_t)65535 * 65535 * ((size_t)1 << 22) * 64);
+    CHECK(rkv_decode_split_hint(&mx, 65535, &(int32_t){0}) == RKV_OK);
+  }
   CHECK(rkv_cache_init(NULL) == RKV_ERR_INVALID_ARG);
   CHECK(rkv_cache_sizes(NULL, sz) == RKV_ERR_INVALID_ARG);
 }

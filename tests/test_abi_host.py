@@ -125,10 +125,18 @@ def test_cache_init_and_sizes(lib):
     (dict(N=65536 * 2, base=2), L.RKV_ERR_RANGE), (dict(A=100, base=16), L.RKV_ERR_INVALID_ARG),
     (dict(ref_bits=2), L.RKV_ERR_INVALID_ARG), (dict(ref_bits=4, bits=0), L.RKV_ERR_INVALID_ARG),
     (dict(latent=2), L.RKV_ERR_INVALID_ARG), (dict(latent=1, bits=0), L.RKV_ERR_INVALID_ARG),
+    # more positions than the kernels' 32-bit row offsets reach
+    (dict(N=(1 << 22) + 32, base=1 << 16), L.RKV_ERR_INVALID_ARG),
 ])
 def test_cache_init_rejects(lib, bad, status):
     c = _cache(**bad)
     assert lib.rkv_cache_init(C.byref(c)) == status
+
+
+def test_longest_sequence_is_accepted(lib):
+    c = _cache(n_inst=1, H=1, N=1 << 22, base=1 << 16)
+    assert lib.rkv_cache_init(C.byref(c)) == L.RKV_OK
+    assert c.n_refs == 64
 
 
 def test_entry_points_validate_before_touching_the_device(lib):
