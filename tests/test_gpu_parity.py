@@ -704,6 +704,32 @@ def test_full_size_sampled_encode(case):
     say(f"  near-ties: {near}")
 
 
+# The longest sequence a cache accepts (2^22 positions), where the kernels'
+# 32-bit per-head byte offsets and buffer ranges are largest: 512 references
+# (the quantiser keeps them in LDS and reads the token rows through one
+# 2^30-byte range) and 32768 references (gathers from memory, and the
+# largest distance/top-k launch of the suite).
+LONGEST = [("longest_512_refs", 8192), ("longest_32768_refs", 128)]
+
+
+@pytest.mark.parametrize("name,base", LONGEST, ids=[c[0] for c in LONGEST])
+def test_longest_sequence_sampled_encode(name, base):
+    _need_gpu()
+    cfg = _cfg(1, n_kv_heads=1, stride_base=base)
+    N = 1 << 22
+    say(f"[longest encode] {name}: N={N} stride={base}")
+    K, V = make_kv(cfg, 1, N)
+    cache = encode(cfg, K, V, 4, 1, N)
+    assert cache.c.n_refs == N // base
+    gc = GpuCache(cache)
+    Kn, Vn = to_np_f32(K[0, 0]), to_np_f32(V[0, 0])
+    del K, V, cache
+    torch.cuda.empty_cache()
+    near = compare_encode(gc, 0, Kn, Vn, cfg.stride_base, cfg.double_after,
+                          rows=_sample_rows(N, 40, 11))["near_ties"]
+    say(f"  near-ties: {near}")
+
+
 @pytest.mark.parametrize("index", [1, 2, 3])
 def test_full_size_decode_one_kv_head(index):
     """Decode at the full context of the workload for all query heads of KV
