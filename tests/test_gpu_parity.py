@@ -730,6 +730,38 @@ def test_longest_sequence_sampled_encode(name, base):
     say(f"  near-ties: {near}")
 
 
+def test_longest_sequence_decode():
+    """Decode over a 2^22-position head (512 references, GQA 4) against the
+    oracle's softmax attention over the library's own reconstruction (whose
+    parity with the oracle is checked at smaller sizes): the property holds at
+    any length, and here one split walks 4096 softmax chunks, so the
+    per-reference weight totals reach their largest values."""
+    _need_gpu()
+    cfg = _cfg(1, n_kv_heads=1, n_q_heads=4, stride_base=8192)
+    N = 1 << 22
+    say(f"[longest decode] N={N} stride={cfg.stride_base}")
+    K, V = make_kv(cfg, 1, N)
+    q = make_q(cfg, 1)
+    cache = encode(cfg, K, V, 4, 1, N)
+    del K, V
+    Kh, Vh = rkv.rkv_reconstruct(cache)
+    torch.cuda.synchronize()
+    Khn, Vhn = Kh[0].cpu().numpy(), Vh[0].cpu().numpy()
+    del Kh, Vh
+    torch.cuda.empty_cache()
+    qn = to_np_f32(q[0])
+    splits = sorted({rkv.rkv_decode_split_hint(cache, cfg.n_q_heads), 1}, reverse=True)
+    for scale in (1.0 / math.sqrt(cfg.head_dim), 1.0):
+        want = oracle.decode_attn(qn, Khn, Vhn, scale)
+        for n_split in splits:
+            got = rkv.rkv_decode_attn(q, cfg.n_q_heads, cache, scale,
+                                      n_split=n_split).cpu().numpy()
+            err = attn_err(got[0], want)
+            say(f"  scale={scale:.4f} n_split={n_split} worst per-head rel L2 = {err:.2e}")
+            assert np.isfinite(got).all()
+            assert err <= 2e-3
+
+
 @pytest.mark.parametrize("index", [1, 2, 3])
 def test_full_size_decode_one_kv_head(index):
     """Decode at the full context of the workload for all query heads of KV
