@@ -175,6 +175,14 @@ static void check_cache_init_and_sizes(void) {
     CHECK(rkv_cache_sizes(&mx, sz) == RKV_OK);
     CHECK(sz[1] == (size_t)65535 * 65535 * ((size_t)1 << 22) * 64);
     CHECK(rkv_decode_split_hint(&mx, 65535, &(int32_t){0}) == RKV_OK);
+    {
+      /* workspaces at that shape: at least the reference keys and norms
+       * (encode) and one fp32 output row per query head (decode) */
+      const size_t ih = (size_t)65535 * 65535;
+      size_t ws = 0;
+      CHECK(rkv_encode_workspace(&mx, &ws) == RKV_OK && ws >= ih * 64 * (256 + 4));
+      CHECK(rkv_decode_workspace(&mx, 65535, 1, &ws) == RKV_OK && ws >= ih * 128 * 4);
+    }
   }
   CHECK(rkv_cache_init(NULL) == RKV_ERR_INVALID_ARG);
   CHECK(rkv_cache_sizes(NULL, sz) == RKV_ERR_INVALID_ARG);
